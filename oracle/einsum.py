@@ -1,0 +1,70 @@
+"""Monolithic definitions of what the looped einsums compute.
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+[OV] = Wang et al., "Overlap Communication with Dependent Computation via
+Decomposition in Large Deep Learning Models", ASPLOS'23.
+
+The decomposed loop is semantically equal to the original collective followed
+by (or preceded by) the original einsum ([OV] Section 4), so the plain
+definition is: gather the shards by partition ID, then one matmul; or one
+matmul per rank, then reduce-scatter.  Orientation is mathematical: left
+factor [m, k] times right factor [k, n], float64.
+
+Parity pins (tests/test_oracle_einsum.py): a pure-Python triple loop on tiny
+inputs, the N = 1 reduction to a plain matmul, bit-equality with the
+brute-force loop simulation on exact-integer inputs, and the AllReduce =
+ReduceScatter + AllGather identity.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .ring import allgather, reducescatter
+
+
+def allgather_einsum(mode: str, looped: list[np.ndarray],
+                     local: list[np.ndarray]) -> list[np.ndarray]:
+    """Result of AllGather(looped shards) followed by the einsum with each
+    rank's local operand ([OV] Section 5.1 cases 1 and 2).
+
+      lhs_rows : Y_r = concat_rows(A_0..A_{N-1}) @ B_r      (case 1)
+      rhs_cols : Y_r = A_r @ concat_cols(B_0..B_{N-1})      (case 1)
+      lhs_cols : Y_r = concat_cols(A_0..A_{N-1}) @ B_r      (case 2)
+      rhs_rows : Y_r = A_r @ concat_rows(B_0..B_{N-1})      (case 2)
+    """
+    if mode == "lhs_rows":
+        full = allgather(looped, axis=0)
+        return [full @ b for b in local]
+    if mode == "rhs_cols":
+        full = allgather(looped, axis=1)
+        return [a @ full for a in local]
+    if mode == "lhs_cols":
+        full = allgather(looped, axis=1)
+        return [full @ b for b in local]
+    if mode == "rhs_rows":
+        full = allgather(looped, axis=0)
+        return [a @ full for a in local]
+    raise ValueError(mode)
+
+
+def einsum_reducescatter(mode: str, a: list[np.ndarray],
+                         b: list[np.ndarray]) -> list[np.ndarray]:
+    """Result of each rank's full einsum followed by ReduceScatter along the
+    result's partitioned non-contracting dim ([OV] Section 5.1).
+
+      slice_lhs_rows : out_r = sum_q (A_q @ B_q)[rows of shard r]
+      slice_rhs_cols : out_r = sum_q (A_q @ B_q)[cols of shard r]
+    """
+    fulls = [x @ y for x, y in zip(a, b)]
+    axis = 0 if mode == "slice_lhs_rows" else 1
+    if mode not in ("slice_lhs_rows", "slice_rhs_cols"):
+        raise ValueError(mode)
+    return reducescatter(fulls, axis=axis)
+
+
+def local_matmuls(a: list[np.ndarray], b: list[np.ndarray]) -> list[np.ndarray]:
+    """The per-rank MatMul of two tensors sliced on the contraction dim,
+    which yields one local (rank-private) partial per rank (CoCoNet, Figure 3
+    program: MatMul of the sliced input and sliced weight)."""
+    return [x @ y for x, y in zip(a, b)]

@@ -1,0 +1,57 @@
+"""The fused reduce epilogue: sum of N partials, + bias, dropout, + residual.
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+[CC] = CoCoNet, "Breaking the Computation and Communication Abstraction
+Barrier in Distributed Machine Learning Workloads", ASPLOS'22.
+
+Order of operations from the [CC] Figure 3 program (the Megatron
+self-attention tail): the local MatMul partials are summed by AllReduce(+),
+the bias is added with PyTorch broadcasting (bias [cols] repeated over rows),
+dropout is applied, and the residual is added.  FusedAllReduce ([CC], fused
+collective communication) performs exactly these operations while the summed
+values are still in registers; the fusion changes where the values live, not
+what is computed, so the plain definition below is the oracle.
+
+Dropout is read as inverted dropout with p the drop probability: kept values
+are multiplied by 1 / (1 - p), dropped ones become 0.  The keep decision
+comes from oracle.philox.keep_mask.
+
+Float64 throughout; the result is rounded to the output dtype only by the
+caller's comparison.
+
+Parity pins (tests/test_oracle_epilogue.py): a per-element pure-Python loop on
+small shapes, p = 0 (exactly sum + bias + residual), p = 1 (exactly the
+residual), linearity in the partials, and the N = 1 case.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .philox import keep_mask
+
+
+def fused_reduce_epilogue(partials, bias, residual, p: float, seed: int,
+                          offset: int, row0: int = 0, col0: int = 0,
+                          mask_ld: int | None = None):
+    """out = residual + keep * (sum_k partials[k] + bias) * 1/(1-p).
+
+    partials: list of [rows, cols] arrays; bias: [cols] or None;
+    residual: [rows, cols] or None.  Returns (out float64, keep bool)."""
+    parts = [np.asarray(x, dtype=np.float64) for x in partials]
+    rows, cols = parts[0].shape
+    s = parts[0].copy()
+    for x in parts[1:]:
+        s = s + x                                  # AllReduce(+)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[None, :]
+    keep = keep_mask(rows, cols, p, seed, offset, row0, col0,
+                     mask_ld if mask_ld is not None else col0 + cols)
+    if p > 0.0:
+        scale = 1.0 / (1.0 - p) if p < 1.0 else 0.0
+        d = np.where(keep, s * scale, 0.0)
+    else:
+        d = s
+    if residual is not None:
+        d = d + np.asarray(residual, dtype=np.float64)
+    return d, keep

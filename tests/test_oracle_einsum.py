@@ -1,0 +1,128 @@
+"""Pins for the monolithic einsum definitions (oracle.einsum): a pure-Python
+triple loop on tiny inputs, the N = 1 reduction to a plain matmul, the fp64
+agreement of the simulated loop with the definition on random inputs."""
+
+import numpy as np
+import pytest
+
+from oracle import einsum, ring
+
+
+def _loop_matmul(a, b):
+    m, k = a.shape
+    k2, n = b.shape
+    assert k == k2
+    out = [[0.0] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            s = 0.0
+            for t in range(k):
+                s += float(a[i, t]) * float(b[t, j])
+            out[i][j] = s
+    return np.array(out)
+
+
+def _shards(n, mode, rng):
+    if mode == "rhs_cols":
+        return ([rng.standard_normal((3, 2)) for _ in range(n)],
+                [rng.standard_normal((4, 3)) for _ in range(n)])
+    if mode == "lhs_rows":
+        return ([rng.standard_normal((2, 3)) for _ in range(n)],
+                [rng.standard_normal((3, 4)) for _ in range(n)])
+    if mode == "lhs_cols":
+        return ([rng.standard_normal((4, 2)) for _ in range(n)],
+                [rng.standard_normal((2 * n, 3)) for _ in range(n)])
+    return ([rng.standard_normal((2, 3)) for _ in range(n)],
+            [rng.standard_normal((4, 2 * n)) for _ in range(n)])
+
+
+@pytest.mark.parametrize("mode", ring.AG_MODES)
+def test_allgather_einsum_vs_triple_loop(mode):
+    rng = np.random.default_rng(11)
+    n = 3
+    looped, local = _shards(n, mode, rng)
+    got = einsum.allgather_einsum(mode, looped, local)
+    for r in range(n):
+        # build the gathered operand element by element from partition IDs
+        if mode in ("lhs_rows", "lhs_cols"):
+            rows = []
+            if mode == "lhs_rows":
+                for s in range(n):
+                    rows.extend(looped[s].tolist())
+            else:
+                m = looped[0].shape[0]
+                rows = [sum((looped[s][i].tolist() for s in range(n)), [])
+                        for i in range(m)]
+            ref = _loop_matmul(np.array(rows), local[r])
+        else:
+            if mode == "rhs_cols":
+                k = looped[0].shape[0]
+                rows = [sum((looped[s][i].tolist() for s in range(n)), [])
+                        for i in range(k)]
+            else:
+                rows = []
+                for s in range(n):
+                    rows.extend(looped[s].tolist())
+            ref = _loop_matmul(local[r], np.array(rows))
+        np.testing.assert_allclose(got[r], ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", ring.RS_MODES)
+def test_einsum_reducescatter_vs_triple_loop(mode):
+    rng = np.random.default_rng(12)
+    n = 3
+    if mode == "slice_lhs_rows":
+        a = [rng.standard_normal((2 * n, 4)) for _ in range(n)]
+        b = [rng.standard_normal((4, 3)) for _ in range(n)]
+    else:
+        a = [rng.standard_normal((2, 4)) for _ in range(n)]
+        b = [rng.standard_normal((4, 2 * n)) for _ in range(n)]
+    got = einsum.einsum_reducescatter(mode, a, b)
+    for r in range(n):
+        acc = None
+        for q in range(n):
+            full = _loop_matmul(a[q], b[q])
+            part = full[2 * r:2 * r + 2, :] if mode == "slice_lhs_rows" \
+                else full[:, 2 * r:2 * r + 2]
+            acc = part if acc is None else acc + part
+        np.testing.assert_allclose(got[r], acc, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", ring.AG_MODES)
+def test_n1_allgather_is_plain_matmul(mode):
+    rng = np.random.default_rng(2)
+    looped, local = _shards(1, mode, rng)
+    got = einsum.allgather_einsum(mode, looped, local)[0]
+    if mode in ("lhs_rows", "lhs_cols"):
+        ref = looped[0] @ local[0]
+    else:
+        ref = local[0] @ looped[0]
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("mode", ring.RS_MODES)
+def test_n1_reducescatter_is_plain_matmul(mode):
+    rng = np.random.default_rng(3)
+    a = [rng.standard_normal((5, 4))]
+    b = [rng.standard_normal((4, 6))]
+    np.testing.assert_array_equal(einsum.einsum_reducescatter(mode, a, b)[0],
+                                  a[0] @ b[0])
+
+
+@pytest.mark.parametrize("mode", ring.AG_MODES)
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_loop_agrees_with_definition_random_fp64(mode, n):
+    rng = np.random.default_rng(100 + n)
+    looped, local = _shards(n, mode, rng)
+    outs, _, _ = ring.simulate_allgather_einsum(mode, looped, local)
+    ref = einsum.allgather_einsum(mode, looped, local)
+    for o, r in zip(outs, ref):
+        np.testing.assert_allclose(o, r, rtol=1e-12, atol=1e-12)
+
+
+def test_local_matmuls():
+    rng = np.random.default_rng(4)
+    a = [rng.standard_normal((3, 2)) for _ in range(2)]
+    b = [rng.standard_normal((2, 4)) for _ in range(2)]
+    for got, x, y in zip(einsum.local_matmuls(a, b), a, b):
+        np.testing.assert_allclose(got, _loop_matmul(x, y), rtol=1e-13, atol=1e-13)

@@ -1,0 +1,71 @@
+"""Pins for oracle.epilogue: a per-element pure-Python loop, p = 0 and p = 1,
+linearity in the partials, N = 1."""
+
+import numpy as np
+import pytest
+
+from oracle import epilogue, philox
+
+
+def _per_element(partials, bias, residual, p, seed, offset, row0, col0, ld):
+    rows, cols = partials[0].shape
+    t = philox.keep_threshold(p)
+    out = np.zeros((rows, cols))
+    for i in range(rows):
+        for j in range(cols):
+            s = 0.0
+            for x in partials:
+                s += float(x[i, j])
+            s += float(bias[j])
+            e = (row0 + i) * ld + (col0 + j)
+            w = int(philox.element_words(np.array([e], dtype=np.uint64), seed, offset)[0])
+            d = s / (1.0 - p) if w >= t else 0.0
+            out[i, j] = d + float(residual[i, j])
+    return out
+
+
+@pytest.mark.parametrize("n", [1, 2, 5])
+def test_fused_epilogue_vs_per_element_loop(n):
+    rng = np.random.default_rng(n)
+    rows, cols = 5, 13
+    parts = [rng.uniform(-1, 1, (rows, cols)) for _ in range(n)]
+    bias = rng.uniform(-1, 1, cols)
+    res = rng.uniform(-1, 1, (rows, cols))
+    got, _ = epilogue.fused_reduce_epilogue(parts, bias, res, 0.3, 42, 7,
+                                            row0=3, col0=5, mask_ld=40)
+    ref = _per_element(parts, bias, res, 0.3, 42, 7, 3, 5, 40)
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_p0_is_sum_bias_residual():
+    rng = np.random.default_rng(1)
+    parts = [rng.standard_normal((4, 8)) for _ in range(3)]
+    bias = rng.standard_normal(8)
+    res = rng.standard_normal((4, 8))
+    got, keep = epilogue.fused_reduce_epilogue(parts, bias, res, 0.0, 0, 0)
+    assert keep.all()
+    np.testing.assert_allclose(got, parts[0] + parts[1] + parts[2] + bias + res,
+                               rtol=1e-15, atol=1e-15)
+
+
+def test_p1_is_residual():
+    rng = np.random.default_rng(2)
+    parts = [rng.standard_normal((4, 8)) for _ in range(2)]
+    res = rng.standard_normal((4, 8))
+    got, keep = epilogue.fused_reduce_epilogue(parts, np.ones(8), res, 1.0, 0, 0)
+    assert not keep.any()
+    np.testing.assert_array_equal(got, res)
+
+
+def test_linear_in_partials_and_kept_scale():
+    rng = np.random.default_rng(3)
+    parts = [rng.standard_normal((6, 16)) for _ in range(2)]
+    zero_b, zero_r = np.zeros(16), np.zeros((6, 16))
+    y1, k1 = epilogue.fused_reduce_epilogue(parts, zero_b, zero_r, 0.25, 3, 4)
+    y2, k2 = epilogue.fused_reduce_epilogue([2 * x for x in parts], zero_b, zero_r,
+                                            0.25, 3, 4)
+    assert np.array_equal(k1, k2)
+    np.testing.assert_allclose(y2, 2 * y1, rtol=1e-15)
+    s = parts[0] + parts[1]
+    np.testing.assert_allclose(y1[k1], s[k1] / 0.75, rtol=1e-15)
+    assert np.all(y1[~k1] == 0)
