@@ -1,0 +1,227 @@
+"""Thin Python binding over the C ABI: torch tensors in, raw pointers out.
+
+Every function here only marshals arguments (pointers, extents, leading
+dimensions, the current stream) and calls the function of the same name in
+libcce.so; all computation runs in the library's HIP kernels.  torch is used
+for device memory and streams only.
+
+Layout reminder (see include/cce.h): a product is A * B^T with A [M, K] and
+B^T [N, K] both row-major; tensors must be 2-D with unit column stride.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_GELU, CCE_FLAG_SERIAL, AG_MODES, RS_MODES,
+                   cce_mat, check, lib, ptr_array)
+
+__all__ = [
+    "Context", "cce_shard_schedule", "cce_looped_allgather_einsum",
+    "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
+    "cce_looped_einsum_reducescatter_workspace", "cce_grouped_gemm",
+    "cce_fused_reduce_epilogue", "cce_describe_plan", "cce_version",
+    "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "AG_MODES", "RS_MODES",
+]
+
+_DT = {torch.float32: CCE_F32, torch.bfloat16: CCE_BF16}
+_DT_NAME = {"f32": CCE_F32, "bf16": CCE_BF16, "fp32": CCE_F32}
+
+
+def _dtype(x) -> int:
+    if isinstance(x, torch.dtype):
+        if x not in _DT:
+            raise TypeError(f"unsupported dtype {x}")
+        return _DT[x]
+    if isinstance(x, str):
+        return _DT_NAME[x]
+    return int(x)
+
+
+def _mat(t: torch.Tensor) -> cce_mat:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("tensor must have unit column stride")
+    if t.shape[1] == 0:
+        ld = 0                                   # empty rows: no element is addressed
+    elif t.shape[0] > 1:
+        ld = t.stride(0)
+    else:
+        ld = max(t.shape[1], t.stride(0))
+    return cce_mat(t.shape[0], t.shape[1], ld)
+
+
+def _same(ts, what):
+    m0 = _mat(ts[0])
+    for t in ts[1:]:
+        m = _mat(t)
+        if (m.rows, m.cols, m.ld) != (m0.rows, m0.cols, m0.ld) or t.dtype != ts[0].dtype:
+            raise ValueError(f"all {what} tensors must share shape, stride and dtype")
+    return m0
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Context:
+    """Owns a cce_ctx (copy stream + event pool) on one device."""
+
+    def __init__(self, device: int | torch.device = 0):
+        if isinstance(device, torch.device):
+            device = device.index or 0
+        self.device = int(device)
+        self._h = ctypes.c_void_p()
+        check(lib().cce_ctx_create(self.device, ctypes.byref(self._h)), "cce_ctx_create")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            lib().cce_ctx_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cce_version() -> str:
+    return lib().cce_version().decode()
+
+
+def cce_shard_schedule(n_ranks: int, kind: int) -> list[list[int]]:
+    """table[i][r]: shard ID rank r works on in iteration i (kind 0
+    AllGather, 1 ReduceScatter)."""
+    buf = (ctypes.c_int32 * (n_ranks * n_ranks))()
+    check(lib().cce_shard_schedule(n_ranks, kind, buf), "cce_shard_schedule")
+    return [[buf[i * n_ranks + r] for r in range(n_ranks)] for i in range(n_ranks)]
+
+
+def cce_describe_plan(kind: int, n_ranks: int, mode: int, out_dtype=CCE_BF16, flags: int = 0) -> str:
+    need = ctypes.c_size_t()
+    check(lib().cce_describe_plan(kind, n_ranks, mode, _dtype(out_dtype), flags, None, 0,
+                                  ctypes.byref(need)), "cce_describe_plan")
+    buf = ctypes.create_string_buffer(need.value)
+    check(lib().cce_describe_plan(kind, n_ranks, mode, _dtype(out_dtype), flags, buf, need.value,
+                                  ctypes.byref(need)), "cce_describe_plan")
+    return buf.value.decode()
+
+
+def cce_looped_allgather_einsum_workspace(n_ranks, mode, in_dtype, out_dtype, looped_shape,
+                                          out_shape) -> int:
+    """looped_shape/out_shape: (rows, cols[, ld])."""
+    def m(s):
+        return cce_mat(s[0], s[1], s[2] if len(s) > 2 else s[1])
+    nb = ctypes.c_size_t()
+    mode = AG_MODES[mode] if isinstance(mode, str) else mode
+    check(lib().cce_looped_allgather_einsum_workspace(n_ranks, mode, _dtype(in_dtype),
+                                                      _dtype(out_dtype), m(looped_shape),
+                                                      m(out_shape), ctypes.byref(nb)),
+          "cce_looped_allgather_einsum_workspace")
+    return nb.value
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def cce_looped_allgather_einsum(ctx: Context, mode, looped, local, out, workspace=None,
+                                flags: int = 0, stream=None):
+    """Looped AllGather-Einsum over n = len(looped) ranks; writes out[r]."""
+    n = len(looped)
+    mode = AG_MODES[mode] if isinstance(mode, str) else mode
+    lm, cm, om = _same(looped, "looped"), _same(local, "local"), _same(out, "out")
+    in_t, out_t = _dtype(looped[0].dtype), _dtype(out[0].dtype)
+    need = cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t,
+                                                 (lm.rows, lm.cols, lm.ld),
+                                                 (om.rows, om.cols, om.ld))
+    ws, wsb = _workspace(need, out[0].device, workspace)
+    check(lib().cce_looped_allgather_einsum(
+        ctx.handle, n, mode, in_t, out_t,
+        ptr_array([t.data_ptr() for t in looped]), lm,
+        ptr_array([t.data_ptr() for t in local]), cm,
+        ptr_array([t.data_ptr() for t in out]), om,
+        ws.data_ptr() if ws is not None else None, wsb, flags,
+        _stream(stream, out[0].device)), "cce_looped_allgather_einsum")
+    return out
+
+
+def cce_looped_einsum_reducescatter_workspace(n_ranks, mode, out_shape) -> int:
+    nb = ctypes.c_size_t()
+    mode = RS_MODES[mode] if isinstance(mode, str) else mode
+    s = out_shape
+    check(lib().cce_looped_einsum_reducescatter_workspace(
+        n_ranks, mode, CCE_F32, cce_mat(s[0], s[1], s[2] if len(s) > 2 else s[1]),
+        ctypes.byref(nb)), "cce_looped_einsum_reducescatter_workspace")
+    return nb.value
+
+
+def cce_looped_einsum_reducescatter(ctx: Context, mode, a, b, out, workspace=None,
+                                    flags: int = 0, stream=None):
+    """Looped Einsum-ReduceScatter over n = len(a) ranks; writes out[r]."""
+    n = len(a)
+    mode = RS_MODES[mode] if isinstance(mode, str) else mode
+    am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
+    in_t, out_t = _dtype(a[0].dtype), _dtype(out[0].dtype)
+    need = cce_looped_einsum_reducescatter_workspace(n, mode, (om.rows, om.cols, om.ld))
+    ws, wsb = _workspace(need, out[0].device, workspace)
+    check(lib().cce_looped_einsum_reducescatter(
+        ctx.handle, n, mode, in_t, CCE_F32, out_t,
+        ptr_array([t.data_ptr() for t in a]), am,
+        ptr_array([t.data_ptr() for t in b]), bm,
+        ptr_array([t.data_ptr() for t in out]), om,
+        ws.data_ptr() if ws is not None else None, wsb, flags,
+        _stream(stream, out[0].device)), "cce_looped_einsum_reducescatter")
+    return out
+
+
+def cce_grouped_gemm(ctx: Context, a, b, c, gelu: bool = False, stream=None):
+    """c[g] = a[g] @ b[g]^T for every g, one launch."""
+    am, bm, cm = _same(a, "a"), _same(b, "b"), _same(c, "c")
+    check(lib().cce_grouped_gemm(
+        ctx.handle, len(a), _dtype(a[0].dtype), _dtype(c[0].dtype),
+        ptr_array([t.data_ptr() for t in a]), am,
+        ptr_array([t.data_ptr() for t in b]), bm,
+        ptr_array([t.data_ptr() for t in c]), cm,
+        CCE_FLAG_GELU if gelu else 0, _stream(stream, c[0].device)), "cce_grouped_gemm")
+    return c
+
+
+def cce_fused_reduce_epilogue(ctx: Context, partials, bias, residual, out, p_drop: float,
+                              seed: int = 0, offset: int = 0, mask_row0: int = 0,
+                              mask_col0: int = 0, mask_ld: int | None = None, mask_out=None,
+                              stream=None):
+    """out = residual + keep * (sum(partials) + bias) / (1 - p_drop)."""
+    pm = _same(partials, "partial")
+    om = _mat(out)
+    rm = _mat(residual) if residual is not None else None
+    if mask_ld is None:
+        mask_ld = mask_col0 + pm.cols
+    bias_t = _dtype(bias.dtype) if bias is not None else _dtype(out.dtype)
+    res_t = _dtype(residual.dtype) if residual is not None else _dtype(out.dtype)
+    check(lib().cce_fused_reduce_epilogue(
+        ctx.handle, len(partials), _dtype(partials[0].dtype),
+        ptr_array([t.data_ptr() for t in partials]), pm,
+        bias.data_ptr() if bias is not None else None, bias_t,
+        residual.data_ptr() if residual is not None else None, res_t,
+        rm.ld if rm is not None else pm.cols,
+        float(p_drop), int(seed), int(offset), int(mask_row0), int(mask_col0), int(mask_ld),
+        out.data_ptr(), _dtype(out.dtype), om.ld,
+        mask_out.data_ptr() if mask_out is not None else None, 0,
+        _stream(stream, out.device)), "cce_fused_reduce_epilogue")
+    return out

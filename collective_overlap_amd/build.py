@@ -1,0 +1,95 @@
+"""Build libcce.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
+
+Usage: python -m collective_overlap_amd.build [--jobs N]
+
+The library links against the HIP runtime that torch ships (torch/lib), so
+that the streams and device pointers torch hands over belong to the same
+runtime instance; /opt/rocm/lib is the fallback search path when the library
+is loaded without torch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libcce.so")
+ROOT = os.path.dirname(PKG)
+
+SOURCES = ["gemm.hip", "epilogue.hip", "plan.cpp", "abi.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def torch_lib_dir() -> str | None:
+    try:
+        import importlib.util
+        spec = importlib.util.find_spec("torch")
+        if spec is None or not spec.submodule_search_locations:
+            return None
+        d = os.path.join(list(spec.submodule_search_locations)[0], "lib")
+        return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
+    except Exception:
+        return None
+
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # Packed fp32 VALU ops stay off: hipcc -O3 would otherwise form them from
+    # plain float code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def compile_one(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"]
+    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", LIB + ".tmp", *objs]
+    tl = torch_lib_dir()
+    if tl:
+        link += [f"-L{tl}", f"-Wl,-rpath,{tl}"]
+    link += ["-Wl,-rpath,/opt/rocm/lib", "-lamdhip64"]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout}\n{r.stderr}")
+    os.replace(LIB + ".tmp", LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=min(4, os.cpu_count() or 1))
+    a = ap.parse_args(argv)
+    build(a.jobs, verbose=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,821 @@
+// C ABI of the library: argument validation, contexts, workspace layout and
+// the executor that turns a plan (plan.cpp) into HIP stream operations.
+//
+// Stream/event discipline follows the completion-handle pattern of MCR-DL
+// (Anthony et al., "MCR-DL: Mix-and-Match Communication Runtime for Deep
+// Learning", its synchronization section): transfers are posted to an
+// internal communication stream, an event is recorded after them, and the
+// consumer waits on that event instead of synchronising the host.  Each call
+// forks the copy stream from the caller's stream and joins it back.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cce_internal.hpp"
+
+struct cce_ctx {
+  int device = 0;
+  hipStream_t copy = nullptr;
+  std::vector<hipEvent_t> events;
+};
+
+namespace cce {
+
+namespace {
+thread_local std::string g_err;
+
+constexpr int64_t kMaxOperandBytes = (int64_t{1} << 31) - 256;
+
+size_t esize(cce_dtype t) { return t == CCE_F32 ? 4 : 2; }
+bool dtype_ok(int t) { return t == CCE_F32 || t == CCE_BF16; }
+int64_t align256(int64_t b) { return (b + 255) & ~int64_t{255}; }
+int64_t round8(int64_t v) { return (v + 7) & ~int64_t{7}; }
+
+int64_t span_bytes(const cce_mat& m, size_t es) {
+  if (m.rows <= 0 || m.cols <= 0) return 0;
+  return ((m.rows - 1) * m.ld + m.cols) * static_cast<int64_t>(es);
+}
+
+std::string mat_str(const cce_mat& m) {
+  return "[" + std::to_string(m.rows) + "," + std::to_string(m.cols) + "] ld " + std::to_string(m.ld);
+}
+
+cce_status check_mat(const char* name, const cce_mat& m) {
+  if (m.rows < 0 || m.cols < 0 || m.ld < m.cols || m.ld < 0)
+    return fail(CCE_EINVAL, std::string(name) + ": bad extents " + mat_str(m));
+  if (m.ld % 8 != 0)
+    return fail(CCE_EUNSUPPORTED, std::string(name) + ": ld must be a multiple of 8, got " + mat_str(m));
+  if (m.rows > 0x7fffffff || m.cols > 0x7fffffff || m.ld > 0x7fffffff)
+    return fail(CCE_EUNSUPPORTED, std::string(name) + ": extent exceeds 2^31");
+  return CCE_OK;
+}
+
+cce_status check_ptr(const char* name, const void* p, int64_t span) {
+  if (span == 0) return CCE_OK;
+  if (!p) return fail(CCE_EINVAL, std::string(name) + ": NULL pointer");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(CCE_EUNSUPPORTED, std::string(name) + ": pointer not 16-byte aligned");
+  return CCE_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  std::string name;
+  bool writes;
+};
+
+// Outputs may overlap nothing; inputs may overlap each other.
+cce_status check_overlaps(const std::vector<Range>& rs) {
+  for (size_t i = 0; i < rs.size(); ++i) {
+    if (rs[i].hi <= rs[i].lo) continue;
+    for (size_t j = i + 1; j < rs.size(); ++j) {
+      if (rs[j].hi <= rs[j].lo) continue;
+      if (!rs[i].writes && !rs[j].writes) continue;
+      if (rs[i].lo < rs[j].hi && rs[j].lo < rs[i].hi)
+        return fail(CCE_EINVAL, rs[i].name + " overlaps " + rs[j].name);
+    }
+  }
+  return CCE_OK;
+}
+
+Range range_of(const void* p, int64_t span, const std::string& name, bool writes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(span), name, writes};
+}
+
+#define CCE_TRY(expr)                       \
+  do {                                      \
+    cce_status _s = (expr);                 \
+    if (_s != CCE_OK) return _s;            \
+  } while (0)
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t _e = (expr);                                                        \
+    if (_e != hipSuccess)                                                          \
+      return fail(CCE_EHIP, std::string(#expr) + ": " + hipGetErrorString(_e));    \
+  } while (0)
+
+// Makes ctx->device current for the duration of a call.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+    if (prev_ != dev) hipSetDevice(dev);
+    dev_ = dev;
+  }
+  ~DeviceGuard() {
+    if (prev_ >= 0 && prev_ != dev_) hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = -1, dev_ = 0;
+};
+
+cce_status ensure_events(cce_ctx* ctx, int n) {
+  while (static_cast<int>(ctx->events.size()) < n) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->events.push_back(e);
+  }
+  return CCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// AllGather: shapes and workspace
+// ---------------------------------------------------------------------------
+struct AgGeom {
+  int n = 0;
+  int mode = 0;
+  bool case2 = false;
+  bool case2_ws = false;
+  int64_t M = 0, N = 0, K = 0;          // per-iteration GEMM
+  int64_t recv_bytes = 0;               // one receive buffer (packed)
+  int64_t acc_ld = 0, acc_bytes = 0;    // case-2 fp32 accumulator
+  int64_t total = 0;
+};
+
+cce_status ag_geometry(int n, int mode, cce_dtype in_t, cce_dtype out_t, const cce_mat& looped,
+                       const cce_mat* local, const cce_mat& out, AgGeom& g) {
+  if (n < 1 || n > CCE_MAX_RANKS)
+    return fail(n < 1 ? CCE_EINVAL : CCE_EUNSUPPORTED, "n_ranks out of range: " + std::to_string(n));
+  if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
+  if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
+  CCE_TRY(check_mat("looped_shard", looped));
+  CCE_TRY(check_mat("out_shape", out));
+  if (local) CCE_TRY(check_mat("local_shape", *local));
+  g.n = n;
+  g.mode = mode;
+  g.case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
+  g.case2_ws = g.case2 && out_t == CCE_BF16 && n > 1;
+  const int64_t nn = n;
+  switch (mode) {
+    case CCE_AG_LHS_ROWS:
+      g.M = looped.rows; g.K = looped.cols; g.N = out.cols;
+      if (out.rows != nn * looped.rows) return fail(CCE_EINVAL, "out rows must be n * looped rows");
+      if (local && (local->rows != out.cols || local->cols != looped.cols))
+        return fail(CCE_EINVAL, "local must be [out cols, looped cols] " + mat_str(*local));
+      break;
+    case CCE_AG_RHS_COLS:
+      g.M = out.rows; g.K = looped.cols; g.N = looped.rows;
+      if (out.cols != nn * looped.rows) return fail(CCE_EINVAL, "out cols must be n * looped rows");
+      if (local && (local->rows != out.rows || local->cols != looped.cols))
+        return fail(CCE_EINVAL, "local must be [out rows, looped cols] " + mat_str(*local));
+      break;
+    case CCE_AG_LHS_COLS:
+      g.M = looped.rows; g.K = looped.cols; g.N = out.cols;
+      if (out.rows != looped.rows) return fail(CCE_EINVAL, "out rows must equal looped rows");
+      if (local && (local->rows != out.cols || local->cols != nn * looped.cols))
+        return fail(CCE_EINVAL, "local must be [out cols, n * looped cols] " + mat_str(*local));
+      break;
+    case CCE_AG_RHS_ROWS:
+      g.M = out.rows; g.K = looped.cols; g.N = looped.rows;
+      if (out.cols != looped.rows) return fail(CCE_EINVAL, "out cols must equal looped rows");
+      if (local && (local->rows != out.rows || local->cols != nn * looped.cols))
+        return fail(CCE_EINVAL, "local must be [out rows, n * looped cols] " + mat_str(*local));
+      break;
+  }
+  if (g.K % 8 != 0) return fail(CCE_EUNSUPPORTED, "contraction length must be a multiple of 8");
+  g.recv_bytes = (n > 1) ? align256(looped.rows * looped.cols * static_cast<int64_t>(esize(in_t))) : 0;
+  if (g.case2_ws) {
+    g.acc_ld = round8(out.cols);
+    g.acc_bytes = align256(out.rows * g.acc_ld * 4);
+  }
+  g.total = 2 * nn * g.recv_bytes + (g.case2_ws ? nn * g.acc_bytes : 0);
+  return CCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// ReduceScatter: shapes and workspace
+// ---------------------------------------------------------------------------
+struct RsGeom {
+  int n = 0;
+  int mode = 0;
+  int64_t K = 0;
+  int64_t shard = 0;              // m_s (rows) or n_s (cols)
+  int64_t other = 0;              // N (cols) or M (rows)
+  int64_t h0 = 0, h1 = 0;         // half extents along the sliced dim
+  int64_t acc_ld = 0, half_bytes = 0;
+  int64_t total = 0;
+};
+
+cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsGeom& g) {
+  if (n < 1 || n > CCE_MAX_RANKS)
+    return fail(n < 1 ? CCE_EINVAL : CCE_EUNSUPPORTED, "n_ranks out of range: " + std::to_string(n));
+  if (mode != CCE_RS_SLICE_LHS_ROWS && mode != CCE_RS_SLICE_RHS_COLS)
+    return fail(CCE_EINVAL, "bad ReduceScatter mode");
+  if (!dtype_ok(acc_t)) return fail(CCE_EINVAL, "bad acc dtype");
+  if (acc_t != CCE_F32) return fail(CCE_EUNSUPPORTED, "the travelling accumulator is fp32 only");
+  CCE_TRY(check_mat("out_shard", out));
+  g.n = n;
+  g.mode = mode;
+  if (mode == CCE_RS_SLICE_LHS_ROWS) {
+    g.shard = out.rows;
+    g.other = out.cols;
+    g.h0 = (g.shard + 1) / 2;
+    g.h1 = g.shard - g.h0;
+    g.acc_ld = round8(g.other);
+    g.half_bytes = align256(g.h0 * g.acc_ld * 4);
+  } else {
+    g.shard = out.cols;
+    g.other = out.rows;
+    g.h0 = round8((g.shard + 1) / 2);
+    if (g.h0 >= g.shard) g.h0 = g.shard;
+    g.h1 = g.shard - g.h0;
+    g.acc_ld = round8(g.h0);
+    g.half_bytes = align256(g.other * g.acc_ld * 4);
+  }
+  g.total = (n > 1) ? 2LL * n * 2 * g.half_bytes : 0;
+  return CCE_OK;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_err = msg; }
+void clear_error() { g_err.clear(); }
+cce_status fail(cce_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Executors
+// ---------------------------------------------------------------------------
+namespace {
+
+hipStream_t stream_of(const Op& o, hipStream_t compute, hipStream_t copy, bool serial) {
+  return (serial || o.stream == S_COMPUTE) ? compute : copy;
+}
+
+cce_status run_events(cce_ctx* ctx, const Op& o, hipStream_t s) {
+  if (o.kind == OP_RECORD) HIP_TRY(hipEventRecord(ctx->events[o.event], s));
+  if (o.kind == OP_WAIT) HIP_TRY(hipStreamWaitEvent(s, ctx->events[o.event], 0));
+  return CCE_OK;
+}
+
+struct AgCall {
+  AgGeom g;
+  cce_dtype in_t, out_t;
+  const void* const* looped;
+  cce_mat lshape;
+  const void* const* local;
+  cce_mat local_shape;
+  void* const* out;
+  cce_mat oshape;
+  char* ws;
+  bool gelu;
+};
+
+// pointer + leading dimension of a symbolic buffer
+struct PtrLd {
+  char* p;
+  int64_t ld;
+};
+
+PtrLd ag_resolve(const AgCall& c, const BufRef& b) {
+  const int r = b.rank;
+  switch (b.kind) {
+    case B_LOOPED: return {const_cast<char*>(static_cast<const char*>(c.looped[r])), c.lshape.ld};
+    case B_LOCAL: return {const_cast<char*>(static_cast<const char*>(c.local[r])), c.local_shape.ld};
+    case B_OUT: return {static_cast<char*>(c.out[r]), c.oshape.ld};
+    case B_RECV:
+      return {c.ws + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes, c.lshape.cols};
+    case B_CASE2:
+      return {c.ws + 2LL * c.g.n * c.g.recv_bytes + r * c.g.acc_bytes, c.g.acc_ld};
+  }
+  return {nullptr, 0};
+}
+
+cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream_t compute) {
+  const size_t ein = esize(c.in_t);
+  for (const Op& o : plan.ops) {
+    hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
+    if (o.kind == OP_RECORD || o.kind == OP_WAIT) {
+      CCE_TRY(run_events(ctx, o, s));
+      continue;
+    }
+    if (o.kind == OP_COPY) {
+      const int64_t w = c.lshape.cols * static_cast<int64_t>(ein);
+      for (const Item& it : o.items) {
+        const PtrLd src = ag_resolve(c, it.a), dst = ag_resolve(c, it.c);
+        if (c.lshape.rows == 0 || w == 0) continue;
+        if (src.ld == dst.ld) {
+          HIP_TRY(hipMemcpyAsync(dst.p, src.p, c.lshape.rows * src.ld * ein, hipMemcpyDeviceToDevice, s));
+        } else {
+          HIP_TRY(hipMemcpy2DAsync(dst.p, dst.ld * ein, src.p, src.ld * ein, w, c.lshape.rows,
+                                   hipMemcpyDeviceToDevice, s));
+        }
+      }
+      continue;
+    }
+    // GEMM
+    GemmLaunch L;
+    L.groups = plan.n;
+    L.M = c.g.M;
+    L.N = c.g.N;
+    L.K = c.g.K;
+    L.in_t = c.in_t;
+    L.epi = o.epi;
+    const bool last = (o.iter == plan.n - 1);
+    L.gelu = c.gelu && (!c.g.case2 || last);
+    for (const Item& it : o.items) {
+      const int r = it.rank;
+      const int64_t s_id = it.shard;
+      const PtrLd held = ag_resolve(c, it.a);
+      const PtrLd loc = ag_resolve(c, it.b);
+      const PtrLd dst = ag_resolve(c, it.c);
+      L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
+      L.ldc = dst.ld;
+      char* cptr = dst.p;
+      const int64_t eo = esize(L.out_t);
+      switch (c.g.mode) {
+        case CCE_AG_LHS_ROWS:
+          L.p.a[r] = held.p; L.lda = held.ld;
+          L.p.b[r] = loc.p; L.ldb = loc.ld;
+          cptr += s_id * c.g.M * dst.ld * eo;
+          break;
+        case CCE_AG_RHS_COLS:
+          L.p.a[r] = loc.p; L.lda = loc.ld;
+          L.p.b[r] = held.p; L.ldb = held.ld;
+          cptr += s_id * c.g.N * eo;
+          break;
+        case CCE_AG_LHS_COLS:
+          L.p.a[r] = held.p; L.lda = held.ld;
+          L.p.b[r] = loc.p + s_id * c.g.K * ein; L.ldb = loc.ld;
+          break;
+        case CCE_AG_RHS_ROWS:
+          L.p.a[r] = loc.p + s_id * c.g.K * ein; L.lda = loc.ld;
+          L.p.b[r] = held.p; L.ldb = held.ld;
+          break;
+      }
+      L.p.c[r] = cptr;
+      if (it.has_cin) {
+        const PtrLd cin = ag_resolve(c, it.cin);
+        L.p.cin[r] = reinterpret_cast<const float*>(cin.p);
+        L.ldcin = cin.ld;
+      } else {
+        L.p.cin[r] = nullptr;
+      }
+    }
+    CCE_TRY(launch_grouped_gemm(L, compute));
+  }
+  return CCE_OK;
+}
+
+struct RsCall {
+  RsGeom g;
+  cce_dtype in_t, out_t;
+  const void* const* a;
+  cce_mat ashape;
+  const void* const* b;
+  cce_mat bshape;
+  void* const* out;
+  cce_mat oshape;
+  char* ws;
+};
+
+PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
+  const int r = b.rank;
+  switch (b.kind) {
+    case B_A: return {const_cast<char*>(static_cast<const char*>(c.a[r])), c.ashape.ld};
+    case B_B: return {const_cast<char*>(static_cast<const char*>(c.b[r])), c.bshape.ld};
+    case B_OUT: {
+      const int64_t eo = esize(c.out_t);
+      char* p = static_cast<char*>(c.out[r]);
+      if (b.half == 1)
+        p += (c.g.mode == CCE_RS_SLICE_LHS_ROWS) ? c.g.h0 * c.oshape.ld * eo : c.g.h0 * eo;
+      return {p, c.oshape.ld};
+    }
+    case B_ACC:
+      return {c.ws + ((static_cast<int64_t>(b.parity) * c.g.n + r) * 2 + b.half) * c.g.half_bytes,
+              c.g.acc_ld};
+  }
+  return {nullptr, 0};
+}
+
+cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream_t compute) {
+  const size_t ein = esize(c.in_t);
+  const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
+  for (const Op& o : plan.ops) {
+    hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
+    if (o.kind == OP_RECORD || o.kind == OP_WAIT) {
+      CCE_TRY(run_events(ctx, o, s));
+      continue;
+    }
+    const int64_t ext = (o.half == 0) ? c.g.h0 : c.g.h1;   // extent along the sliced dim
+    if (o.kind == OP_COPY) {
+      const int64_t bytes = (rows_mode ? ext * c.g.acc_ld : c.g.other * c.g.acc_ld) * 4;
+      if (bytes == 0) continue;
+      for (const Item& it : o.items) {
+        const PtrLd src = rs_resolve(c, it.a), dst = rs_resolve(c, it.c);
+        HIP_TRY(hipMemcpyAsync(dst.p, src.p, bytes, hipMemcpyDeviceToDevice, s));
+      }
+      continue;
+    }
+    GemmLaunch L;
+    L.groups = plan.n;
+    L.K = c.g.K;
+    L.in_t = c.in_t;
+    L.epi = o.epi;
+    L.gelu = false;
+    if (rows_mode) {
+      L.M = ext;
+      L.N = c.g.other;
+    } else {
+      L.M = c.g.other;
+      L.N = ext;
+    }
+    for (const Item& it : o.items) {
+      const int r = it.rank;
+      const int64_t t = it.shard;
+      const PtrLd A = rs_resolve(c, it.a), B = rs_resolve(c, it.b), D = rs_resolve(c, it.c);
+      L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
+      const int64_t off = t * c.g.shard + o.half * c.g.h0;     // start along the sliced dim
+      if (rows_mode) {
+        L.p.a[r] = A.p + off * A.ld * ein;
+        L.p.b[r] = B.p;
+      } else {
+        L.p.a[r] = A.p;
+        L.p.b[r] = B.p + off * B.ld * ein;
+      }
+      L.lda = A.ld;
+      L.ldb = B.ld;
+      L.p.c[r] = D.p;
+      L.ldc = D.ld;
+      if (it.has_cin) {
+        const PtrLd cin = rs_resolve(c, it.cin);
+        L.p.cin[r] = reinterpret_cast<const float*>(cin.p);
+        L.ldcin = cin.ld;
+      } else {
+        L.p.cin[r] = nullptr;
+      }
+    }
+    if (L.M > 0 && L.N > 0) CCE_TRY(launch_grouped_gemm(L, compute));
+  }
+  return CCE_OK;
+}
+
+}  // namespace
+}  // namespace cce
+
+using namespace cce;
+
+extern "C" {
+
+const char* cce_status_string(cce_status s) {
+  switch (s) {
+    case CCE_OK: return "CCE_OK";
+    case CCE_EINVAL: return "CCE_EINVAL: invalid argument";
+    case CCE_EUNSUPPORTED: return "CCE_EUNSUPPORTED: unsupported argument";
+    case CCE_EWORKSPACE: return "CCE_EWORKSPACE: workspace missing or too small";
+    case CCE_EHIP: return "CCE_EHIP: HIP runtime error";
+  }
+  return "unknown cce_status";
+}
+
+const char* cce_last_error(void) { return g_err.c_str(); }
+
+const char* cce_version(void) { return "0.1.0"; }
+
+cce_status cce_ctx_create(int device, cce_ctx** out) {
+  clear_error();
+  if (!out) return fail(CCE_EINVAL, "out is NULL");
+  *out = nullptr;
+  int count = 0;
+  HIP_TRY(hipGetDeviceCount(&count));
+  if (device < 0 || device >= count) return fail(CCE_EINVAL, "bad device " + std::to_string(device));
+  DeviceGuard guard(device);
+  cce_ctx* c = new cce_ctx();
+  c->device = device;
+  hipError_t e = hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(CCE_EHIP, std::string("hipStreamCreateWithFlags: ") + hipGetErrorString(e));
+  }
+  *out = c;
+  return CCE_OK;
+}
+
+cce_status cce_ctx_destroy(cce_ctx* ctx) {
+  clear_error();
+  if (!ctx) return CCE_OK;
+  DeviceGuard guard(ctx->device);
+  hipStreamSynchronize(ctx->copy);
+  for (hipEvent_t e : ctx->events) hipEventDestroy(e);
+  hipStreamDestroy(ctx->copy);
+  delete ctx;
+  return CCE_OK;
+}
+
+cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table) {
+  clear_error();
+  if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
+  if (kind != 0 && kind != 1) return fail(CCE_EINVAL, "kind must be 0 or 1");
+  if (!table) return fail(CCE_EINVAL, "table is NULL");
+  // The schedule the plans use: read it back from the built plan itself.
+  const Plan p = (kind == 0) ? build_allgather_plan(n_ranks, CCE_AG_LHS_ROWS, false, true)
+                             : build_reducescatter_plan(n_ranks, CCE_RS_SLICE_LHS_ROWS, false, true);
+  for (const Op& o : p.ops) {
+    if (o.kind != OP_GEMM) continue;
+    for (const Item& it : o.items) table[o.iter * n_ranks + it.rank] = it.shard;
+  }
+  return CCE_OK;
+}
+
+cce_status cce_looped_allgather_einsum_workspace(int n_ranks, cce_ag_mode mode, cce_dtype in_t,
+                                                 cce_dtype out_t, cce_mat looped_shard,
+                                                 cce_mat out_shape, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(CCE_EINVAL, "bytes is NULL");
+  AgGeom g;
+  CCE_TRY(ag_geometry(n_ranks, mode, in_t, out_t, looped_shard, nullptr, out_shape, g));
+  *bytes = static_cast<size_t>(g.total);
+  return CCE_OK;
+}
+
+cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mode, cce_dtype in_t,
+                                       cce_dtype out_t, const void* const* looped,
+                                       cce_mat looped_shard, const void* const* local,
+                                       cce_mat local_shape, void* const* out, cce_mat out_shape,
+                                       void* workspace, size_t workspace_bytes, uint32_t flags,
+                                       cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU)) return fail(CCE_EINVAL, "unknown flags");
+  if (!looped || !local || !out) return fail(CCE_EINVAL, "pointer array is NULL");
+  AgGeom g;
+  CCE_TRY(ag_geometry(n_ranks, mode, in_t, out_t, looped_shard, &local_shape, out_shape, g));
+  const size_t ein = esize(in_t), eout = esize(out_t);
+  const int64_t ls = span_bytes(looped_shard, ein), cs = span_bytes(local_shape, ein),
+                os = span_bytes(out_shape, eout);
+  if (ls > kMaxOperandBytes || cs > kMaxOperandBytes)
+    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+  std::vector<Range> ranges;
+  for (int r = 0; r < n_ranks; ++r) {
+    const std::string rs = std::to_string(r);
+    CCE_TRY(check_ptr(("looped[" + rs + "]").c_str(), looped[r], ls));
+    CCE_TRY(check_ptr(("local[" + rs + "]").c_str(), local[r], cs));
+    CCE_TRY(check_ptr(("out[" + rs + "]").c_str(), out[r], os));
+    ranges.push_back(range_of(looped[r], ls, "looped[" + rs + "]", false));
+    ranges.push_back(range_of(local[r], cs, "local[" + rs + "]", false));
+    ranges.push_back(range_of(out[r], os, "out[" + rs + "]", true));
+  }
+  if (g.total > 0) {
+    if (!workspace || workspace_bytes < static_cast<size_t>(g.total))
+      return fail(CCE_EWORKSPACE, "workspace needs " + std::to_string(g.total) + " bytes");
+    CCE_TRY(check_ptr("workspace", workspace, g.total));
+    ranges.push_back(range_of(workspace, g.total, "workspace", true));
+  }
+  CCE_TRY(check_overlaps(ranges));
+  if (g.M == 0 || g.N == 0) return CCE_OK;
+
+  DeviceGuard guard(ctx->device);
+  const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
+  const Plan plan = build_allgather_plan(n_ranks, mode, g.case2_ws, serial);
+  CCE_TRY(ensure_events(ctx, plan.n_events));
+  AgCall c{g, in_t, out_t, looped, looped_shard, local, local_shape, out, out_shape,
+           static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0};
+  return ag_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
+}
+
+cce_status cce_looped_einsum_reducescatter_workspace(int n_ranks, cce_rs_mode mode, cce_dtype acc_t,
+                                                     cce_mat out_shard, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(CCE_EINVAL, "bytes is NULL");
+  RsGeom g;
+  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g));
+  *bytes = static_cast<size_t>(g.total);
+  return CCE_OK;
+}
+
+cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,
+                                           cce_dtype in_t, cce_dtype acc_t, cce_dtype out_t,
+                                           const void* const* a, cce_mat a_shape,
+                                           const void* const* b, cce_mat b_shape,
+                                           void* const* out, cce_mat out_shard, void* workspace,
+                                           size_t workspace_bytes, uint32_t flags,
+                                           cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  if (flags & ~CCE_FLAG_SERIAL) return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
+  if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
+  if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
+  RsGeom g;
+  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g));
+  CCE_TRY(check_mat("a_shape", a_shape));
+  CCE_TRY(check_mat("b_shape", b_shape));
+  const int64_t nn = n_ranks;
+  if (a_shape.cols != b_shape.cols) return fail(CCE_EINVAL, "a and b must share the contraction length");
+  g.K = a_shape.cols;
+  if (mode == CCE_RS_SLICE_LHS_ROWS) {
+    if (a_shape.rows != nn * out_shard.rows) return fail(CCE_EINVAL, "a rows must be n * out rows");
+    if (b_shape.rows != out_shard.cols) return fail(CCE_EINVAL, "b rows must equal out cols");
+  } else {
+    if (a_shape.rows != out_shard.rows) return fail(CCE_EINVAL, "a rows must equal out rows");
+    if (b_shape.rows != nn * out_shard.cols) return fail(CCE_EINVAL, "b rows must be n * out cols");
+  }
+  if (g.K % 8 != 0) return fail(CCE_EUNSUPPORTED, "contraction length must be a multiple of 8");
+  const size_t ein = esize(in_t), eout = esize(out_t);
+  const int64_t as = span_bytes(a_shape, ein), bs = span_bytes(b_shape, ein),
+                os = span_bytes(out_shard, eout);
+  if (as > kMaxOperandBytes || bs > kMaxOperandBytes)
+    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+  std::vector<Range> ranges;
+  for (int r = 0; r < n_ranks; ++r) {
+    const std::string rs = std::to_string(r);
+    CCE_TRY(check_ptr(("a[" + rs + "]").c_str(), a[r], as));
+    CCE_TRY(check_ptr(("b[" + rs + "]").c_str(), b[r], bs));
+    CCE_TRY(check_ptr(("out[" + rs + "]").c_str(), out[r], os));
+    ranges.push_back(range_of(a[r], as, "a[" + rs + "]", false));
+    ranges.push_back(range_of(b[r], bs, "b[" + rs + "]", false));
+    ranges.push_back(range_of(out[r], os, "out[" + rs + "]", true));
+  }
+  if (g.total > 0) {
+    if (!workspace || workspace_bytes < static_cast<size_t>(g.total))
+      return fail(CCE_EWORKSPACE, "workspace needs " + std::to_string(g.total) + " bytes");
+    CCE_TRY(check_ptr("workspace", workspace, g.total));
+    ranges.push_back(range_of(workspace, g.total, "workspace", true));
+  }
+  CCE_TRY(check_overlaps(ranges));
+  if (out_shard.rows == 0 || out_shard.cols == 0) return CCE_OK;
+
+  DeviceGuard guard(ctx->device);
+  const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
+  const Plan plan = build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial);
+  CCE_TRY(ensure_events(ctx, plan.n_events));
+  RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace)};
+  return rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
+}
+
+cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtype out_t,
+                            const void* const* a, cce_mat a_shape, const void* const* b,
+                            cce_mat b_shape, void* const* c, cce_mat c_shape, uint32_t flags,
+                            cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  if (flags & ~CCE_FLAG_GELU) return fail(CCE_EINVAL, "unsupported flags for grouped GEMM");
+  if (n_groups < 1) return fail(CCE_EINVAL, "n_groups < 1");
+  if (n_groups > CCE_MAX_RANKS) return fail(CCE_EUNSUPPORTED, "n_groups > CCE_MAX_RANKS");
+  if (!a || !b || !c) return fail(CCE_EINVAL, "pointer array is NULL");
+  if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
+  CCE_TRY(check_mat("a_shape", a_shape));
+  CCE_TRY(check_mat("b_shape", b_shape));
+  CCE_TRY(check_mat("c_shape", c_shape));
+  if (a_shape.cols != b_shape.cols) return fail(CCE_EINVAL, "a and b must share the contraction length");
+  if (c_shape.rows != a_shape.rows || c_shape.cols != b_shape.rows)
+    return fail(CCE_EINVAL, "c must be [a rows, b rows]");
+  if (a_shape.cols % 8 != 0) return fail(CCE_EUNSUPPORTED, "contraction length must be a multiple of 8");
+  const size_t ein = esize(in_t), eout = esize(out_t);
+  const int64_t as = span_bytes(a_shape, ein), bs = span_bytes(b_shape, ein),
+                cs = span_bytes(c_shape, eout);
+  if (as > kMaxOperandBytes || bs > kMaxOperandBytes)
+    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+  std::vector<Range> ranges;
+  for (int r = 0; r < n_groups; ++r) {
+    const std::string rs = std::to_string(r);
+    CCE_TRY(check_ptr(("a[" + rs + "]").c_str(), a[r], as));
+    CCE_TRY(check_ptr(("b[" + rs + "]").c_str(), b[r], bs));
+    CCE_TRY(check_ptr(("c[" + rs + "]").c_str(), c[r], cs));
+    ranges.push_back(range_of(a[r], as, "a[" + rs + "]", false));
+    ranges.push_back(range_of(b[r], bs, "b[" + rs + "]", false));
+    ranges.push_back(range_of(c[r], cs, "c[" + rs + "]", true));
+  }
+  CCE_TRY(check_overlaps(ranges));
+  if (c_shape.rows == 0 || c_shape.cols == 0) return CCE_OK;
+  DeviceGuard guard(ctx->device);
+  GemmLaunch L;
+  L.groups = n_groups;
+  L.M = a_shape.rows;
+  L.N = b_shape.rows;
+  L.K = a_shape.cols;
+  L.lda = a_shape.ld;
+  L.ldb = b_shape.ld;
+  L.ldc = c_shape.ld;
+  L.in_t = in_t;
+  L.out_t = out_t;
+  L.epi = EPI_STORE;
+  L.gelu = (flags & CCE_FLAG_GELU) != 0;
+  for (int r = 0; r < n_groups; ++r) {
+    L.p.a[r] = a[r];
+    L.p.b[r] = b[r];
+    L.p.c[r] = c[r];
+    L.p.cin[r] = nullptr;
+  }
+  return launch_grouped_gemm(L, stream);
+}
+
+cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype part_t,
+                                     const void* const* partials, cce_mat shape, const void* bias,
+                                     cce_dtype bias_t, const void* residual, cce_dtype res_t,
+                                     int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
+                                     int64_t mask_row0, int64_t mask_col0, int64_t mask_ld,
+                                     void* out, cce_dtype out_t, int64_t ld_out, uint8_t* mask_out,
+                                     uint32_t flags, cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  if (flags != 0) return fail(CCE_EINVAL, "flags must be 0");
+  if (n_partials < 1) return fail(CCE_EINVAL, "n_partials < 1");
+  if (n_partials > CCE_MAX_RANKS) return fail(CCE_EUNSUPPORTED, "n_partials > CCE_MAX_RANKS");
+  if (!partials) return fail(CCE_EINVAL, "partials is NULL");
+  if (!dtype_ok(part_t) || !dtype_ok(out_t) || (bias && !dtype_ok(bias_t)) || (residual && !dtype_ok(res_t)))
+    return fail(CCE_EINVAL, "bad dtype");
+  if ((bias && bias_t != out_t) || (residual && res_t != out_t))
+    return fail(CCE_EUNSUPPORTED, "bias and residual must have the output dtype");
+  if (std::isnan(p_drop)) return fail(CCE_EINVAL, "p_drop is NaN");
+  CCE_TRY(check_mat("shape", shape));
+  const cce_mat rmat{shape.rows, shape.cols, ld_res}, omat{shape.rows, shape.cols, ld_out};
+  if (residual) CCE_TRY(check_mat("residual", rmat));
+  CCE_TRY(check_mat("out", omat));
+  if (mask_row0 < 0 || mask_col0 < 0 || mask_ld < mask_col0 + shape.cols)
+    return fail(CCE_EINVAL, "mask index base must satisfy 0 <= row0, 0 <= col0, col0 + cols <= mask_ld");
+  const size_t ep = esize(part_t), eo = esize(out_t);
+  const int64_t ps = span_bytes(shape, ep), rs = residual ? span_bytes(rmat, eo) : 0,
+                os = span_bytes(omat, eo), bs = bias ? shape.cols * static_cast<int64_t>(eo) : 0,
+                ms = mask_out ? shape.rows * shape.cols : 0;
+  std::vector<Range> ranges;
+  for (int k = 0; k < n_partials; ++k) {
+    const std::string ks = std::to_string(k);
+    CCE_TRY(check_ptr(("partials[" + ks + "]").c_str(), partials[k], ps));
+    ranges.push_back(range_of(partials[k], ps, "partials[" + ks + "]", false));
+  }
+  if (bias) CCE_TRY(check_ptr("bias", bias, bs));
+  if (residual) CCE_TRY(check_ptr("residual", residual, rs));
+  CCE_TRY(check_ptr("out", out, os));
+  if (mask_out) CCE_TRY(check_ptr("mask_out", mask_out, ms));
+  ranges.push_back(range_of(bias, bs, "bias", false));
+  ranges.push_back(range_of(residual, rs, "residual", false));
+  ranges.push_back(range_of(out, os, "out", true));
+  if (mask_out) ranges.push_back(range_of(mask_out, ms, "mask_out", true));
+  CCE_TRY(check_overlaps(ranges));
+  if (shape.rows == 0 || shape.cols == 0) return CCE_OK;
+
+  EpilogueLaunch L;
+  L.n = n_partials;
+  L.part_t = part_t;
+  for (int k = 0; k < n_partials; ++k) L.parts[k] = partials[k];
+  L.rows = shape.rows;
+  L.cols = shape.cols;
+  L.ld_part = shape.ld;
+  L.bias = bias;
+  L.bias_t = bias_t;
+  L.res = residual;
+  L.res_t = res_t;
+  L.ld_res = ld_res;
+  L.out = out;
+  L.out_t = out_t;
+  L.ld_out = ld_out;
+  L.mask = mask_out;
+  L.seed = seed;
+  L.offset = offset;
+  L.mrow0 = mask_row0;
+  L.mcol0 = mask_col0;
+  L.mld = mask_ld;
+  if (p_drop <= 0.0) {
+    L.dropout = false;
+    L.scale = 1.0f;
+  } else if (p_drop >= 1.0) {
+    L.drop_all = true;
+  } else {
+    L.dropout = true;
+    const double t = std::floor(p_drop * 4294967296.0);
+    L.threshold = static_cast<uint32_t>(t);
+    L.scale = static_cast<float>(1.0 / (1.0 - p_drop));
+  }
+  DeviceGuard guard(ctx->device);
+  return launch_fused_epilogue(L, stream);
+}
+
+cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, uint32_t flags,
+                             char* buf, size_t buf_len, size_t* needed) {
+  clear_error();
+  if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
+  if (!dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU)) return fail(CCE_EINVAL, "unknown flags");
+  const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
+  Plan p;
+  if (kind == 0) {
+    if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
+    const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
+    p = build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1, serial);
+  } else if (kind == 1) {
+    if (mode != 0 && mode != 1) return fail(CCE_EINVAL, "bad ReduceScatter mode");
+    p = build_reducescatter_plan(n_ranks, mode, true, serial);
+  } else {
+    return fail(CCE_EINVAL, "kind must be 0 or 1");
+  }
+  const std::string s = describe_plan(p);
+  if (needed) *needed = s.size() + 1;
+  if (buf && buf_len > 0) {
+    const size_t k = std::min(buf_len - 1, s.size());
+    std::memcpy(buf, s.data(), k);
+    buf[k] = '\0';
+  }
+  return CCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/cce.h"
+
+namespace cce {
+
+// ---------------------------------------------------------------------------
+// Error reporting
+// ---------------------------------------------------------------------------
+void set_error(const std::string& msg);
+void clear_error();
+cce_status fail(cce_status s, const std::string& msg);
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM launch description: one launch computes, for every group g,
+//   C_g[M, N] = epilogue(A_g[M, K] * B_g[N, K]^T, Cin_g)
+// with shared extents and leading dimensions.
+// ---------------------------------------------------------------------------
+enum Epi : int {
+  EPI_STORE = 0,        // C = part
+  EPI_ACCUM = 1,        // C = Cin + part       (Cin fp32, may alias C)
+};
+
+constexpr int kMaxGroups = CCE_MAX_RANKS;
+
+struct GemmGroupPtrs {
+  const void* a[kMaxGroups];
+  const void* b[kMaxGroups];
+  void* c[kMaxGroups];
+  const float* cin[kMaxGroups];
+};
+
+struct GemmLaunch {
+  int groups = 0;
+  int64_t M = 0, N = 0, K = 0;
+  int64_t lda = 0, ldb = 0, ldc = 0, ldcin = 0;
+  cce_dtype in_t = CCE_BF16;
+  cce_dtype out_t = CCE_BF16;
+  int epi = EPI_STORE;
+  bool gelu = false;
+  GemmGroupPtrs p{};
+};
+
+// Enqueue one grouped GEMM on `stream` (a hipStream_t).  Returns CCE_OK or
+// CCE_EHIP.  Shapes must already be validated.
+cce_status launch_grouped_gemm(const GemmLaunch& g, void* stream);
+
+// ---------------------------------------------------------------------------
+// Fused reduce epilogue launch.
+// ---------------------------------------------------------------------------
+struct EpilogueLaunch {
+  int n = 0;
+  cce_dtype part_t = CCE_F32;
+  const void* parts[kMaxGroups];
+  int64_t rows = 0, cols = 0, ld_part = 0;
+  const void* bias = nullptr;
+  cce_dtype bias_t = CCE_F32;
+  const void* res = nullptr;
+  cce_dtype res_t = CCE_F32;
+  int64_t ld_res = 0;
+  void* out = nullptr;
+  cce_dtype out_t = CCE_F32;
+  int64_t ld_out = 0;
+  uint8_t* mask = nullptr;
+  uint32_t threshold = 0;     // keep iff word >= threshold (when !drop_all)
+  bool drop_all = false;
+  bool dropout = false;       // p > 0
+  float scale = 1.0f;
+  uint64_t seed = 0, offset = 0;
+  int64_t mrow0 = 0, mcol0 = 0, mld = 0;
+};
+
+cce_status launch_fused_epilogue(const EpilogueLaunch& e, void* stream);
+
+// ---------------------------------------------------------------------------
+// Plan IR: the ordered operations of one looped call, independent of HIP.
+// Buffers are symbolic so that the same plan can be printed and race-checked
+// on the host, and resolved to device pointers by the executor.
+// ---------------------------------------------------------------------------
+enum BufKind : uint8_t {
+  B_LOOPED = 0,   // caller's looped shard of a rank (AllGather)
+  B_LOCAL = 1,    // caller's local operand of a rank
+  B_OUT = 2,      // caller's output of a rank
+  B_RECV = 3,     // workspace receive buffer (rank, parity)  AllGather
+  B_ACC = 4,      // workspace accumulator (rank, parity, half) ReduceScatter
+  B_CASE2 = 5,    // workspace fp32 accumulator (rank) AllGather case 2, bf16 out
+  B_A = 6,        // caller's left factor (ReduceScatter)
+  B_B = 7,        // caller's right factor (ReduceScatter)
+};
+
+struct BufRef {
+  uint8_t kind = 0;
+  uint8_t parity = 0;
+  uint8_t half = 0;
+  int16_t rank = 0;
+};
+
+struct Item {            // one rank's share of a GEMM or copy
+  int rank = 0;
+  int shard = 0;         // shard / slice ID worked on
+  BufRef a, b, cin, c;   // gemm: reads a, b (and cin if has_cin), writes c
+                         // copy: reads a, writes c
+  bool has_cin = false;
+};
+
+enum OpKind : uint8_t { OP_GEMM = 0, OP_COPY = 1, OP_RECORD = 2, OP_WAIT = 3 };
+enum StreamId : uint8_t { S_COMPUTE = 0, S_COPY = 1 };
+
+struct Op {
+  OpKind kind = OP_GEMM;
+  StreamId stream = S_COMPUTE;
+  int iter = 0;
+  int half = 0;          // ReduceScatter half-step (0/1); 0 for AllGather
+  int event = -1;        // record / wait
+  int epi = EPI_STORE;   // gemm epilogue
+  bool final_store = false;   // gemm writes the caller's output dtype
+  std::vector<Item> items;
+};
+
+struct Plan {
+  int kind = 0;          // 0 AllGather, 1 ReduceScatter
+  int n = 0;
+  int mode = 0;
+  int n_events = 0;
+  bool serial = false;
+  std::vector<Op> ops;
+};
+
+// Shard ID rank r uses in iteration i.
+inline int ag_shard(int n, int r, int i) { return (r + i) % n; }
+inline int rs_slice(int n, int r, int i) { return (r + i + 1) % n; }
+
+// Build the plan of a looped call.  `case2_ws` selects the workspace fp32
+// accumulator for AllGather case 2 (bf16 output); `two_halves` is false when
+// the ReduceScatter shard has a single row/column (no second chain).
+Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial);
+Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial);
+
+std::string describe_plan(const Plan& p);
+
+}  // namespace cce

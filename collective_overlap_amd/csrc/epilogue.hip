@@ -1,0 +1,308 @@
+// Fused reduce epilogue for gfx950:
+//
+//   out = residual + keep * (sum_k partials[k] + bias) * scale
+//
+// CoCoNet (Jangda et al., ASPLOS'22), the Figure 3 program and its
+// FusedAllReduce: the sum that the AllReduce produces is consumed by the bias
+// add, the dropout and the residual add while it is still in registers, so
+// the reduced tensor is never stored and reloaded.  Here the N partials are
+// N rank buffers in one HBM: every operand is read exactly once and the
+// output written exactly once; the keep mask costs no memory traffic.
+//
+// Work unit: 8 consecutive columns of one row ("vector").  A 64-lane wave
+// covers 512 consecutive columns, so every operand load is a fully coalesced
+// 16-byte-per-lane access (two for fp32), and all N partial loads plus the
+// residual load of a lane are issued before the first add.
+//
+// Arithmetic order is fixed and contraction is off: ((p0 + p1) + ...) + bias,
+// times scale if kept (else 0), plus residual, each in fp32; one
+// round-to-nearest-even conversion to the output type.
+//
+// Keep mask: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC'11) keyed by the seed, with counter
+// (e >> 2, offset) for the global element index e; word e & 3 decides e.
+// When 8 | row stride and 4 | start column, one vector needs exactly two
+// Philox blocks.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "cce_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace cce {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct EArgs {
+  const void* parts[kMaxGroups];
+  int n;
+  int rows, cols;
+  int64_t ld_part, ld_res, ld_out;
+  const void* bias;
+  const void* res;
+  void* out;
+  uint8_t* mask;
+  uint32_t threshold;
+  int mode;                 // 0: no dropout, 1: dropout, 2: drop everything
+  float scale;
+  uint32_t key0, key1, off0, off1;
+  int64_t mrow0, mcol0, mld;
+  bool aligned;             // 4 | mld and 4 | mcol0: two Philox blocks per vector
+};
+
+// ---- Philox4x32-10 -------------------------------------------------------
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c1 = static_cast<uint32_t>(p1);
+    c3 = static_cast<uint32_t>(p0);
+    c0 = n0;
+    c2 = n2;
+    k0 += kW0;
+    k1 += kW1;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+__device__ __forceinline__ uint32_t pick(const Philox4& x, uint32_t i) {
+  return i == 0 ? x.w[0] : (i == 1 ? x.w[1] : (i == 2 ? x.w[2] : x.w[3]));
+}
+
+__device__ __forceinline__ Philox4 block_for(const EArgs& a, uint64_t blk) {
+  return philox10(static_cast<uint32_t>(blk), static_cast<uint32_t>(blk >> 32), a.off0, a.off1,
+                  a.key0, a.key1);
+}
+
+// ---- typed loads / stores -------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
+    const f32x4 x = p[0], y = p[1];
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    v[4] = y[0]; v[5] = y[1]; v[6] = y[2]; v[7] = y[3];
+  } else {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + idx);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(x[e]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (sizeof(T) == 4) return reinterpret_cast<const float*>(base)[idx];
+  else return static_cast<float>(reinterpret_cast<const __bf16*>(base)[idx]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(void* base, int64_t idx, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx);
+    p[0] = f32x4{v[0], v[1], v[2], v[3]};
+    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = static_cast<__bf16>(v[e]);
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(base) + idx) = h;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store1(void* base, int64_t idx, float v) {
+  if constexpr (sizeof(T) == 4) reinterpret_cast<float*>(base)[idx] = v;
+  else reinterpret_cast<__bf16*>(base)[idx] = static_cast<__bf16>(v);
+}
+
+// NP > 0: compile-time partial count; NP == 0: runtime count a.n.
+// T is the type of the bias, the residual and the output.
+template <int NP, typename TP, typename T>
+__global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
+  using TB = T;
+  using TR = T;
+  using TO = T;
+  const bool ALIGNED = a.aligned;
+  const int vpr = (a.cols + 7) >> 3;
+  const int jv = blockIdx.x * 256 + threadIdx.x;
+  if (jv >= vpr) return;
+  const int j = jv * 8;
+  const bool full = (j + 8 <= a.cols);
+  for (int i = blockIdx.y; i < a.rows; i += gridDim.y) {
+    float s[8];
+    bool keep[8];
+    const int64_t e0 = (a.mrow0 + i) * a.mld + a.mcol0 + j;
+    if (full) {
+      // ---- vector path: 8 columns ----
+      const int64_t ip = static_cast<int64_t>(i) * a.ld_part + j;
+      float r[8];
+      if (a.res) load8<TR>(a.res, static_cast<int64_t>(i) * a.ld_res + j, r);
+      load8<TP>(a.parts[0], ip, s);
+      if constexpr (NP > 0) {
+        float t[NP > 1 ? NP - 1 : 1][8];
+#pragma unroll
+        for (int k = 1; k < NP; ++k) load8<TP>(a.parts[k], ip, t[k - 1]);
+#pragma unroll
+        for (int k = 1; k < NP; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = s[e] + t[k - 1][e];
+      } else {
+        for (int k = 1; k < a.n; ++k) {
+          float t[8];
+          load8<TP>(a.parts[k], ip, t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = s[e] + t[e];
+        }
+      }
+      if (a.bias) {
+        float b[8];
+        load8<TB>(a.bias, j, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = s[e] + b[e];
+      }
+      if (a.mode == 1) {
+        if (ALIGNED) {
+          const uint64_t blk = static_cast<uint64_t>(e0) >> 2;
+          const Philox4 x = block_for(a, blk), y = block_for(a, blk + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            keep[e] = x.w[e] >= a.threshold;
+            keep[e + 4] = y.w[e] >= a.threshold;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint64_t ee = static_cast<uint64_t>(e0 + e);
+            const Philox4 x = block_for(a, ee >> 2);
+            keep[e] = pick(x, static_cast<uint32_t>(ee & 3)) >= a.threshold;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = keep[e] ? s[e] * a.scale : 0.0f;
+      } else if (a.mode == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          keep[e] = false;
+          s[e] = 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) keep[e] = true;
+      }
+      if (a.res) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = s[e] + r[e];
+      }
+      store8<TO>(a.out, static_cast<int64_t>(i) * a.ld_out + j, s);
+      if (a.mask) {
+        uint64_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bits |= static_cast<uint64_t>(keep[e] ? 1 : 0) << (8 * e);
+        uint8_t* mp = a.mask + static_cast<int64_t>(i) * a.cols + j;
+        if ((a.cols & 7) == 0) {
+          *reinterpret_cast<uint64_t*>(mp) = bits;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mp[e] = static_cast<uint8_t>(bits >> (8 * e));
+        }
+      }
+    } else {
+      // ---- ragged tail of a row: element by element ----
+      for (int e = 0; j + e < a.cols; ++e) {
+        const int c = j + e;
+        const int64_t ip = static_cast<int64_t>(i) * a.ld_part + c;
+        float v = load1<TP>(a.parts[0], ip);
+        const int n = NP > 0 ? NP : a.n;
+        for (int k = 1; k < n; ++k) v = v + load1<TP>(a.parts[k], ip);
+        if (a.bias) v = v + load1<TB>(a.bias, c);
+        bool kp = true;
+        if (a.mode == 1) {
+          const uint64_t ee = static_cast<uint64_t>(e0 + e);
+          const Philox4 x = block_for(a, ee >> 2);
+          kp = pick(x, static_cast<uint32_t>(ee & 3)) >= a.threshold;
+          v = kp ? v * a.scale : 0.0f;
+        } else if (a.mode == 2) {
+          kp = false;
+          v = 0.0f;
+        }
+        if (a.res) v = v + load1<TR>(a.res, static_cast<int64_t>(i) * a.ld_res + c);
+        store1<TO>(a.out, static_cast<int64_t>(i) * a.ld_out + c, v);
+        if (a.mask) a.mask[static_cast<int64_t>(i) * a.cols + c] = kp ? 1 : 0;
+      }
+    }
+  }
+}
+
+template <int NP, typename TP, typename T>
+hipError_t launch_np(const EArgs& k, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((epilogue_kernel<NP, TP, T>), grid, dim3(256), 0, s, k);
+  return hipGetLastError();
+}
+
+template <typename TP, typename T>
+hipError_t launch_t(const EArgs& k, dim3 grid, hipStream_t s) {
+  switch (k.n) {
+    case 1: return launch_np<1, TP, T>(k, grid, s);
+    case 2: return launch_np<2, TP, T>(k, grid, s);
+    case 8: return launch_np<8, TP, T>(k, grid, s);
+    default: return launch_np<0, TP, T>(k, grid, s);
+  }
+}
+
+}  // namespace
+
+cce_status launch_fused_epilogue(const EpilogueLaunch& L, void* stream) {
+  if (L.rows <= 0 || L.cols <= 0) return CCE_OK;
+  EArgs k{};
+  for (int i = 0; i < L.n; ++i) k.parts[i] = L.parts[i];
+  k.n = L.n;
+  k.rows = static_cast<int>(L.rows);
+  k.cols = static_cast<int>(L.cols);
+  k.ld_part = L.ld_part;
+  k.ld_res = L.ld_res;
+  k.ld_out = L.ld_out;
+  k.bias = L.bias;
+  k.res = L.res;
+  k.out = L.out;
+  k.mask = L.mask;
+  k.threshold = L.threshold;
+  k.mode = L.drop_all ? 2 : (L.dropout ? 1 : 0);
+  k.scale = L.scale;
+  k.key0 = static_cast<uint32_t>(L.seed);
+  k.key1 = static_cast<uint32_t>(L.seed >> 32);
+  k.off0 = static_cast<uint32_t>(L.offset);
+  k.off1 = static_cast<uint32_t>(L.offset >> 32);
+  k.mrow0 = L.mrow0;
+  k.mcol0 = L.mcol0;
+  k.mld = L.mld;
+  k.aligned = (L.mld % 4 == 0) && (L.mcol0 % 4 == 0);
+  const int vpr = static_cast<int>((L.cols + 7) / 8);
+  dim3 grid((vpr + 255) / 256, static_cast<unsigned>(L.rows < 65535 ? L.rows : 65535));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // bias and residual share the output type (checked by the caller).
+  hipError_t e;
+  if (L.part_t == CCE_F32)
+    e = (L.out_t == CCE_F32) ? launch_t<float, float>(k, grid, s) : launch_t<float, __bf16>(k, grid, s);
+  else
+    e = (L.out_t == CCE_F32) ? launch_t<__bf16, float>(k, grid, s) : launch_t<__bf16, __bf16>(k, grid, s);
+  if (e != hipSuccess) return fail(CCE_EHIP, std::string("epilogue launch: ") + hipGetErrorString(e));
+  return CCE_OK;
+}
+
+}  // namespace cce

@@ -1,0 +1,274 @@
+// Plan builder: the ordered stream/event operations of one looped call.
+//
+// Wang et al., "Overlap Communication with Dependent Computation via
+// Decomposition in Large Deep Learning Models" (ASPLOS'23):
+//   * Section 5.1 -- the loop, the {source, destination} pairs of its
+//     CollectivePermute (rank r sends to r - 1) and the shard movement
+//     (AllGather aligned with the partition ID at loop start, ReduceScatter at
+//     loop end);
+//   * Section 5.2 -- each permute split into a Start that only launches the
+//     transfer and a Done that marks its completion: here a copy enqueued on
+//     the copy stream followed by an event record (Start), and an event wait
+//     on the compute stream right before the first GEMM that reads the data
+//     (Done);
+//   * Section 5.4.1 -- unrolling by two: the AllGather alternates two receive
+//     buffers per rank (no loop-carried alias copy), and the ReduceScatter
+//     accumulation chain is split into two interleaved chains so that the
+//     transfer of one chain overlaps the fused GEMM+add of the other.
+//
+// The permute in the last AllGather iteration and the first ReduceScatter
+// permute (which would move the zero-initialised accumulator) move nothing
+// that is used, so N-1 transfers per rank are built; the first ReduceScatter
+// partial is stored instead of added to zero.
+//
+// Host order matters for events: a wait enqueued before the matching record
+// would not wait, so every record below is enqueued before its wait.
+
+#include <cstdio>
+#include <string>
+
+#include "cce_internal.hpp"
+
+namespace cce {
+
+namespace {
+
+BufRef ref(uint8_t kind, int rank, int parity = 0, int half = 0) {
+  BufRef b;
+  b.kind = kind;
+  b.rank = static_cast<int16_t>(rank);
+  b.parity = static_cast<uint8_t>(parity);
+  b.half = static_cast<uint8_t>(half);
+  return b;
+}
+
+Op rec(StreamId s, int ev) {
+  Op o;
+  o.kind = OP_RECORD;
+  o.stream = s;
+  o.event = ev;
+  return o;
+}
+
+Op wait(StreamId s, int ev) {
+  Op o;
+  o.kind = OP_WAIT;
+  o.stream = s;
+  o.event = ev;
+  return o;
+}
+
+}  // namespace
+
+Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
+  Plan p;
+  p.kind = 0;
+  p.n = n;
+  p.mode = mode;
+  p.serial = serial;
+  const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
+  // events: 0 fork, 2+i gemm_done[i], 2+n+i arrive[i]
+  p.n_events = 2 + 2 * n;
+  const int EV_FORK = 0;
+  auto ev_gemm = [&](int i) { return 2 + i; };
+  auto ev_arrive = [&](int i) { return 2 + n + i; };
+  const StreamId cs = serial ? S_COMPUTE : S_COPY;
+
+  auto held = [&](int r, int i) {
+    return i == 0 ? ref(B_LOOPED, r) : ref(B_RECV, r, i % 2);
+  };
+
+  if (!serial && n > 1) {
+    p.ops.push_back(rec(S_COMPUTE, EV_FORK));
+    p.ops.push_back(wait(S_COPY, EV_FORK));
+  }
+  for (int i = 0; i < n; ++i) {
+    // Start of the permute that brings the shard of iteration i+1.
+    if (i + 1 < n) {
+      // WAR: the destination parity was last read by GEMM(i-1); GEMM(0)
+      // reads the caller's shards, so the first two copies need no wait.
+      if (!serial && i >= 2) p.ops.push_back(wait(S_COPY, ev_gemm(i - 1)));
+      Op c;
+      c.kind = OP_COPY;
+      c.stream = cs;
+      c.iter = i;
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = ag_shard(n, r, i + 1);
+        it.a = held((r + 1) % n, i);
+        it.c = ref(B_RECV, r, (i + 1) % 2);
+        c.items.push_back(it);
+      }
+      p.ops.push_back(c);
+      if (!serial) p.ops.push_back(rec(S_COPY, ev_arrive(i + 1)));
+    }
+    // Done of the permute that brought this iteration's shard, then the GEMM.
+    if (!serial && i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i)));
+    Op g;
+    g.kind = OP_GEMM;
+    g.stream = S_COMPUTE;
+    g.iter = i;
+    const bool last = (i == n - 1);
+    if (!case2) {
+      g.epi = EPI_STORE;
+      g.final_store = true;
+    } else {
+      g.epi = (i == 0) ? EPI_STORE : EPI_ACCUM;
+      g.final_store = last || !case2_ws;   // fp32 out accumulates in place
+    }
+    for (int r = 0; r < n; ++r) {
+      Item it;
+      it.rank = r;
+      it.shard = ag_shard(n, r, i);
+      it.a = held(r, i);
+      it.b = ref(B_LOCAL, r);
+      const BufRef acc = case2_ws ? ref(B_CASE2, r) : ref(B_OUT, r);
+      if (!case2) {
+        it.c = ref(B_OUT, r);
+      } else {
+        it.c = last ? ref(B_OUT, r) : acc;
+        if (i > 0) {
+          it.cin = acc;
+          it.has_cin = true;
+        }
+      }
+      g.items.push_back(it);
+    }
+    p.ops.push_back(g);
+    if (!serial && i >= 1 && i + 2 < n) p.ops.push_back(rec(S_COMPUTE, ev_gemm(i)));
+  }
+  // No join is needed: the last copy's arrival is waited for by the last
+  // GEMM, so all copy-stream work is ordered before later work on `stream`.
+  return p;
+}
+
+Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
+  Plan p;
+  p.kind = 1;
+  p.n = n;
+  p.mode = mode;
+  p.serial = serial;
+  const int H = two_halves ? 2 : 1;
+  // events: 2+(2i+h) gemm_done, 2+2n+(2i+h) arrive
+  p.n_events = 2 + 4 * n;
+  auto ev_gemm = [&](int i, int h) { return 2 + 2 * i + h; };
+  auto ev_arrive = [&](int i, int h) { return 2 + 2 * n + 2 * i + h; };
+  const StreamId cs = serial ? S_COMPUTE : S_COPY;
+
+  // No fork is needed either: the first copy waits for GEMM(0, 0), which is
+  // ordered after the caller's earlier work on `stream`.
+  for (int i = 0; i < n; ++i) {
+    const bool last = (i == n - 1);
+    for (int h = 0; h < H; ++h) {
+      if (!serial && i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i, h)));
+      Op g;
+      g.kind = OP_GEMM;
+      g.stream = S_COMPUTE;
+      g.iter = i;
+      g.half = h;
+      g.epi = (i == 0) ? EPI_STORE : EPI_ACCUM;
+      g.final_store = last;
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = rs_slice(n, r, i);
+        it.a = ref(B_A, r);
+        it.b = ref(B_B, r);
+        const BufRef acc = ref(B_ACC, r, i % 2, h);
+        it.c = last ? ref(B_OUT, r, 0, h) : acc;
+        if (i > 0) {
+          it.cin = acc;   // the accumulator received from rank r + 1
+          it.has_cin = true;
+        }
+        g.items.push_back(it);
+      }
+      p.ops.push_back(g);
+      if (!last) {
+        if (!serial) {
+          p.ops.push_back(rec(S_COMPUTE, ev_gemm(i, h)));
+          p.ops.push_back(wait(S_COPY, ev_gemm(i, h)));
+        }
+        Op c;
+        c.kind = OP_COPY;
+        c.stream = cs;
+        c.iter = i;
+        c.half = h;
+        for (int r = 0; r < n; ++r) {
+          Item it;
+          it.rank = r;
+          it.shard = rs_slice(n, (r + 1) % n, i);
+          it.a = ref(B_ACC, (r + 1) % n, i % 2, h);
+          it.c = ref(B_ACC, r, (i + 1) % 2, h);
+          c.items.push_back(it);
+        }
+        p.ops.push_back(c);
+        if (!serial) p.ops.push_back(rec(S_COPY, ev_arrive(i + 1, h)));
+      }
+    }
+  }
+  // No join is needed: the last copy's arrival is waited for by the last
+  // GEMM, so all copy-stream work is ordered before later work on `stream`.
+  return p;
+}
+
+namespace {
+
+std::string bufname(const BufRef& b) {
+  char s[64];
+  switch (b.kind) {
+    case B_LOOPED: std::snprintf(s, sizeof s, "looped%d", b.rank); break;
+    case B_LOCAL: std::snprintf(s, sizeof s, "local%d", b.rank); break;
+    case B_OUT: std::snprintf(s, sizeof s, "out%d.h%d", b.rank, b.half); break;
+    case B_RECV: std::snprintf(s, sizeof s, "recv%d.p%d", b.rank, b.parity); break;
+    case B_ACC: std::snprintf(s, sizeof s, "acc%d.p%d.h%d", b.rank, b.parity, b.half); break;
+    case B_CASE2: std::snprintf(s, sizeof s, "c2acc%d", b.rank); break;
+    case B_A: std::snprintf(s, sizeof s, "a%d", b.rank); break;
+    case B_B: std::snprintf(s, sizeof s, "b%d", b.rank); break;
+    default: std::snprintf(s, sizeof s, "?%d", b.rank); break;
+  }
+  return s;
+}
+
+}  // namespace
+
+std::string describe_plan(const Plan& p) {
+  std::string out;
+  char line[128];
+  for (const Op& o : p.ops) {
+    out += (o.stream == S_COMPUTE) ? "compute " : "copy ";
+    switch (o.kind) {
+      case OP_RECORD:
+        std::snprintf(line, sizeof line, "record ev=%d\n", o.event);
+        out += line;
+        break;
+      case OP_WAIT:
+        std::snprintf(line, sizeof line, "wait ev=%d\n", o.event);
+        out += line;
+        break;
+      case OP_GEMM:
+      case OP_COPY: {
+        std::snprintf(line, sizeof line, "%s it=%d h=%d epi=%d final=%d",
+                      o.kind == OP_GEMM ? "gemm" : "copy", o.iter, o.half, o.epi,
+                      o.final_store ? 1 : 0);
+        out += line;
+        std::string rd, wr, sh;
+        for (const Item& it : o.items) {
+          if (!rd.empty()) rd += ",";
+          rd += bufname(it.a);
+          if (o.kind == OP_GEMM) rd += "," + bufname(it.b);
+          if (it.has_cin) rd += "," + bufname(it.cin);
+          if (!wr.empty()) wr += ",";
+          wr += bufname(it.c);
+          if (!sh.empty()) sh += ",";
+          sh += std::to_string(it.rank) + ":" + std::to_string(it.shard);
+        }
+        out += " r=" + rd + " w=" + wr + " shard=" + sh + "\n";
+        break;
+      }
+    }
+  }
+  return out;
+}
+
+}  // namespace cce

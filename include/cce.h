@@ -1,0 +1,262 @@
+/*
+ * cce.h -- C ABI of the looped CollectiveEinsum library for one MI355X (gfx950).
+ *
+ * The library computes an AllGather- or ReduceScatter-bound einsum as a loop
+ * of N per-shard partial GEMMs, with the collective replaced by a ring of
+ * point-to-point shard transfers, and a fused "sum of partials + bias +
+ * dropout + residual" epilogue.  All N logical ranks are separate buffers in
+ * the HBM of one GPU; a transfer is an asynchronous device-to-device copy on a
+ * second stream, ordered by events and double-buffered against the GEMMs.
+ *
+ * Sources (cited by page title and section):
+ *   [OV] Wang et al., "Overlap Communication with Dependent Computation via
+ *        Decomposition in Large Deep Learning Models", ASPLOS'23.
+ *   [CC] Jangda et al., "Breaking the Computation and Communication
+ *        Abstraction Barrier in Distributed Machine Learning Workloads"
+ *        (CoCoNet), ASPLOS'22.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Matrices are row-major: element (i, j) of a cce_mat lives at
+ * base[i * ld + j]; ld >= cols, counted in elements.  A product is written
+ * C = A * B^T: the left factor A is stored [M, K] and the right factor is
+ * stored out-major as B^T [N, K] (the nn.Linear weight layout), so both
+ * factors are contiguous along the contraction dim.  The mathematical right
+ * factor [K, N] of the pages is the transpose of what is passed.
+ *
+ * Pointer arrays (const void* const* ...) are HOST arrays of n DEVICE
+ * pointers, read only during the call.  Every device buffer (inputs,
+ * outputs, workspace) is owned by the caller and must stay alive until the
+ * work enqueued on `stream` has finished.  The library never writes inputs.
+ * Outputs must not overlap inputs or each other.
+ *
+ * Alignment: every device base pointer must be 16-byte aligned and every ld
+ * and every contraction length K a multiple of 8 elements; otherwise the call
+ * returns CCE_EUNSUPPORTED.  Other extents (M, N, rows, cols) are arbitrary,
+ * including ragged tile tails; a zero extent is a valid no-op.
+ *
+ * Ordering: calls are asynchronous.  All work of a call is ordered after the
+ * work already enqueued on `stream` and before work enqueued on it later; the
+ * library's internal copy stream is forked from and joined back to `stream`
+ * with events.  Nothing blocks the host.
+ *
+ * Errors: every argument is validated before anything is enqueued, so a
+ * status other than CCE_OK means no work was enqueued (except CCE_EHIP, which
+ * reports a failing HIP call; cce_last_error() then names it).  Faults inside
+ * kernels surface at the caller's next synchronisation, as in HIP.
+ * A cce_ctx is not thread-safe; distinct contexts are independent.
+ */
+#ifndef CCE_H_
+#define CCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cce_status {
+  CCE_OK = 0,
+  CCE_EINVAL = 1,        /* bad argument: NULL, negative or mismatched extent */
+  CCE_EUNSUPPORTED = 2,  /* valid but outside what the kernels take (alignment, dtype combination, n_ranks) */
+  CCE_EWORKSPACE = 3,    /* workspace NULL or smaller than the query returned */
+  CCE_EHIP = 4           /* a HIP runtime call failed; see cce_last_error() */
+} cce_status;
+
+typedef enum cce_dtype { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
+
+typedef struct cce_mat { int64_t rows, cols, ld; } cce_mat;
+
+typedef struct cce_ctx cce_ctx;
+typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
+
+#define CCE_MAX_RANKS 64
+
+/* Flags (bitwise OR). */
+#define CCE_FLAG_SERIAL 0x1u  /* run every copy on `stream` itself, no overlap:
+                                 the same kernels and the same results, used as
+                                 the unoverlapped comparison */
+#define CCE_FLAG_GELU 0x2u    /* apply exact GELU, x*Phi(x), to each output
+                                 element as it is stored (AllGather-Einsum and
+                                 grouped GEMM only) */
+
+/* Status text; never NULL. */
+const char* cce_status_string(cce_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* cce_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* cce_version(void);
+
+/* Create a context on HIP device `device`: it owns a copy stream (default
+ * priority, non-blocking) and a pool of events.  *out receives the context. */
+cce_status cce_ctx_create(int device, cce_ctx** out);
+cce_status cce_ctx_destroy(cce_ctx* ctx);
+
+/* ------------------------------------------------------------------------
+ * Ring schedule ([OV] Section 5.1).
+ * Fills table[i * n_ranks + r] with the shard ID rank r works on in
+ * iteration i.  kind 0: looped AllGather-Einsum (aligned with the partition
+ * ID at loop start); kind 1: looped Einsum-ReduceScatter (aligned at loop
+ * end).  Transfers always go from rank r to rank (r - 1) mod n, the
+ * {source, destination} pairs {0, N-1}, {1, 0}, ..., {N-1, N-2}.
+ * table is host memory of n_ranks * n_ranks int32.  Host-only; no device.
+ * ---------------------------------------------------------------------- */
+cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
+
+/* ------------------------------------------------------------------------
+ * Looped AllGather-Einsum ([OV] Sections 4 and 5.1, cases 1 and 2).
+ *
+ * looped[r] is rank r's own shard (shard ID r) of the operand the AllGather
+ * would rebuild; local[r] is rank r's operand that never moves; out[r]
+ * receives rank r's full result.  In iteration i rank r computes the partial
+ * einsum on shard s = (r + i) mod n while that shard travels on to rank
+ * r - 1; the update is a store into the result slice of shard s (case 1,
+ * DynamicUpdateSlice) or an addition (case 2).  Shapes (storage orientation,
+ * see the header comment):
+ *
+ *   CCE_AG_LHS_ROWS  case 1, looped left factor split on rows M:
+ *                    looped [m_s, K], local B^T [N, K], out [n*m_s, N];
+ *                    shard s fills out rows [s*m_s, (s+1)*m_s).
+ *   CCE_AG_RHS_COLS  case 1, looped right factor split on columns N:
+ *                    looped B^T [n_s, K], local A [M, K], out [M, n*n_s];
+ *                    shard s fills out columns [s*n_s, (s+1)*n_s).
+ *   CCE_AG_LHS_COLS  case 2, looped left factor split on K:
+ *                    looped [M, k_s], local B^T [N, n*k_s], out [M, N];
+ *                    out += shard * (B^T columns [s*k_s, (s+1)*k_s))^T.
+ *   CCE_AG_RHS_ROWS  case 2, looped right factor split on K:
+ *                    looped B^T [N, k_s], local A [M, n*k_s], out [M, N];
+ *                    out += (A columns [s*k_s, (s+1)*k_s)) * shard^T.
+ *
+ * in_t: CCE_BF16 (fp32 accumulation) or CCE_F32 (both inputs the same type).
+ * out_t: CCE_BF16 or CCE_F32 (round to nearest even on the final store).
+ * Case 2 accumulates across iterations in fp32 (in `out` itself when out_t is
+ * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU.
+ * workspace: device memory of at least the size the query returns (two
+ * receive buffers per rank, plus the fp32 accumulators of case 2 with a bf16
+ * output); its contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+typedef enum cce_ag_mode {
+  CCE_AG_LHS_ROWS = 0,
+  CCE_AG_RHS_COLS = 1,
+  CCE_AG_LHS_COLS = 2,
+  CCE_AG_RHS_ROWS = 3
+} cce_ag_mode;
+
+cce_status cce_looped_allgather_einsum_workspace(int n_ranks, cce_ag_mode mode, cce_dtype in_t,
+                                                 cce_dtype out_t, cce_mat looped_shard,
+                                                 cce_mat out_shape, size_t* bytes);
+
+cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mode,
+                                       cce_dtype in_t, cce_dtype out_t,
+                                       const void* const* looped, cce_mat looped_shard,
+                                       const void* const* local, cce_mat local_shape,
+                                       void* const* out, cce_mat out_shape,
+                                       void* workspace, size_t workspace_bytes,
+                                       uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Looped Einsum-ReduceScatter ([OV] Sections 4, 5.1 and 5.4.1).
+ *
+ * a[r], b[r] are rank r's factors; out[r] receives shard r of the sum over
+ * all ranks of a[q] * b[q]^T:
+ *
+ *   CCE_RS_SLICE_LHS_ROWS  a [n*m_s, K], b^T [N, K], out [m_s, N];
+ *                          out_r = sum_q (a_q b_q^T)[rows r*m_s .. +m_s).
+ *   CCE_RS_SLICE_RHS_COLS  a [M, K], b^T [n*n_s, K], out [M, n_s];
+ *                          out_r = sum_q (a_q b_q^T)[cols r*n_s .. +n_s).
+ *
+ * The accumulator of each shard travels the ring (rank r -> r - 1) and ends
+ * on the rank of its shard ID; in iteration i rank r adds its partial for
+ * slice t = (r + i + 1) mod n.  As in the loop unrolling of [OV] 5.4.1, each
+ * accumulator is split into two halves that form two interleaved chains, so
+ * the transfer of one half overlaps the GEMM of the other.  For every element
+ * of out[s] the sum runs over the partials of ranks s-1, s-2, ..., s+1, s
+ * (mod n) in that order, in fp32, whatever the flags.
+ * in_t: CCE_BF16 or CCE_F32; acc_t: CCE_F32 only; out_t: CCE_F32 or CCE_BF16.
+ * workspace: two fp32 accumulators per rank (the query returns the size).
+ * ---------------------------------------------------------------------- */
+typedef enum cce_rs_mode { CCE_RS_SLICE_LHS_ROWS = 0, CCE_RS_SLICE_RHS_COLS = 1 } cce_rs_mode;
+
+cce_status cce_looped_einsum_reducescatter_workspace(int n_ranks, cce_rs_mode mode,
+                                                     cce_dtype acc_t, cce_mat out_shard,
+                                                     size_t* bytes);
+
+cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,
+                                           cce_dtype in_t, cce_dtype acc_t, cce_dtype out_t,
+                                           const void* const* a, cce_mat a_shape,
+                                           const void* const* b, cce_mat b_shape,
+                                           void* const* out, cce_mat out_shard,
+                                           void* workspace, size_t workspace_bytes,
+                                           uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped local GEMM: c[g] = a[g] * b[g]^T for g < n_groups, one launch.
+ * This is the per-rank MatMul of two tensors sliced on the contraction dim,
+ * producing one local partial per rank ([CC] Figure 3 program, the MatMul
+ * before the AllReduce).  a [M, K], b^T [N, K], c [M, N].  in_t CCE_BF16 or
+ * CCE_F32; out_t CCE_BF16 or CCE_F32.  flags: CCE_FLAG_GELU.
+ * ---------------------------------------------------------------------- */
+cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtype out_t,
+                            const void* const* a, cce_mat a_shape,
+                            const void* const* b, cce_mat b_shape,
+                            void* const* c, cce_mat c_shape,
+                            uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Fused reduce epilogue ([CC] Figure 3 program and its FusedAllReduce):
+ *
+ *   out = residual + keep * (sum_k partials[k] + bias) * c,   c = 1 / (1 - p_drop)
+ *
+ * in one pass: each partial, the residual and the bias are read once, the
+ * output is written once, and the keep mask is generated in registers.
+ * partials[k] (k < n_partials) share `shape` (rows, cols, ld) and part_t;
+ * bias: [cols] of bias_t, or NULL; residual: [rows, cols] with ld_res, of
+ * res_t, or NULL; out: [rows, cols] with ld_out, of out_t.  The bias and the
+ * residual share the output's dtype (bias_t == res_t == out_t, else
+ * CCE_EUNSUPPORTED); part_t is independent (e.g. fp32 accumulators into a
+ * bf16 output).
+ * Sum order: ((p0 + p1) + ...) + p_{n-1} in fp32, then + bias, then the
+ * dropout scale, then + residual, each rounded to fp32, no fused
+ * multiply-add; the output is rounded to nearest even once.
+ * Keep mask: element (i, j) has the global index
+ *   e = (mask_row0 + i) * mask_ld + (mask_col0 + j);
+ * Philox4x32-10 (Salmon et al., SC'11) with counter (lo(e>>2), hi(e>>2),
+ * lo(offset), hi(offset)) and key (lo(seed), hi(seed)) gives word e & 3;
+ * the element is kept iff word >= floor(p_drop * 2^32).  p_drop <= 0 keeps
+ * everything, p_drop >= 1 drops everything (out = residual).
+ * mask_out: NULL, or a device [rows, cols] uint8 array (ld = cols) that
+ * receives the keep decisions (1 kept, 0 dropped), for tests.
+ * 1 <= n_partials <= CCE_MAX_RANKS.  flags: must be 0.
+ * ---------------------------------------------------------------------- */
+cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype part_t,
+                                     const void* const* partials, cce_mat shape,
+                                     const void* bias, cce_dtype bias_t,
+                                     const void* residual, cce_dtype res_t, int64_t ld_res,
+                                     double p_drop, uint64_t seed, uint64_t offset,
+                                     int64_t mask_row0, int64_t mask_col0, int64_t mask_ld,
+                                     void* out, cce_dtype out_t, int64_t ld_out,
+                                     uint8_t* mask_out, uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Plan description, host-only (no device, no context): writes the ordered
+ * list of operations that a looped call with these arguments would enqueue,
+ * one per line, into buf (NUL-terminated; *needed receives the full length
+ * including the NUL).  Line format:
+ *   <stream> <op> [key=value ...]
+ * stream is "compute" or "copy"; op is gemm, copy, record or wait; gemm and
+ * copy lines list the symbolic buffers they read (r=) and write (w=); record
+ * and wait lines name an event (ev=).  kind 0 = AllGather (mode is a
+ * cce_ag_mode), kind 1 = ReduceScatter (mode is a cce_rs_mode).  Used to check
+ * the stream/event ordering for races on the CPU.
+ * ---------------------------------------------------------------------- */
+cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t,
+                             uint32_t flags, char* buf, size_t buf_len, size_t* needed);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCE_H_ */

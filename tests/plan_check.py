@@ -1,0 +1,127 @@
+"""Happens-before race checker for the library's plan descriptions
+(cce_describe_plan).  Pure Python, CPU only.
+
+Model: ops on one stream run in the order they were enqueued; a `wait ev=e`
+orders everything after it on its stream after everything up to the most
+recent `record ev=e` enqueued before the wait (a wait with no earlier record
+waits for nothing).  The caller's own work is modelled as a virtual op at the
+start and one at the end of the compute stream that touch every buffer.
+
+A plan is race-free when every pair of operations that touch a common buffer,
+at least one of them writing it, is ordered by happens-before in the same
+direction as the host enqueue order (which is the sequential semantics: the
+serial plan runs exactly that order on one stream).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+@dataclass
+class POp:
+    idx: int
+    stream: str
+    kind: str
+    attrs: dict = field(default_factory=dict)
+    reads: set = field(default_factory=set)
+    writes: set = field(default_factory=set)
+
+
+def parse(text: str) -> list[POp]:
+    ops = []
+    for line in text.strip().splitlines():
+        parts = line.split()
+        stream, kind = parts[0], parts[1]
+        attrs = {}
+        for p in parts[2:]:
+            k, v = p.split("=", 1)
+            attrs[k] = v
+        op = POp(len(ops), stream, kind, attrs)
+        if kind in ("gemm", "copy"):
+            op.reads = set(attrs["r"].split(","))
+            op.writes = set(attrs["w"].split(","))
+        ops.append(op)
+    return ops
+
+
+def _with_caller(ops: list[POp]) -> list[POp]:
+    bufs = set()
+    for o in ops:
+        bufs |= o.reads | o.writes
+    start = POp(0, "compute", "caller", {}, set(), set(bufs))
+    body = [POp(o.idx + 1, o.stream, o.kind, o.attrs, o.reads, o.writes) for o in ops]
+    end = POp(len(ops) + 1, "compute", "caller", {}, set(bufs), set(bufs))
+    return [start] + body + [end]
+
+
+def happens_before(ops: list[POp]):
+    """Return (succ adjacency, problems) for the HB graph."""
+    n = len(ops)
+    succ = [set() for _ in range(n)]
+    problems = []
+    last_on = {}
+    last_record = {}
+    for o in ops:
+        prev = last_on.get(o.stream)
+        if prev is not None:
+            succ[prev].add(o.idx)
+        last_on[o.stream] = o.idx
+        if o.kind == "record":
+            last_record[o.attrs["ev"]] = o.idx
+        elif o.kind == "wait":
+            r = last_record.get(o.attrs["ev"])
+            if r is None:
+                problems.append(f"op {o.idx}: wait on ev={o.attrs['ev']} before any record")
+            else:
+                succ[r].add(o.idx)
+    return succ, problems
+
+
+def _reach(succ):
+    n = len(succ)
+    reach = []
+    for s in range(n):
+        seen = set()
+        stack = [s]
+        while stack:
+            u = stack.pop()
+            for v in succ[u]:
+                if v not in seen:
+                    seen.add(v)
+                    stack.append(v)
+        reach.append(seen)
+    return reach
+
+
+def check(text: str) -> list[str]:
+    """List of problems (empty when the plan is race-free)."""
+    ops = _with_caller(parse(text))
+    succ, problems = happens_before(ops)
+    reach = _reach(succ)
+    acc = [o for o in ops if o.kind in ("gemm", "copy", "caller")]
+    for i, x in enumerate(acc):
+        for y in acc[i + 1:]:
+            conflict = (x.writes & (y.reads | y.writes)) or (y.writes & x.reads)
+            if conflict and y.idx not in reach[x.idx]:
+                problems.append(f"race: op {x.idx} ({x.stream} {x.kind} {x.attrs.get('it')}) "
+                                f"and op {y.idx} ({y.stream} {y.kind} {y.attrs.get('it')}) "
+                                f"on {sorted(conflict)[:3]}")
+    return problems
+
+
+def concurrent(text: str, a_pred, b_pred) -> bool:
+    """True if some op matching a_pred and some op matching b_pred are not
+    ordered by happens-before (they may overlap in time)."""
+    ops = parse(text)
+    succ, _ = happens_before(ops)
+    reach = _reach(succ)
+    for x in ops:
+        if not a_pred(x):
+            continue
+        for y in ops:
+            if y is x or not b_pred(y):
+                continue
+            if y.idx not in reach[x.idx] and x.idx not in reach[y.idx]:
+                return True
+    return False

@@ -1,0 +1,222 @@
+"""CPU tests of the C ABI library: it loads, exports every declared symbol,
+its shard schedule is the oracle's, its stream/event plans are race-free and
+overlap copies with GEMMs, and its host-side validation rejects bad shapes.
+No GPU is needed: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import ring
+import plan_check
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cce.h")
+
+
+@pytest.fixture(scope="module")
+def cce():
+    from collective_overlap_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libcce.so is not built (python -m collective_overlap_amd.build)")
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cce_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(cce):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(cce, n), n
+
+
+def test_status_strings(cce):
+    for s in range(5):
+        assert cce.cce_status_string(s).decode().startswith("CCE_")
+    assert cce.cce_version().decode().count(".") == 2
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)) + [31, 64])
+def test_shard_schedule_is_the_oracles(n):
+    from collective_overlap_amd import cce_shard_schedule
+    looped = [np.zeros((1, 1)) for _ in range(n)]
+    local = [np.zeros((1, 1)) for _ in range(n)]
+    _, ag, _ = ring.simulate_allgather_einsum("lhs_rows", looped, local)
+    assert cce_shard_schedule(n, 0) == ag
+    a = [np.zeros((n, 1)) for _ in range(n)]
+    b = [np.zeros((1, 1)) for _ in range(n)]
+    _, rs, _ = ring.simulate_einsum_reducescatter("slice_lhs_rows", a, b)
+    assert cce_shard_schedule(n, 1) == rs
+
+
+def _plan(kind, n, mode, out_t=1, flags=0):
+    from collective_overlap_amd import cce_describe_plan
+    return cce_describe_plan(kind, n, mode, out_t, flags)
+
+
+def _shards(op):
+    return {int(k): int(v) for k, v in (p.split(":") for p in op.attrs["shard"].split(","))}
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("out_t", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_allgather_plan_race_free(n, mode, out_t, flags):
+    text = _plan(0, n, mode, out_t, flags)
+    assert plan_check.check(text) == []
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_reducescatter_plan_race_free(n, mode, flags):
+    text = _plan(1, n, mode, 0, flags)
+    assert plan_check.check(text) == []
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_allgather_plan_matches_simulated_loop(n):
+    ops = plan_check.parse(_plan(0, n, 0))
+    looped = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, transfers = ring.simulate_allgather_einsum("lhs_rows", looped, looped)
+    gemms = [o for o in ops if o.kind == "gemm"]
+    copies = [o for o in ops if o.kind == "copy"]
+    assert len(gemms) == n and len(copies) == n - 1        # N-1 hops per rank
+    for o in gemms:
+        i = int(o.attrs["it"])
+        assert _shards(o) == {r: sched[i][r] for r in range(n)}
+    for o in copies:
+        i = int(o.attrs["it"])
+        # the copy of iteration i lands the shard that the simulation's
+        # permute of iteration i delivers to each destination rank
+        want = {dst: sid for src, dst, sid in transfers[i]}
+        assert _shards(o) == want
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_reducescatter_plan_matches_simulated_loop(n):
+    ops = plan_check.parse(_plan(1, n, 0))
+    a = [np.zeros((n, 1)) for _ in range(n)]
+    b = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, _ = ring.simulate_einsum_reducescatter("slice_lhs_rows", a, b)
+    gemms = [o for o in ops if o.kind == "gemm"]
+    assert len(gemms) == 2 * n
+    for o in gemms:
+        i = int(o.attrs["it"])
+        assert _shards(o) == {r: sched[i][r] for r in range(n)}
+    assert len([o for o in ops if o.kind == "copy"]) == 2 * (n - 1)
+
+
+def _is(kind, it, h=None):
+    def f(o):
+        return (o.kind == kind and int(o.attrs["it"]) == it
+                and (h is None or int(o.attrs["h"]) == h))
+    return f
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_allgather_copy_overlaps_gemm(n):
+    text = _plan(0, n, 1)
+    for i in range(n - 1):
+        assert plan_check.concurrent(text, _is("copy", i), _is("gemm", i))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_reducescatter_half_copies_overlap_other_chain(n):
+    text = _plan(1, n, 0)
+    for i in range(n - 1):
+        assert plan_check.concurrent(text, _is("copy", i, 0), _is("gemm", i, 1))
+        assert plan_check.concurrent(text, _is("copy", i, 1), _is("gemm", i + 1, 0))
+
+
+def test_serial_plan_has_no_copy_stream():
+    for kind, mode in ((0, 0), (1, 0)):
+        assert all(o.stream == "compute" for o in plan_check.parse(_plan(kind, 4, mode, 1, 1)))
+
+
+@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 2), (1, 0), (1, 1)])
+def test_checker_flags_every_dropped_wait(kind, mode):
+    """Each wait of the overlapped plan is necessary: removing any single one
+    (a mistake planted in the description, on the CPU) is flagged."""
+    lines = _plan(kind, 4, mode, 1).strip().splitlines()
+    waits = [i for i, l in enumerate(lines) if " wait " in l]
+    assert waits
+    for w in waits:
+        broken = "\n".join(l for i, l in enumerate(lines) if i != w)
+        assert plan_check.check(broken), f"dropping line {w} went unnoticed"
+
+
+def test_checker_flags_wait_before_record():
+    text = "copy wait ev=9\ncompute record ev=9\n"
+    assert plan_check.check(text)
+
+
+# ---------------------------------------------------------------------------
+# Host-side validation (workspace queries need no device)
+# ---------------------------------------------------------------------------
+
+def _ws_ag(cce, n, mode, in_t, out_t, looped, out):
+    from collective_overlap_amd._lib import cce_mat
+    nb = ctypes.c_size_t()
+    s = cce.cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t, cce_mat(*looped),
+                                                  cce_mat(*out), ctypes.byref(nb))
+    return s, nb.value
+
+
+def test_allgather_workspace_sizes(cce):
+    # case 1, bf16, rhs_cols: two receive buffers of [512, 256] bf16 per rank
+    s, nb = _ws_ag(cce, 4, 1, 1, 1, (512, 256, 256), (64, 2048, 2048))
+    assert s == 0 and nb == 2 * 4 * 512 * 256 * 2
+    # case 2 with bf16 output adds an fp32 accumulator per rank
+    s, nb2 = _ws_ag(cce, 4, 2, 1, 1, (64, 256, 256), (64, 512, 512))
+    assert s == 0 and nb2 == 2 * 4 * 64 * 256 * 2 + 4 * 64 * 512 * 4
+    # a single rank needs no workspace
+    s, nb = _ws_ag(cce, 1, 1, 1, 1, (512, 256, 256), (64, 512, 512))
+    assert s == 0 and nb == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 1, 1, (8, 8, 8), (8, 0, 8)), 1),          # n < 1
+    ((65, 1, 1, 1, (8, 8, 8), (8, 520, 520)), 2),     # n > max
+    ((2, 7, 1, 1, (8, 8, 8), (8, 16, 16)), 1),        # bad mode
+    ((2, 1, 5, 1, (8, 8, 8), (8, 16, 16)), 1),        # bad dtype
+    ((2, 1, 1, 1, (8, 8, 4), (8, 16, 16)), 1),        # ld < cols
+    ((2, 1, 1, 1, (8, 12, 12), (8, 16, 16)), 2),      # ld % 8
+    ((2, 1, 1, 1, (8, 8, 8), (8, 24, 24)), 1),        # out cols != n * n_s
+    ((2, 0, 1, 1, (8, 8, 8), (15, 8, 8)), 1),         # out rows != n * m_s
+])
+def test_allgather_validation(cce, args, status):
+    s, _ = _ws_ag(cce, *args)
+    assert s == status
+    assert cce.cce_last_error().decode()
+
+
+def test_reducescatter_workspace_and_validation(cce):
+    from collective_overlap_amd._lib import cce_mat
+    nb = ctypes.c_size_t()
+    assert cce.cce_looped_einsum_reducescatter_workspace(
+        8, 0, 0, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 0
+    assert nb.value == 2 * 8 * 2 * 1024 * 4096 * 4
+    # bf16 travelling accumulator is not offered
+    assert cce.cce_looped_einsum_reducescatter_workspace(
+        8, 0, 1, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 2
+    assert cce.cce_looped_einsum_reducescatter_workspace(
+        8, 3, 0, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 1
+
+
+def test_null_context_rejected_before_any_work(cce):
+    from collective_overlap_amd._lib import cce_mat, ptr_array
+    arr = ptr_array([0, 0])
+    m = cce_mat(8, 8, 8)
+    assert cce.cce_looped_allgather_einsum(None, 2, 1, 1, 1, arr, m, arr, m, arr,
+                                           cce_mat(8, 16, 16), None, 0, 0, None) == 1
+    assert cce.cce_grouped_gemm(None, 2, 1, 1, arr, m, arr, m, arr, m, 0, None) == 1

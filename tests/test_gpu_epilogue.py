@@ -1,0 +1,98 @@
+"""GPU parity of the fused reduce epilogue: keep masks bit-exact against the
+oracle's Philox, values against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import epilogue as oep
+import workloads as W
+from gpu_util import np64, assert_bf16_close, assert_f32_close, sync
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import collective_overlap_amd as cce
+    c = cce.Context(0)
+    yield c
+    sync()
+    c.close()
+
+
+def _mk(shape, k, dtype, ld=None):
+    rows, cols = shape
+    x = W.normal((rows, ld or cols), 1.0, k, device=DEV, dtype=dtype)
+    return x[:, :cols] if ld else x
+
+
+CASES = [
+    # rows, cols, ld, n, part, out, p, seed, offset, row0, col0, mask_ld
+    (100, 264, None, 2, "f32", "f32", 0.1, 0, 0, 0, 0, None),
+    (64, 256, None, 2, "f32", "f32", 0.1, 0, 0, 0, 0, None),
+    (257, 512, None, 8, "bf16", "bf16", 0.1, 1234, 5, 0, 0, None),
+    (33, 261, 272, 3, "bf16", "bf16", 0.3, 7, 9, 4, 8, 400),
+    (40, 96, None, 1, "f32", "bf16", 0.1, 99, 0, 1024, 0, 96),
+    (17, 88, None, 5, "f32", "f32", 0.5, 3, 2, 2, 3, 97),         # misaligned mask index
+    (20, 64, None, 2, "bf16", "bf16", 0.0, 0, 0, 0, 0, None),
+    (20, 64, None, 2, "f32", "f32", 1.0, 0, 0, 0, 0, None),
+    (9, 8, None, 64, "f32", "f32", 0.2, 11, 1, 0, 0, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_fused_epilogue(ctx, case):
+    import collective_overlap_amd as cce
+    rows, cols, ld, n, pt, ot, p, seed, off, r0, c0, mld = case
+    print(f"[gpu] epilogue {case}", flush=True)
+    pdt = torch.float32 if pt == "f32" else torch.bfloat16
+    odt = torch.float32 if ot == "f32" else torch.bfloat16
+    parts = [_mk((rows, cols), 10 + k, pdt, ld) for k in range(n)]
+    bias = W.normal((cols,), 0.02, 90, device=DEV, dtype=odt)
+    res = _mk((rows, cols), 91, odt, ld)
+    out_full = torch.full((rows, ld or cols), float("nan"), device=DEV, dtype=odt)
+    out = out_full[:, :cols]
+    mask = torch.full((rows, cols), 7, device=DEV, dtype=torch.uint8)
+    cce.cce_fused_reduce_epilogue(ctx, parts, bias, res, out, p, seed, off, r0, c0, mld,
+                                  mask_out=mask)
+    sync()
+    ref, keep = oep.fused_reduce_epilogue([np64(x) for x in parts], np64(bias), np64(res), p,
+                                          seed, off, r0, c0, mld if mld else c0 + cols)
+    assert np.array_equal(mask.cpu().numpy().astype(bool), keep), "keep mask differs"
+    assert set(np.unique(mask.cpu().numpy())) <= {0, 1}
+    if ot == "f32":
+        assert_f32_close(np64(out), ref, "epilogue", tol=1e-6)
+    else:
+        assert_bf16_close(np64(out), ref, "epilogue")
+    if ld:
+        assert torch.isnan(out_full[:, cols:].float()).all()    # padding untouched
+
+
+def test_no_bias_no_residual(ctx):
+    import collective_overlap_amd as cce
+    parts = [_mk((32, 128), 1 + k, torch.float32) for k in range(2)]
+    out = torch.empty((32, 128), device=DEV)
+    cce.cce_fused_reduce_epilogue(ctx, parts, None, None, out, 0.25, 5, 6)
+    sync()
+    ref, _ = oep.fused_reduce_epilogue([np64(x) for x in parts], None, None, 0.25, 5, 6)
+    assert_f32_close(np64(out), ref, "no bias/residual", tol=1e-6)
+
+
+def test_keep_rate_full_size_mask(ctx):
+    """p = 0.1 over 8192 x 8192: keep count within 6 sigma of the binomial."""
+    import collective_overlap_amd as cce
+    rows = cols = 8192
+    part = torch.zeros((rows, cols), device=DEV, dtype=torch.bfloat16)
+    out = torch.empty_like(part)
+    mask = torch.empty((rows, cols), device=DEV, dtype=torch.uint8)
+    cce.cce_fused_reduce_epilogue(ctx, [part], None, None, out, 0.1, 0, 0, mask_out=mask)
+    kept = int(mask.sum(dtype=torch.int64).item())
+    n = rows * cols
+    assert abs(kept - 0.9 * n) < 6 * (n * 0.09) ** 0.5
+    # sampled rows against the oracle's mask
+    from oracle import philox
+    for r in (0, 1, 4095, 8191):
+        want = philox.keep_mask(1, cols, 0.1, 0, 0, row0=r, col0=0, ld=cols)[0]
+        assert np.array_equal(mask[r].cpu().numpy().astype(bool), want)

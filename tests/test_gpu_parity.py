@@ -1,0 +1,276 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Sizes here finish in the oracle within seconds yet span several tiles and
+ragged tails in M, N and K.  Float results are compared with the float64
+oracle on the exact bf16/fp32 input values; integer-valued probes make every
+fp32 sum exact, so those must match bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import einsum as oe
+from oracle import numerics
+import workloads as W
+from gpu_util import np64, assert_bf16_close, assert_f32_close, sync
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import collective_overlap_amd as cce
+    print(f"[gpu] libcce {cce.cce_version()} on {torch.cuda.get_device_name(0)}", flush=True)
+    c = cce.Context(0)
+    yield c
+    sync()
+    c.close()
+
+
+def _t(shape, k, dtype, probe, ld=None):
+    rows, cols = shape
+    full_cols = ld if ld is not None else cols
+    if probe:
+        x = W.int_probe((rows, full_cols), k, device=DEV, dtype=dtype)
+    else:
+        x = W.normal((rows, full_cols), 1.0, k, device=DEV, dtype=dtype)
+    return x[:, :cols] if ld is not None else x
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMM
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,G", [(256, 256, 64, 1), (300, 200, 136, 3), (1000, 520, 264, 2),
+                                     (2048, 1024, 512, 4), (17, 24, 8, 2), (512, 768, 0, 1)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_grouped_gemm(ctx, M, N, K, G, dt):
+    import collective_overlap_amd as cce
+    print(f"[gpu] grouped_gemm M={M} N={N} K={K} G={G} {dt}", flush=True)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    a = [_t((M, K), 10 + g, dtype, False) for g in range(G)]
+    b = [_t((N, K), 20 + g, dtype, False) for g in range(G)]
+    c32 = [torch.full((M, N), float("nan"), device=DEV) for _ in range(G)]
+    cce.cce_grouped_gemm(ctx, a, b, c32)
+    c16 = [torch.empty((M, N), device=DEV, dtype=torch.bfloat16) for _ in range(G)]
+    cce.cce_grouped_gemm(ctx, a, b, c16)
+    sync()
+    for g in range(G):
+        ref = oe.local_matmuls([np64(a[g])], [np64(b[g]).T])[0]
+        assert_f32_close(np64(c32[g]), ref, f"group {g} fp32 out", tol=1e-5 if dt == "bf16" else 2e-5)
+        assert_bf16_close(np64(c16[g]), ref, f"group {g} bf16 out")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_grouped_gemm_integer_probe_bit_exact(ctx, dt):
+    import collective_overlap_amd as cce
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    M, N, K, G = 600, 392, 1032, 3
+    a = [_t((M, K), 30 + g, dtype, True) for g in range(G)]
+    b = [_t((N, K), 40 + g, dtype, True) for g in range(G)]
+    c = [torch.empty((M, N), device=DEV) for _ in range(G)]
+    cce.cce_grouped_gemm(ctx, a, b, c)
+    sync()
+    for g in range(G):
+        ref = np64(a[g]) @ np64(b[g]).T
+        assert np.array_equal(np64(c[g]), ref)
+
+
+def test_grouped_gemm_gelu_and_strided(ctx):
+    import collective_overlap_amd as cce
+    M, N, K = 384, 261, 200
+    a = [_t((M, K), 50, torch.bfloat16, False, ld=208)]
+    b = [_t((N, K), 51, torch.bfloat16, False, ld=216)]
+    big = torch.zeros((M, 272), device=DEV, dtype=torch.bfloat16)
+    c = [big[:, :N]]
+    cce.cce_grouped_gemm(ctx, a, b, c, gelu=True)
+    sync()
+    ref = numerics.gelu(np64(a[0]) @ np64(b[0]).T)
+    assert_bf16_close(np64(c[0]), ref, "gelu strided")
+    assert torch.count_nonzero(big[:, N:]) == 0     # padding untouched
+
+
+# ---------------------------------------------------------------------------
+# looped AllGather-Einsum
+# ---------------------------------------------------------------------------
+def _ag_inputs(mode, n, dims, dtype, probe, seed=0):
+    """Storage-orientation device tensors and math-orientation oracle inputs."""
+    m, k, c = dims           # m: rows-ish, k: contraction per shard, c: cols-ish
+    if mode == "lhs_rows":
+        looped = [_t((m, k), seed + r, dtype, probe) for r in range(n)]          # A_s [m_s, K]
+        local = [_t((c, k), seed + 100 + r, dtype, probe) for r in range(n)]     # B_r^T [N, K]
+        out_shape = (n * m, c)
+        o_looped = [np64(x) for x in looped]
+        o_local = [np64(x).T for x in local]
+    elif mode == "rhs_cols":
+        looped = [_t((c, k), seed + r, dtype, probe) for r in range(n)]          # B_s^T [n_s, K]
+        local = [_t((m, k), seed + 100 + r, dtype, probe) for r in range(n)]     # A_r [M, K]
+        out_shape = (m, n * c)
+        o_looped = [np64(x).T for x in looped]
+        o_local = [np64(x) for x in local]
+    elif mode == "lhs_cols":
+        looped = [_t((m, k), seed + r, dtype, probe) for r in range(n)]          # A_s [M, k_s]
+        local = [_t((c, n * k), seed + 100 + r, dtype, probe) for r in range(n)] # B_r^T [N, n k_s]
+        out_shape = (m, c)
+        o_looped = [np64(x) for x in looped]
+        o_local = [np64(x).T for x in local]
+    else:  # rhs_rows
+        looped = [_t((c, k), seed + r, dtype, probe) for r in range(n)]          # B_s^T [N, k_s]
+        local = [_t((m, n * k), seed + 100 + r, dtype, probe) for r in range(n)] # A_r [M, n k_s]
+        out_shape = (m, c)
+        o_looped = [np64(x).T for x in looped]
+        o_local = [np64(x) for x in local]
+    return looped, local, out_shape, o_looped, o_local
+
+
+AG_CASES = [("lhs_rows", (136, 200, 264)), ("rhs_cols", (300, 136, 200)),
+            ("lhs_cols", (264, 136, 296)), ("rhs_rows", (200, 264, 136))]
+
+
+@pytest.mark.parametrize("mode,dims", AG_CASES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_allgather_einsum(ctx, mode, dims, n, out_dt):
+    import collective_overlap_amd as cce
+    print(f"[gpu] allgather {mode} n={n} dims={dims} out={out_dt}", flush=True)
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    looped, local, oshape, ol, oc = _ag_inputs(mode, n, dims, torch.bfloat16, False, seed=n)
+    out = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, mode, looped, local, out)
+    out_s = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, mode, looped, local, out_s, flags=cce.CCE_FLAG_SERIAL)
+    sync()
+    ref = oe.allgather_einsum(mode, ol, oc)
+    for r in range(n):
+        if out_dt == "bf16":
+            assert_bf16_close(np64(out[r]), ref[r], f"rank {r}")
+        else:
+            assert_f32_close(np64(out[r]), ref[r], f"rank {r}")
+        assert torch.equal(out[r], out_s[r]), "overlapped and serial results differ"
+
+
+@pytest.mark.parametrize("mode,dims", AG_CASES)
+@pytest.mark.parametrize("n", [2, 4])
+def test_allgather_einsum_integer_probe_bit_exact(ctx, mode, dims, n):
+    import collective_overlap_amd as cce
+    looped, local, oshape, ol, oc = _ag_inputs(mode, n, dims, torch.bfloat16, True, seed=7)
+    out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, mode, looped, local, out)
+    sync()
+    ref = oe.allgather_einsum(mode, ol, oc)
+    for r in range(n):
+        assert np.array_equal(np64(out[r]), ref[r]), f"rank {r}"
+
+
+@pytest.mark.parametrize("mode,dims", [AG_CASES[1], AG_CASES[2]])
+def test_allgather_einsum_gelu(ctx, mode, dims):
+    import collective_overlap_amd as cce
+    n = 3
+    looped, local, oshape, ol, oc = _ag_inputs(mode, n, dims, torch.bfloat16, False, seed=11)
+    out = [torch.empty(oshape, device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, mode, looped, local, out, flags=cce.CCE_FLAG_GELU)
+    sync()
+    ref = oe.allgather_einsum(mode, ol, oc)
+    for r in range(n):
+        assert_bf16_close(np64(out[r]), numerics.gelu(ref[r]), f"rank {r}")
+
+
+def test_allgather_einsum_fp32_inputs(ctx):
+    import collective_overlap_amd as cce
+    n = 2
+    looped, local, oshape, ol, oc = _ag_inputs("rhs_cols", n, (72, 264, 136), torch.float32, False)
+    out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", looped, local, out)
+    sync()
+    ref = oe.allgather_einsum("rhs_cols", ol, oc)
+    for r in range(n):
+        assert_f32_close(np64(out[r]), ref[r], f"rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# looped Einsum-ReduceScatter
+# ---------------------------------------------------------------------------
+def _rs_inputs(mode, n, dims, dtype, probe, seed=0):
+    s, k, c = dims
+    if mode == "slice_lhs_rows":
+        a = [_t((n * s, k), seed + r, dtype, probe) for r in range(n)]     # [n m_s, K]
+        b = [_t((c, k), seed + 50 + r, dtype, probe) for r in range(n)]    # B^T [N, K]
+        oshape = (s, c)
+    else:
+        a = [_t((c, k), seed + r, dtype, probe) for r in range(n)]         # [M, K]
+        b = [_t((n * s, k), seed + 50 + r, dtype, probe) for r in range(n)]  # B^T [n n_s, K]
+        oshape = (c, s)
+    return a, b, oshape, [np64(x) for x in a], [np64(x).T for x in b]
+
+
+RS_CASES = [("slice_lhs_rows", (200, 264, 296)), ("slice_rhs_cols", (136, 264, 200)),
+            ("slice_lhs_rows", (1, 64, 40)), ("slice_rhs_cols", (8, 64, 40))]
+
+
+@pytest.mark.parametrize("mode,dims", RS_CASES)
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_einsum_reducescatter(ctx, mode, dims, n, out_dt):
+    import collective_overlap_amd as cce
+    print(f"[gpu] reducescatter {mode} n={n} dims={dims} out={out_dt}", flush=True)
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    a, b, oshape, oa, ob = _rs_inputs(mode, n, dims, torch.bfloat16, False, seed=3 * n)
+    out = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out)
+    out_s = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out_s, flags=cce.CCE_FLAG_SERIAL)
+    sync()
+    ref = oe.einsum_reducescatter(mode, oa, ob)
+    for r in range(n):
+        if out_dt == "bf16":
+            assert_bf16_close(np64(out[r]), ref[r], f"rank {r}")
+        else:
+            assert_f32_close(np64(out[r]), ref[r], f"rank {r}")
+        assert torch.equal(out[r], out_s[r]), "overlapped and serial results differ"
+
+
+@pytest.mark.parametrize("mode,dims", RS_CASES[:2])
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_einsum_reducescatter_integer_probe_bit_exact(ctx, mode, dims, n):
+    import collective_overlap_amd as cce
+    a, b, oshape, oa, ob = _rs_inputs(mode, n, dims, torch.bfloat16, True, seed=5)
+    out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out)
+    sync()
+    ref = oe.einsum_reducescatter(mode, oa, ob)
+    for r in range(n):
+        assert np.array_equal(np64(out[r]), ref[r]), f"rank {r}"
+
+
+def test_repeated_calls_reuse_events(ctx):
+    """Back-to-back calls on one context (events reused) stay correct."""
+    import collective_overlap_amd as cce
+    n = 4
+    a, b, oshape, oa, ob = _rs_inputs("slice_lhs_rows", n, (64, 128, 96), torch.bfloat16, True, 9)
+    ref = oe.einsum_reducescatter("slice_lhs_rows", oa, ob)
+    outs = []
+    for _ in range(5):
+        out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", a, b, out)
+        outs.append(out)
+    sync()
+    for out in outs:
+        for r in range(n):
+            assert np.array_equal(np64(out[r]), ref[r])
+
+
+def test_invalid_arguments_enqueue_nothing(ctx):
+    import collective_overlap_amd as cce
+    from collective_overlap_amd._lib import CceError
+    a = [torch.zeros((16, 12), device=DEV, dtype=torch.bfloat16)]   # K % 8 != 0
+    b = [torch.zeros((16, 12), device=DEV, dtype=torch.bfloat16)]
+    c = [torch.zeros((16, 16), device=DEV, dtype=torch.bfloat16)]
+    with pytest.raises(CceError) as e:
+        cce.cce_grouped_gemm(ctx, a, b, c)
+    assert e.value.status in (1, 2)
+    x = torch.zeros((64, 64), device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(CceError) as e:       # output aliases an input
+        cce.cce_grouped_gemm(ctx, [x], [x], [x])
+    assert e.value.status == 1
+    assert torch.count_nonzero(x) == 0
