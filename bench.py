@@ -1,0 +1,441 @@
+#!/usr/bin/env python3
+"""Benchmark of the looped CollectiveEinsum hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is the GPT-3-scale FFN layer, 8-way: a looped
+AllGather-Einsum into the W1 shards with GELU fused into its store, a looped
+Einsum-ReduceScatter out of the W2 shards with an fp32 travelling
+accumulator, and the fused bias + dropout + residual epilogue on every rank's
+shard.  All 8 logical ranks are separate HBM buffers on the one GPU.
+
+Prints one JSON line: whole-step bf16 TFLOP/s (value), the dominant kernel's
+roofline, the epilogue's HBM rate, the looped-vs-serial comparison with the
+hidden copy fraction, and the CPU oracle timed on a bounded sample (rank 0,
+N = 1 only), which doubles as an end-to-end parity check of the timed
+outputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "looped einsum bf16 TFLOP/s (% MFMA peak); fused reduce-epilogue HBM GB/s"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}     # dense MFMA, MI355X datasheet
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+class Gpt3Ffn:
+    name = "gpt3_ffn_n8"
+    dtype = "bf16"
+
+    def __init__(self, dev):
+        import torch
+        import workloads as W
+        self.n, self.T, self.Hd, self.F = 8, 8192, 12288, 49152
+        n, ts, fs = self.n, self.T // self.n, self.F // self.n
+        self.ts, self.fs = ts, fs
+        bf = torch.bfloat16
+        self.X = [W.normal((ts, self.Hd), 1.0, s, device=dev) for s in range(n)]
+        self.W1 = [W.weight_store(self.Hd, fs, 0.02, 10 + r, device=dev) for r in range(n)]
+        self.W2 = [W.weight_store(fs, self.Hd, 0.02, 20 + r, device=dev) for r in range(n)]
+        self.b = W.normal((self.Hd,), 0.02, 30, device=dev)
+        self.R = [W.normal((ts, self.Hd), 1.0, 40 + r, device=dev) for r in range(n)]
+        self.H = [torch.empty((self.T, fs), device=dev, dtype=bf) for _ in range(n)]
+        self.acc = [torch.empty((ts, self.Hd), device=dev) for _ in range(n)]
+        self.out = [torch.empty((ts, self.Hd), device=dev, dtype=bf) for _ in range(n)]
+        import collective_overlap_amd as cce
+        self.ws_ag = torch.empty(cce.cce_looped_allgather_einsum_workspace(
+            n, "lhs_rows", "bf16", "bf16", (ts, self.Hd), (self.T, fs)), dtype=torch.uint8,
+            device=dev)
+        self.ws_rs = torch.empty(cce.cce_looped_einsum_reducescatter_workspace(
+            n, "slice_lhs_rows", (ts, self.Hd)), dtype=torch.uint8, device=dev)
+        self.flops = 2 * (2.0 * self.T * self.Hd * fs * n)
+        self.p = 0.1
+
+    def config(self):
+        return {"workload": self.name, "n_ranks": self.n, "tokens": self.T, "hidden": self.Hd,
+                "ffn": self.F, "w1_shard": [self.Hd, self.fs], "w2_shard": [self.fs, self.Hd],
+                "p_drop": self.p, "acc_dtype": "f32", "global_batch": self.T}
+
+    def run(self, ctx, flags=0):
+        import collective_overlap_amd as cce
+        cce.cce_looped_allgather_einsum(ctx, "lhs_rows", self.X, self.W1, self.H, self.ws_ag,
+                                        flags=flags | cce.CCE_FLAG_GELU)
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", self.H, self.W2, self.acc,
+                                            self.ws_rs, flags=flags)
+        for r in range(self.n):
+            cce.cce_fused_reduce_epilogue(ctx, [self.acc[r]], self.b, self.R[r], self.out[r],
+                                          self.p, 0, 0, mask_row0=r * self.ts, mask_col0=0,
+                                          mask_ld=self.Hd)
+
+    def oracle_sample(self, t=8):
+        """The oracle end to end on t tokens of every shard; returns
+        (seconds, flops, description, rel error vs the device outputs)."""
+        import numpy as np
+        from oracle import einsum as oe, epilogue as oep, numerics
+        f64 = _f64
+        xs = [f64(x[:t]) for x in self.X]
+        w1 = [f64(w).T for w in self.W1]
+        w2 = [f64(w).T for w in self.W2]
+        b, rr = f64(self.b), [f64(r[:t]) for r in self.R]
+        t0 = time.perf_counter()
+        h = oe.allgather_einsum("lhs_rows", xs, w1)
+        h = [numerics.bf16_round(numerics.gelu(x).astype(np.float32)).astype(np.float64) for x in h]
+        a = oe.einsum_reducescatter("slice_lhs_rows", h, w2)
+        outs = [oep.fused_reduce_epilogue([a[r]], b, rr[r], self.p, 0, 0, row0=r * self.ts,
+                                          col0=0, mask_ld=self.Hd)[0] for r in range(self.n)]
+        dt = time.perf_counter() - t0
+        got = np.concatenate([f64(o[:t]) for o in self.out])
+        ref = np.concatenate(outs)
+        err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        flops = 2 * (2.0 * self.n * t * self.Hd * self.fs * self.n)
+        return dt, flops, f"{t} tokens per shard ({self.n * t} of {self.T}), all 8 ranks, " \
+                          f"float64 NumPy oracle end to end", err
+
+
+class AttnOutProj:
+    name = "attn_outproj_n8"
+    dtype = "bf16"
+
+    def __init__(self, dev):
+        import torch
+        import workloads as W
+        self.n, self.M, self.K, self.N = 8, 8192, 1024, 8192
+        n = self.n
+        bf = torch.bfloat16
+        self.IN = [W.normal((self.M, self.K), 1.0, k, device=dev) for k in range(n)]
+        self.Wt = [W.weight_store(self.K, self.N, 0.02, 10 + k, device=dev) for k in range(n)]
+        self.P = [torch.empty((self.M, self.N), device=dev, dtype=bf) for _ in range(n)]
+        self.b = W.normal((self.N,), 0.02, 20, device=dev)
+        self.R = W.normal((self.M, self.N), 1.0, 21, device=dev)
+        self.out = torch.empty((self.M, self.N), device=dev, dtype=bf)
+        self.flops = 2.0 * self.M * self.N * self.K * n
+        self.p = 0.1
+
+    def config(self):
+        return {"workload": self.name, "n_ranks": self.n, "tokens": self.M, "in_shard": self.K,
+                "hidden": self.N, "p_drop": self.p, "global_batch": self.M}
+
+    def run(self, ctx, flags=0):
+        import collective_overlap_amd as cce
+        cce.cce_grouped_gemm(ctx, self.IN, self.Wt, self.P)
+        cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, self.p, 0, 0)
+
+    def oracle_sample(self, t=16):
+        import numpy as np
+        from oracle import einsum as oe, epilogue as oep, numerics
+        f64 = _f64
+        ins = [f64(x[:t]) for x in self.IN]
+        ws = [f64(w).T for w in self.Wt]
+        b, rr = f64(self.b), f64(self.R[:t])
+        t0 = time.perf_counter()
+        parts = oe.local_matmuls(ins, ws)
+        parts = [numerics.bf16_round(p.astype(np.float32)).astype(np.float64) for p in parts]
+        ref, _ = oep.fused_reduce_epilogue(parts, b, rr, self.p, 0, 0, mask_ld=self.N)
+        dt = time.perf_counter() - t0
+        err = float(np.linalg.norm(f64(self.out[:t]) - ref) / np.linalg.norm(ref))
+        return dt, 2.0 * t * self.K * self.N * self.n, \
+            f"{t} of {self.M} token rows, all 8 partials, float64 NumPy oracle", err
+
+
+class Mlp2:
+    name = "mlp2_n4"
+    dtype = "bf16"
+
+    def __init__(self, dev):
+        import torch
+        import workloads as W
+        self.n, self.B, self.F, self.Hh = 4, 2048, 4096, 16384
+        n = self.n
+        bf = torch.bfloat16
+        self.X = [W.normal((self.B, self.F), 1.0, r, device=dev) for r in range(n)]
+        self.W1 = [W.weight_store(self.F, self.Hh // n, 0.02, 10 + s, device=dev) for s in range(n)]
+        self.W2 = [W.weight_store(self.Hh, self.F // n, 0.02, 20 + s, device=dev) for s in range(n)]
+        self.H = [torch.empty((self.B, self.Hh), device=dev, dtype=bf) for _ in range(n)]
+        self.Y = [torch.empty((self.B, self.F), device=dev, dtype=bf) for _ in range(n)]
+        self.flops = 2 * (2.0 * self.B * self.F * self.Hh * n)
+
+    def config(self):
+        return {"workload": self.name, "n_ranks": self.n, "batch": self.B, "features": self.F,
+                "hidden": self.Hh, "global_batch": self.B * self.n}
+
+    def run(self, ctx, flags=0):
+        import collective_overlap_amd as cce
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W1, self.X, self.H,
+                                        flags=flags | cce.CCE_FLAG_GELU)
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W2, self.H, self.Y, flags=flags)
+
+    def oracle_sample(self, t=8):
+        import numpy as np
+        from oracle import einsum as oe, numerics
+        f64 = _f64
+        xs = [f64(x[:t]) for x in self.X]
+        w1 = [f64(w).T for w in self.W1]
+        w2 = [f64(w).T for w in self.W2]
+        t0 = time.perf_counter()
+        h = oe.allgather_einsum("rhs_cols", w1, xs)
+        h = [numerics.bf16_round(numerics.gelu(x).astype(np.float32)).astype(np.float64) for x in h]
+        y = oe.allgather_einsum("rhs_cols", w2, h)
+        dt = time.perf_counter() - t0
+        got = np.concatenate([f64(o[:t]) for o in self.Y])
+        ref = np.concatenate(y)
+        err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        return dt, 2 * (2.0 * t * self.F * self.Hh * self.n), \
+            f"{t} of {self.B} rows per rank, all 4 ranks, float64 NumPy oracle", err
+
+
+class RsN8:
+    name = "rs_n8"
+    dtype = "bf16"
+
+    def __init__(self, dev):
+        import torch
+        import workloads as W
+        self.n, self.T, self.K, self.N = 8, 16384, 2048, 4096
+        n = self.n
+        self.X = [W.normal((self.T, self.K), 1.0, r, device=dev) for r in range(n)]
+        self.Wt = [W.weight_store(self.K, self.N, 0.02, 10 + r, device=dev) for r in range(n)]
+        self.out = [torch.empty((self.T // n, self.N), device=dev) for _ in range(n)]
+        self.flops = 2.0 * self.T * self.K * self.N * n
+
+    def config(self):
+        return {"workload": self.name, "n_ranks": self.n, "tokens": self.T, "k_shard": self.K,
+                "hidden": self.N, "acc_dtype": "f32", "global_batch": self.T}
+
+    def run(self, ctx, flags=0):
+        import collective_overlap_amd as cce
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", self.X, self.Wt, self.out,
+                                            flags=flags)
+
+    def oracle_sample(self, t=16):
+        import numpy as np
+        from oracle import einsum as oe
+        f64 = _f64
+        ms = self.T // self.n
+        a = [np.concatenate([f64(x[s * ms:s * ms + t]) for s in range(self.n)]) for x in self.X]
+        b = [f64(w).T for w in self.Wt]
+        t0 = time.perf_counter()
+        ref = oe.einsum_reducescatter("slice_lhs_rows", a, b)
+        dt = time.perf_counter() - t0
+        got = np.concatenate([f64(o[:t]) for o in self.out])
+        err = float(np.linalg.norm(got - np.concatenate(ref)) / np.linalg.norm(np.concatenate(ref)))
+        return dt, 2.0 * self.n * t * self.K * self.N * self.n, \
+            f"{t} of {ms} rows of every shard, float64 NumPy oracle", err
+
+
+class AgFp32N2:
+    name = "ag_fp32_n2"
+    dtype = "f32"
+
+    def __init__(self, dev):
+        import torch
+        import workloads as W
+        self.n = 2
+        self.X = [W.uniform((64, 256), r, device=dev) for r in range(2)]
+        self.Wt = [W.uniform((512, 256), 10 + r, device=dev) for r in range(2)]
+        self.Y = [torch.empty((64, 1024), device=dev) for _ in range(2)]
+        self.P = [W.uniform((64, 256), 20 + k, device=dev) for k in range(2)]
+        self.b = W.uniform((256,), 30, device=dev)
+        self.R = W.uniform((64, 256), 31, device=dev)
+        self.out = torch.empty((64, 256), device=dev)
+        self.flops = 2.0 * 64 * 256 * 1024 * 2
+
+    def config(self):
+        return {"workload": self.name, "n_ranks": 2, "x": [64, 256], "w_shard": [256, 512],
+                "epilogue": [64, 256], "p_drop": 0.1, "global_batch": 128}
+
+    def run(self, ctx, flags=0):
+        import collective_overlap_amd as cce
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.Wt, self.X, self.Y, flags=flags)
+        cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, 0.1, 0, 0)
+
+    def oracle_sample(self, t=64):
+        import numpy as np
+        from oracle import einsum as oe
+        f64 = _f64
+        t0 = time.perf_counter()
+        ref = oe.allgather_einsum("rhs_cols", [f64(w).T for w in self.Wt], [f64(x) for x in self.X])
+        dt = time.perf_counter() - t0
+        err = float(max(np.linalg.norm(f64(y) - r) / np.linalg.norm(r) for y, r in zip(self.Y, ref)))
+        return dt, self.flops, "whole workload, float64 NumPy oracle", err
+
+
+WORKLOADS = {c.name: c for c in (Gpt3Ffn, AttnOutProj, Mlp2, RsN8, AgFp32N2)}
+
+
+def _f64(t):
+    import numpy as np
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Measurement helpers
+# ---------------------------------------------------------------------------
+def timed(step, ctx, steps, flags, profile):
+    import torch
+    torch.cuda.synchronize()
+    if profile:
+        ctx.set_profiling(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run(ctx, flags)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs = []
+    if profile:
+        recs = ctx.read_profile()
+        ctx.set_profiling(False)
+    return wall, recs
+
+
+def gemm_roofline(recs, dtype, steps):
+    """Dominant GEMM kernel: the launch shape (by FLOPs per launch) with the
+    largest total time."""
+    groups = {}
+    for r in recs:
+        if r["kind"] != "gemm":
+            continue
+        groups.setdefault(r["flops"], []).append(r["ms"])
+    if not groups:
+        return None, {}
+    per = {}
+    for fl, ms in groups.items():
+        avg = sum(ms) / len(ms)
+        per[fl] = dict(flops_per_launch=fl, launches=len(ms), avg_ms=avg,
+                       tflops=fl / (avg * 1e-3) / 1e12, total_ms=sum(ms) / steps)
+    dom = max(per.values(), key=lambda d: d["total_ms"])
+    peak = PEAK_TFLOPS[dtype]
+    roof = {"bound": "mfma", "achieved": round(dom["tflops"], 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4), "traffic": None,
+            "kernel": "grouped GEMM launch", "flops_per_launch": dom["flops_per_launch"],
+            "avg_launch_ms": round(dom["avg_ms"], 4), "launches": dom["launches"]}
+    return roof, per
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt3_ffn_n8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serial", action="store_true", help="skip the unoverlapped comparison")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: all N logical ranks live as "
+                                   "separate HBM buffers of a single MI355X; --gpus must be 1",
+                          "n_gpus": a.gpus}), flush=True)
+        return 2
+
+    import torch
+    import collective_overlap_amd as cce
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = "cuda:0"
+    log(f"device {torch.cuda.get_device_name(0)}; workload {a.workload}")
+    step = WORKLOADS[a.workload](dev)
+    ctx = cce.Context(0)
+    torch.cuda.synchronize()
+    log("inputs ready; warmup")
+    for _ in range(a.warmup):
+        step.run(ctx, 0)
+    torch.cuda.synchronize()
+    log("timed region (overlapped)")
+    wall, recs = timed(step, ctx, a.steps, 0, profile=True)
+    ms_per_step = wall / a.steps * 1e3
+    value = step.flops * a.steps / wall / 1e12
+    roof, per_shape = gemm_roofline(recs, step.dtype, a.steps)
+
+    epi = [r for r in recs if r["kind"] == "epilogue"]
+    epi_info = None
+    if epi:
+        tb = sum(r["bytes"] for r in epi)
+        tm = sum(r["ms"] for r in epi)
+        gbs = tb / (tm * 1e-3) / 1e9
+        epi_info = {"GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                    "launches": len(epi), "avg_launch_ms": round(tm / len(epi), 4),
+                    "bytes_per_launch": tb / len(epi)}
+    gemm_ms = sum(r["ms"] for r in recs if r["kind"] == "gemm") / a.steps
+    copy_recs = [r for r in recs if r["kind"] == "copy"]
+
+    overlap = None
+    if not a.no_serial and copy_recs:
+        log("timed region (serial: same kernels, copies on the compute stream)")
+        for _ in range(max(1, a.warmup // 2)):
+            step.run(ctx, cce.CCE_FLAG_SERIAL)
+        swall, srecs = timed(step, ctx, a.steps, cce.CCE_FLAG_SERIAL, profile=True)
+        s_ms = swall / a.steps * 1e3
+        copy_ms = sum(r["ms"] for r in srecs if r["kind"] == "copy") / a.steps
+        copy_bytes = sum(r["bytes"] for r in srecs if r["kind"] == "copy") / a.steps
+        hidden = 1.0 - (ms_per_step - (s_ms - copy_ms)) / copy_ms if copy_ms > 0 else 1.0
+        overlap = {"overlapped_ms": round(ms_per_step, 3), "serial_ms": round(s_ms, 3),
+                   "speedup_vs_serial": round(s_ms / ms_per_step, 4),
+                   "copy_ms_serial": round(copy_ms, 3),
+                   "copy_GB/s_serial": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
+                   "hidden_copy_frac": round(min(1.0, max(0.0, hidden)), 4)}
+
+    cpu = None
+    parity = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline: oracle on a bounded sample")
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            threads = os.cpu_count()
+        dt, fl, desc, err = step.oracle_sample()
+        cpu = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "sample": desc, "seconds": round(dt, 3),
+               "host_cpus": os.cpu_count(), "cpu_model": platform.processor() or platform.machine()}
+        parity = {"rel_fro_err_vs_oracle": err, "bar": 2e-2 if step.dtype == "bf16" else 1e-5,
+                  "ok": err <= (2e-2 if step.dtype == "bf16" else 1e-5)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": step.dtype,
+        "data": "synthetic (seeded torch generators; no dataset)",
+        "config": step.config(),
+        "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "epilogue": epi_info,
+        "overlap": overlap,
+        "gemm_ms_per_step": round(gemm_ms, 3),
+        "gemm_shapes": list(per_shape.values()),
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+    ctx.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -17,6 +17,7 @@ CCE_F32, CCE_BF16 = 0, 1
 CCE_MAX_RANKS = 64
 CCE_FLAG_SERIAL = 0x1
 CCE_FLAG_GELU = 0x2
+CCE_FLAG_COPY_DMA = 0x4
 
 AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3}
 RS_MODES = {"slice_lhs_rows": 0, "slice_rhs_cols": 1}
@@ -24,6 +25,11 @@ RS_MODES = {"slice_lhs_rows": 0, "slice_rhs_cols": 1}
 
 class cce_mat(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+class cce_prof_record(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("iter", ctypes.c_int32), ("ms", ctypes.c_float),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
 
 
 class CceError(RuntimeError):
@@ -48,6 +54,8 @@ PROTOTYPES = {
     "cce_version": (ctypes.c_char_p, []),
     "cce_ctx_create": (_I, [_I, ctypes.POINTER(_P)]),
     "cce_ctx_destroy": (_I, [_P]),
+    "cce_ctx_set_profiling": (_I, [_P, _I]),
+    "cce_ctx_read_profile": (_I, [_P, _I, ctypes.POINTER(cce_prof_record), ctypes.POINTER(_I)]),
     "cce_shard_schedule": (_I, [_I, _I, ctypes.POINTER(ctypes.c_int32)]),
     "cce_looped_allgather_einsum_workspace": (_I, [_I, _I, _I, _I, cce_mat, cce_mat,
                                                    ctypes.POINTER(_SZ)]),

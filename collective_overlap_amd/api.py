@@ -16,7 +16,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_GELU, CCE_FLAG_SERIAL, AG_MODES, RS_MODES,
+from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_COPY_DMA, CCE_FLAG_GELU, CCE_FLAG_SERIAL,
+                   AG_MODES, RS_MODES,
                    cce_mat, check, lib, ptr_array)
 
 __all__ = [
@@ -24,7 +25,7 @@ __all__ = [
     "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
     "cce_looped_einsum_reducescatter_workspace", "cce_grouped_gemm",
     "cce_fused_reduce_epilogue", "cce_describe_plan", "cce_version",
-    "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "AG_MODES", "RS_MODES",
+    "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "AG_MODES", "RS_MODES",
 ]
 
 _DT = {torch.float32: CCE_F32, torch.bfloat16: CCE_BF16}
@@ -83,6 +84,20 @@ class Context:
     @property
     def handle(self):
         return self._h
+
+    def set_profiling(self, enable: bool = True):
+        """Bracket every kernel / permute step with timing events."""
+        check(lib().cce_ctx_set_profiling(self._h, 1 if enable else 0), "cce_ctx_set_profiling")
+
+    def read_profile(self, max_records: int = 65536) -> list[dict]:
+        """Wait for the recorded events; return and clear the records."""
+        recs = (_lib.cce_prof_record * max_records)()
+        n = ctypes.c_int()
+        check(lib().cce_ctx_read_profile(self._h, max_records, recs, ctypes.byref(n)),
+              "cce_ctx_read_profile")
+        kinds = {0: "gemm", 1: "copy", 2: "epilogue"}
+        return [dict(kind=kinds.get(r.kind, str(r.kind)), iter=r.iter, ms=r.ms, flops=r.flops,
+                     bytes=r.bytes) for r in recs[:n.value]]
 
     def close(self):
         if self._h:

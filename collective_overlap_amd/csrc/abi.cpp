@@ -5,8 +5,10 @@
 // (Anthony et al., "MCR-DL: Mix-and-Match Communication Runtime for Deep
 // Learning", its synchronization section): transfers are posted to an
 // internal communication stream, an event is recorded after them, and the
-// consumer waits on that event instead of synchronising the host.  Each call
-// forks the copy stream from the caller's stream and joins it back.
+// consumer waits on that event instead of synchronising the host.  A call
+// forks the copy stream from the caller's stream when its first copy reads
+// caller data; the last copy is always waited for by the last GEMM on the
+// caller's stream, which joins the copy stream back.
 
 #include <hip/hip_runtime.h>
 
@@ -18,10 +20,21 @@
 
 #include "cce_internal.hpp"
 
+struct cce_prof_slot {
+  int kind = 0;
+  int iter = -1;
+  double flops = 0, bytes = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 struct cce_ctx {
   int device = 0;
   hipStream_t copy = nullptr;
-  std::vector<hipEvent_t> events;
+  std::vector<hipEvent_t> events;        // ordering events (no timing)
+  bool profiling = false;
+  std::vector<hipEvent_t> timing_pool;   // timing events, reused
+  size_t timing_used = 0;
+  std::vector<cce_prof_slot> prof;
 };
 
 namespace cce {
@@ -29,7 +42,8 @@ namespace cce {
 namespace {
 thread_local std::string g_err;
 
-constexpr int64_t kMaxOperandBytes = (int64_t{1} << 31) - 256;
+// GEMM operands are addressed through 32-bit buffer offsets (see gemm.hip).
+constexpr int64_t kMaxOperandBytes = (int64_t{1} << 30) - 256;
 
 size_t esize(cce_dtype t) { return t == CCE_F32 ? 4 : 2; }
 bool dtype_ok(int t) { return t == CCE_F32 || t == CCE_BF16; }
@@ -123,6 +137,40 @@ cce_status ensure_events(cce_ctx* ctx, int n) {
     HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     ctx->events.push_back(e);
   }
+  return CCE_OK;
+}
+
+// Timing brackets (only while profiling is enabled).
+cce_status timing_event(cce_ctx* ctx, hipEvent_t* out) {
+  if (ctx->timing_used == ctx->timing_pool.size()) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    ctx->timing_pool.push_back(e);
+  }
+  *out = ctx->timing_pool[ctx->timing_used++];
+  return CCE_OK;
+}
+
+cce_status prof_begin(cce_ctx* ctx, hipStream_t s, int kind, int iter, double flops, double bytes,
+                      int* slot) {
+  *slot = -1;
+  if (!ctx->profiling) return CCE_OK;
+  cce_prof_slot p;
+  p.kind = kind;
+  p.iter = iter;
+  p.flops = flops;
+  p.bytes = bytes;
+  CCE_TRY(timing_event(ctx, &p.start));
+  CCE_TRY(timing_event(ctx, &p.stop));
+  HIP_TRY(hipEventRecord(p.start, s));
+  ctx->prof.push_back(p);
+  *slot = static_cast<int>(ctx->prof.size()) - 1;
+  return CCE_OK;
+}
+
+cce_status prof_end(cce_ctx* ctx, hipStream_t s, int slot) {
+  if (slot < 0) return CCE_OK;
+  HIP_TRY(hipEventRecord(ctx->prof[slot].stop, s));
   return CCE_OK;
 }
 
@@ -248,6 +296,10 @@ cce_status fail(cce_status s, const std::string& msg) {
 // ---------------------------------------------------------------------------
 namespace {
 
+hipMemcpyKind copy_kind(uint32_t flags) {
+  return (flags & CCE_FLAG_COPY_DMA) ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+}
+
 hipStream_t stream_of(const Op& o, hipStream_t compute, hipStream_t copy, bool serial) {
   return (serial || o.stream == S_COMPUTE) ? compute : copy;
 }
@@ -269,6 +321,7 @@ struct AgCall {
   cce_mat oshape;
   char* ws;
   bool gelu;
+  hipMemcpyKind copy_kind;
 };
 
 // pointer + leading dimension of a symbolic buffer
@@ -301,16 +354,20 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
     }
     if (o.kind == OP_COPY) {
       const int64_t w = c.lshape.cols * static_cast<int64_t>(ein);
+      int slot;
+      CCE_TRY(prof_begin(ctx, s, 1, o.iter, 0.0,
+                         2.0 * static_cast<double>(w) * c.lshape.rows * o.items.size(), &slot));
       for (const Item& it : o.items) {
         const PtrLd src = ag_resolve(c, it.a), dst = ag_resolve(c, it.c);
         if (c.lshape.rows == 0 || w == 0) continue;
         if (src.ld == dst.ld) {
-          HIP_TRY(hipMemcpyAsync(dst.p, src.p, c.lshape.rows * src.ld * ein, hipMemcpyDeviceToDevice, s));
+          HIP_TRY(hipMemcpyAsync(dst.p, src.p, c.lshape.rows * src.ld * ein, c.copy_kind, s));
         } else {
           HIP_TRY(hipMemcpy2DAsync(dst.p, dst.ld * ein, src.p, src.ld * ein, w, c.lshape.rows,
-                                   hipMemcpyDeviceToDevice, s));
+                                   c.copy_kind, s));
         }
       }
+      CCE_TRY(prof_end(ctx, s, slot));
       continue;
     }
     // GEMM
@@ -362,7 +419,10 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
         L.p.cin[r] = nullptr;
       }
     }
+    int slot;
+    CCE_TRY(prof_begin(ctx, compute, 0, o.iter, 2.0 * L.M * L.N * L.K * L.groups, 0.0, &slot));
     CCE_TRY(launch_grouped_gemm(L, compute));
+    CCE_TRY(prof_end(ctx, compute, slot));
   }
   return CCE_OK;
 }
@@ -377,6 +437,7 @@ struct RsCall {
   void* const* out;
   cce_mat oshape;
   char* ws;
+  hipMemcpyKind copy_kind;
 };
 
 PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
@@ -411,10 +472,13 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
     if (o.kind == OP_COPY) {
       const int64_t bytes = (rows_mode ? ext * c.g.acc_ld : c.g.other * c.g.acc_ld) * 4;
       if (bytes == 0) continue;
+      int slot;
+      CCE_TRY(prof_begin(ctx, s, 1, o.iter, 0.0, 2.0 * bytes * o.items.size(), &slot));
       for (const Item& it : o.items) {
         const PtrLd src = rs_resolve(c, it.a), dst = rs_resolve(c, it.c);
-        HIP_TRY(hipMemcpyAsync(dst.p, src.p, bytes, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(dst.p, src.p, bytes, c.copy_kind, s));
       }
+      CCE_TRY(prof_end(ctx, s, slot));
       continue;
     }
     GemmLaunch L;
@@ -455,7 +519,12 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
         L.p.cin[r] = nullptr;
       }
     }
-    if (L.M > 0 && L.N > 0) CCE_TRY(launch_grouped_gemm(L, compute));
+    if (L.M > 0 && L.N > 0) {
+      int slot;
+      CCE_TRY(prof_begin(ctx, compute, 0, o.iter, 2.0 * L.M * L.N * L.K * L.groups, 0.0, &slot));
+      CCE_TRY(launch_grouped_gemm(L, compute));
+      CCE_TRY(prof_end(ctx, compute, slot));
+    }
   }
   return CCE_OK;
 }
@@ -507,8 +576,43 @@ cce_status cce_ctx_destroy(cce_ctx* ctx) {
   DeviceGuard guard(ctx->device);
   hipStreamSynchronize(ctx->copy);
   for (hipEvent_t e : ctx->events) hipEventDestroy(e);
+  for (hipEvent_t e : ctx->timing_pool) hipEventDestroy(e);
   hipStreamDestroy(ctx->copy);
   delete ctx;
+  return CCE_OK;
+}
+
+cce_status cce_ctx_set_profiling(cce_ctx* ctx, int enable) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  ctx->profiling = enable != 0;
+  if (enable) {
+    ctx->prof.clear();
+    ctx->timing_used = 0;
+  }
+  return CCE_OK;
+}
+
+cce_status cce_ctx_read_profile(cce_ctx* ctx, int max_records, cce_prof_record* out, int* n_out) {
+  clear_error();
+  if (!ctx || !n_out || (max_records > 0 && !out)) return fail(CCE_EINVAL, "NULL argument");
+  DeviceGuard guard(ctx->device);
+  int n = 0;
+  for (const cce_prof_slot& p : ctx->prof) {
+    if (n >= max_records) break;
+    HIP_TRY(hipEventSynchronize(p.stop));
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, p.start, p.stop));
+    out[n].kind = p.kind;
+    out[n].iter = p.iter;
+    out[n].ms = ms;
+    out[n].flops = p.flops;
+    out[n].bytes = p.bytes;
+    ++n;
+  }
+  *n_out = n;
+  ctx->prof.clear();
+  ctx->timing_used = 0;
   return CCE_OK;
 }
 
@@ -546,7 +650,8 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
                                        cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU)) return fail(CCE_EINVAL, "unknown flags");
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA))
+    return fail(CCE_EINVAL, "unknown flags");
   if (!looped || !local || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   AgGeom g;
   CCE_TRY(ag_geometry(n_ranks, mode, in_t, out_t, looped_shard, &local_shape, out_shape, g));
@@ -554,7 +659,7 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
   const int64_t ls = span_bytes(looped_shard, ein), cs = span_bytes(local_shape, ein),
                 os = span_bytes(out_shape, eout);
   if (ls > kMaxOperandBytes || cs > kMaxOperandBytes)
-    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+    return fail(CCE_EUNSUPPORTED, "a GEMM operand exceeds 1 GiB");
   std::vector<Range> ranges;
   for (int r = 0; r < n_ranks; ++r) {
     const std::string rs = std::to_string(r);
@@ -579,7 +684,7 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
   const Plan plan = build_allgather_plan(n_ranks, mode, g.case2_ws, serial);
   CCE_TRY(ensure_events(ctx, plan.n_events));
   AgCall c{g, in_t, out_t, looped, looped_shard, local, local_shape, out, out_shape,
-           static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0};
+           static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0, copy_kind(flags)};
   return ag_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
 }
 
@@ -602,7 +707,8 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
                                            cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~CCE_FLAG_SERIAL) return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA))
+    return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
   if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   RsGeom g;
@@ -624,7 +730,7 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
   const int64_t as = span_bytes(a_shape, ein), bs = span_bytes(b_shape, ein),
                 os = span_bytes(out_shard, eout);
   if (as > kMaxOperandBytes || bs > kMaxOperandBytes)
-    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+    return fail(CCE_EUNSUPPORTED, "a GEMM operand exceeds 1 GiB");
   std::vector<Range> ranges;
   for (int r = 0; r < n_ranks; ++r) {
     const std::string rs = std::to_string(r);
@@ -648,7 +754,8 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
   const Plan plan = build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial);
   CCE_TRY(ensure_events(ctx, plan.n_events));
-  RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace)};
+  RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
+           copy_kind(flags)};
   return rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
 }
 
@@ -674,7 +781,7 @@ cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtyp
   const int64_t as = span_bytes(a_shape, ein), bs = span_bytes(b_shape, ein),
                 cs = span_bytes(c_shape, eout);
   if (as > kMaxOperandBytes || bs > kMaxOperandBytes)
-    return fail(CCE_EUNSUPPORTED, "an operand exceeds 2 GiB");
+    return fail(CCE_EUNSUPPORTED, "a GEMM operand exceeds 1 GiB");
   std::vector<Range> ranges;
   for (int r = 0; r < n_groups; ++r) {
     const std::string rs = std::to_string(r);
@@ -706,7 +813,11 @@ cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtyp
     L.p.c[r] = c[r];
     L.p.cin[r] = nullptr;
   }
-  return launch_grouped_gemm(L, stream);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int slot;
+  CCE_TRY(prof_begin(ctx, hs, 0, -1, 2.0 * L.M * L.N * L.K * L.groups, 0.0, &slot));
+  CCE_TRY(launch_grouped_gemm(L, stream));
+  return prof_end(ctx, hs, slot);
 }
 
 cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype part_t,
@@ -787,7 +898,14 @@ cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype par
     L.scale = static_cast<float>(1.0 / (1.0 - p_drop));
   }
   DeviceGuard guard(ctx->device);
-  return launch_fused_epilogue(L, stream);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const double ebytes = static_cast<double>(shape.rows) * shape.cols *
+                            (static_cast<double>(n_partials) * ep + (residual ? eo : 0) + eo) +
+                        (bias ? static_cast<double>(shape.cols) * eo : 0.0);
+  int slot;
+  CCE_TRY(prof_begin(ctx, hs, 2, -1, 0.0, ebytes, &slot));
+  CCE_TRY(launch_fused_epilogue(L, stream));
+  return prof_end(ctx, hs, slot);
 }
 
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, uint32_t flags,

@@ -43,9 +43,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
-constexpr int kOutOfRange = 0x7ffffff0;    // offset steered past num_records
+constexpr int kOob = 0x40000000;           // added to steer a load past num_records
+constexpr int64_t kMaxRsrcBytes = kOob - 256;
+
+// Interleave groups of the scheduling region: for every MFMA one DS read,
+// one DS write and one VMEM load while any of those remain.
+template <int NMF, int NRD, int NWR, int NGL>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int q = 0; q < NMF; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    if (q < NWR) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+    if (q < NGL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+  }
+  if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
+  if (NWR > NMF) __builtin_amdgcn_sched_group_barrier(0x200, NWR - NMF, 0);
+  if (NGL > NMF) __builtin_amdgcn_sched_group_barrier(0x020, NGL - NMF, 0);
+}
 
 struct KArgs {
   int groups;
@@ -56,7 +74,7 @@ struct KArgs {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
+  int n = bytes > kMaxRsrcBytes ? static_cast<int>(kMaxRsrcBytes) : static_cast<int>(bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferFlags);
 }
 
@@ -76,6 +94,17 @@ __device__ __forceinline__ void map_tile(const KArgs& a, int& g, int& tm, int& t
   tm = first + in_band % rows;
   tn = in_band / rows;
 }
+
+// 16-byte global->LDS load: lane L of the wave writes bytes [16 L, 16 L + 16)
+// after the wave-uniform LDS address `lds`.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voffset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
+// vmcnt[5:4] bits 15:14).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float gelu_exact(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
@@ -123,6 +152,21 @@ __device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, const fl
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
+//
+// Software pipeline of one 64-deep k tile (4 steps of k16), with fragment
+// double buffering so that the LDS reads for step kk+1 issue between the
+// MFMAs of step kk:
+//   kk=0: MFMA(F0) | read F1 (kk=1)
+//   kk=1: MFMA(F1) | read F0 (kk=2)
+//   kk=2: MFMA(F0) | read F1 (kk=3)
+//   barrier (waits for the next tile's global->LDS loads)
+//   kk=3: MFMA(F1) | read F0 (kk=0 of the next tile) | global->LDS loads of
+//                    the tile after next into this tile's buffer
+// One barrier per k tile.  It separates (a) the other buffer's loads from its
+// first reads and (b) this buffer's last reads (issued in kk=2 and completed
+// before the barrier) from the loads that overwrite it.  The loop body has no
+// branches: loads past the end of K are steered out of range and land as
+// zeros, so the tail needs no special case.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, typename TOut, int EPI, bool GELU>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
@@ -154,40 +198,65 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + static_cast<int64_t>(m0) * a.lda, a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<int64_t>(n0) * a.ldb, b_bytes);
 
-  // Per-thread chunk coordinates: chunk c = tid % 8 of rows tid/8 + 32*p.
-  const int lc = tid & 7;
-  const int lr = tid >> 3;
-  int a_off[A_CH], b_off[B_CH];       // byte offsets at k0 = 0 (row part)
-  int a_lds[A_CH], b_lds[B_CH];       // LDS byte offsets (swizzled)
+  // Direct global->LDS staging (buffer_load ... lds): one instruction of a
+  // wave fills 1 KB of LDS = 8 consecutive rows of 128 B, lane L landing at
+  // byte 16 L, i.e. row L / 8, physical chunk L % 8.  The lane fetches the
+  // logical chunk that belongs there under the swizzle
+  //   physical = logical ^ f(row),  f(row) = (row & 7) ^ ((row >> 3) & 1),
+  // which makes the fragment reads below conflict-free for 8-lane (32-bank)
+  // and 16-lane (64-bank) LDS service groups alike.  For wave w and
+  // instruction p the rows are 8 (4 p + w) + L / 8, so the fetched logical
+  // chunk (L % 8) ^ (L / 8) ^ (w & 1) does not depend on p.
+  constexpr int A_DMA = BM * ROWB / (4 * 1024);   // instructions per wave per stage
+  constexpr int B_DMA = BN * ROWB / (4 * 1024);
+  const int dl_row = lane >> 3;
+  const int dl_chunk = (lane & 7) ^ dl_row ^ (wave & 1);
+  uint32_t a_off[A_DMA], b_off[B_DMA];
 #pragma unroll
-  for (int p = 0; p < A_CH; ++p) {
-    const int r = lr + 32 * p;
-    a_off[p] = (m0 + r < a.M) ? (r * a.lda + lc * 8) * 2 : kOutOfRange;
-    a_lds[p] = r * ROWB + ((lc ^ (r & 7)) << 4);
+  for (int p = 0; p < A_DMA; ++p) {
+    const int r = 8 * (4 * p + wave) + dl_row;
+    a_off[p] = (m0 + r < a.M) ? (r * a.lda + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
 #pragma unroll
-  for (int p = 0; p < B_CH; ++p) {
-    const int r = lr + 32 * p;
-    b_off[p] = (n0 + r < a.N) ? (r * a.ldb + lc * 8) * 2 : kOutOfRange;
-    b_lds[p] = BM * ROWB + r * ROWB + ((lc ^ (r & 7)) << 4);
+  for (int p = 0; p < B_DMA; ++p) {
+    const int r = 8 * (4 * p + wave) + dl_row;
+    b_off[p] = (n0 + r < a.N) ? (r * a.ldb + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
-
-  u32x4 ra_reg[A_CH], rb_reg[B_CH];
-  auto gload = [&](int k0) {
-    const bool kin = (k0 + lc * 8) < a.K;
+  // Rows past M / N start at kOob; chunks past K add kOob.  Operands are
+  // smaller than kOob bytes, so either lands out of the buffer's range (the
+  // sum stays below 2^32 because offsets within range are below 2^30); an
+  // out-of-range lane writes zeros into its LDS slot.
+  auto gload = [&](int stage, int k0) {
+    const uint32_t kadd = k0 * 2u + ((k0 + dl_chunk * 8) < a.K ? 0u : uint32_t(kOob));
+    char* s = smem + stage * STAGE + wave * 1024;
 #pragma unroll
-    for (int p = 0; p < A_CH; ++p)
-      ra_reg[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, kin ? a_off[p] + k0 * 2 : kOutOfRange, 0, 0);
+    for (int p = 0; p < A_DMA; ++p) dma16(ra, s + p * 4096, a_off[p] + kadd);
 #pragma unroll
-    for (int p = 0; p < B_CH; ++p)
-      rb_reg[p] = __builtin_amdgcn_raw_buffer_load_b128(rb, kin ? b_off[p] + k0 * 2 : kOutOfRange, 0, 0);
+    for (int p = 0; p < B_DMA; ++p) dma16(rb, s + BM * ROWB + p * 4096, b_off[p] + kadd);
   };
-  auto lstore = [&](int stage) {
-    char* s = smem + stage * STAGE;
+
+  // Fragment addressing: row r = base + 32 i (+ lane & 31); chunk 2 kk + fk,
+  // swizzled with r & 7 = lane & 7.
+  const int frow = lane & 31;
+  const int fk = lane >> 5;
+  const int fa_base = (wm * WTM + frow) * ROWB;
+  const int fb_base = BM * ROWB + (wn * WTN + frow) * ROWB;
+  const int frow_sw = (frow & 7) ^ ((frow >> 3) & 1);
+  int fsw[4];
 #pragma unroll
-    for (int p = 0; p < A_CH; ++p) *reinterpret_cast<u32x4*>(s + a_lds[p]) = ra_reg[p];
+  for (int kk = 0; kk < 4; ++kk) fsw[kk] = ((2 * kk + fk) ^ frow_sw) << 4;
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto fread = [&](int stage, int kk, int slot) {
+    const char* s = smem + stage * STAGE;
 #pragma unroll
-    for (int p = 0; p < B_CH; ++p) *reinterpret_cast<u32x4*>(s + b_lds[p]) = rb_reg[p];
+    for (int i = 0; i < FN; ++i)
+      fb[slot][i] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(s + fb_base + fsw[kk] + i * 32 * ROWB));
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      fa[slot][j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(s + fa_base + fsw[kk] + j * 32 * ROWB));
   };
 
   f32x16 acc[FN][FM];
@@ -196,46 +265,52 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
 
-  // Fragment rows read by this lane.
-  const int frow = lane & 31;
-  const int fk = lane >> 5;           // which 8-element half of a 16-wide k step
+  auto mfma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][i], fa[slot][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+
   const int KT = (a.K + BK - 1) / BK;
-
   if (KT > 0) {
-    gload(0);
-    lstore(0);
+    gload(0, 0);
+    gload(1, BK);
+    wait_vmcnt0();
+    __syncthreads();
+    fread(0, 0, 0);
   }
-  __syncthreads();
-
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const char* s = smem + cur * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + fk;
-      bf16x8 bf[FN], af[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int r = wn * WTN + i * 32 + frow;
-        bf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               s + BM * ROWB + r * ROWB + ((c ^ (r & 7)) << 4)));
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int r = wm * WTM + j * 32 + frow;
-        af[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               s + r * ROWB + ((c ^ (r & 7)) << 4)));
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[i], af[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(cur ^ 1);
+    // kk = 0
+    fread(cur, 1, 1);
+    mfma(0);
+    interleave<FM * FN, FM + FN, 0, 0>();
+    // kk = 1
+    fread(cur, 2, 0);
+    mfma(1);
+    interleave<FM * FN, FM + FN, 0, 0>();
+    // kk = 2
+    fread(cur, 3, 1);
+    mfma(0);
+    interleave<FM * FN, FM + FN, 0, 0>();
+    // Wait for this wave's global->LDS loads of the next tile (the compiler
+    // does not order them before the barrier by itself), then the barrier
+    // makes every wave's loads visible.
+    wait_vmcnt0();
     __syncthreads();
+    // kk = 3 (+ first fragments of the next tile, loads two tiles on into
+    // the buffer just finished with)
+    fread(cur ^ 1, 0, 0);
+    gload(cur, (kt + 2) * BK);
+    mfma(1);
+    interleave<FM * FN, FM + FN, 0, A_DMA + B_DMA>();
   }
+  // The last iterations issued loads past K (they land as zeros); drain them
+  // before the workgroup's LDS can be handed to another workgroup.
+  wait_vmcnt0();
 
   // Epilogue: block (i, j) holds C^T; lane owns row m, columns n..n+3 per quad.
   void* cbase = a.p.c[g];
@@ -252,6 +327,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
                    acc[i][j][4 * q + 3]};
         store_quad<TOut, EPI, GELU>(a, cbase, cin, m, n, v);
       }
+      // One block at a time: keeps the accumulate-mode loads from being
+      // hoisted all at once (register pressure).
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

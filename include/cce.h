@@ -31,7 +31,8 @@
  * Outputs must not overlap inputs or each other.
  *
  * Alignment: every device base pointer must be 16-byte aligned and every ld
- * and every contraction length K a multiple of 8 elements; otherwise the call
+ * and every contraction length K a multiple of 8 elements, and every GEMM
+ * operand (one rank's factor) must span less than 1 GiB; otherwise the call
  * returns CCE_EUNSUPPORTED.  Other extents (M, N, rows, cols) are arbitrary,
  * including ragged tile tails; a zero extent is a valid no-op.
  *
@@ -80,6 +81,8 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
 #define CCE_FLAG_GELU 0x2u    /* apply exact GELU, x*Phi(x), to each output
                                  element as it is stored (AllGather-Einsum and
                                  grouped GEMM only) */
+#define CCE_FLAG_COPY_DMA 0x4u /* run the permute copies on the DMA engines
+                                  (no compute units) instead of copy kernels */
 
 /* Status text; never NULL. */
 const char* cce_status_string(cce_status s);
@@ -94,6 +97,31 @@ const char* cce_version(void);
  * priority, non-blocking) and a pool of events.  *out receives the context. */
 cce_status cce_ctx_create(int device, cce_ctx** out);
 cce_status cce_ctx_destroy(cce_ctx* ctx);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing.  While profiling is enabled on a context, every GEMM launch,
+ * every permute step (the batch of copies of one iteration or half-step) and
+ * every epilogue launch it enqueues is bracketed by a pair of timing events
+ * on the stream that runs it.  cce_ctx_read_profile waits for those events,
+ * returns up to max_records records in enqueue order, and clears the list.
+ * Enabling (enable != 0) also clears it.  Host memory only; no allocation on
+ * the device.
+ *   kind: 0 GEMM launch, 1 permute step (copies), 2 fused epilogue launch
+ *   iter: loop iteration (GEMM, copies), -1 otherwise
+ *   ms:   event-to-event time on the device
+ *   flops: 2*M*N*K summed over the launch's groups (GEMM), else 0
+ *   bytes: bytes moved (copies: read + write), algorithmic bytes (epilogue)
+ * ---------------------------------------------------------------------- */
+typedef struct cce_prof_record {
+  int32_t kind;
+  int32_t iter;
+  float ms;
+  double flops;
+  double bytes;
+} cce_prof_record;
+
+cce_status cce_ctx_set_profiling(cce_ctx* ctx, int enable);
+cce_status cce_ctx_read_profile(cce_ctx* ctx, int max_records, cce_prof_record* out, int* n_out);
 
 /* ------------------------------------------------------------------------
  * Ring schedule ([OV] Section 5.1).
@@ -133,7 +161,8 @@ cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
  * in_t: CCE_BF16 (fp32 accumulation) or CCE_F32 (both inputs the same type).
  * out_t: CCE_BF16 or CCE_F32 (round to nearest even on the final store).
  * Case 2 accumulates across iterations in fp32 (in `out` itself when out_t is
- * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU.
+ * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU,
+ * CCE_FLAG_COPY_DMA.
  * workspace: device memory of at least the size the query returns (two
  * receive buffers per rank, plus the fp32 accumulators of case 2 with a bf16
  * output); its contents on entry do not matter.
@@ -176,6 +205,7 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
  * of out[s] the sum runs over the partials of ranks s-1, s-2, ..., s+1, s
  * (mod n) in that order, in fp32, whatever the flags.
  * in_t: CCE_BF16 or CCE_F32; acc_t: CCE_F32 only; out_t: CCE_F32 or CCE_BF16.
+ * flags: CCE_FLAG_SERIAL, CCE_FLAG_COPY_DMA.
  * workspace: two fp32 accumulators per rank (the query returns the size).
  * ---------------------------------------------------------------------- */
 typedef enum cce_rs_mode { CCE_RS_SLICE_LHS_ROWS = 0, CCE_RS_SLICE_RHS_COLS = 1 } cce_rs_mode;
