@@ -56,21 +56,24 @@ COMMON = [
 ]
 
 
-def compile_one(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def compile_one(src: str, extra=(), build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 4, verbose: bool = False, extra=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link `out`.  `extra` adds compiler flags
+    (e.g. the GEMM pipeline knobs -DCCE_GEMM_BK=.. -DCCE_GEMM_NS=..)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda src: compile_one(src, extra, build_dir), SOURCES))
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", out + ".tmp", *objs]
     tl = torch_lib_dir()
     if tl:
         link += [f"-L{tl}", f"-Wl,-rpath,{tl}"]
@@ -78,10 +81,10 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout}\n{r.stderr}")
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 def main(argv=None):

@@ -117,6 +117,7 @@ struct Op {
   int iter = 0;
   int half = 0;          // ReduceScatter half-step (0/1); 0 for AllGather
   int event = -1;        // record / wait
+  bool hint = false;     // wait that orders dispatch only (not needed for correctness)
   int epi = EPI_STORE;   // gemm epilogue
   bool final_store = false;   // gemm writes the caller's output dtype
   std::vector<Item> items;

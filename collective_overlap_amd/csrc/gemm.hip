@@ -46,7 +46,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
-constexpr int kOob = 0x40000000;           // added to steer a load past num_records
+constexpr int kOob = 0x40000000;
+
+// Pipeline shape of the bf16 kernel: k-tile depth and LDS stages (build-time
+// tuning knobs; 256x256 tiles need NS * (BM + BN) * BK * 2 <= 160 KB).
+#ifndef CCE_GEMM_BK
+#define CCE_GEMM_BK 64
+#endif
+#ifndef CCE_GEMM_NS
+#define CCE_GEMM_NS 2
+#endif
+constexpr int kBK = CCE_GEMM_BK;
+constexpr int kNS = CCE_GEMM_NS;           // added to steer a load past num_records
 constexpr int64_t kMaxRsrcBytes = kOob - 256;
 
 // Interleave groups of the scheduling region: for every MFMA one DS read,
@@ -101,10 +112,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voffset, 0, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
 // vmcnt[5:4] bits 15:14).
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ float gelu_exact(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
@@ -168,19 +183,35 @@ __device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, const fl
 // branches: loads past the end of K are steered out of range and land as
 // zeros, so the tail needs no special case.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, typename TOut, int EPI, bool GELU>
+// LDS swizzle of 16-byte chunks: physical chunk = logical ^ swz(row).  Rows
+// of 8 chunks (k tile 64): swz = (r & 7) ^ ((r >> 3) & 1).  Rows of 4 chunks
+// (k tile 32): swz = ((r >> 1) ^ (r >> 3)) & 3.  Either way the ds_read_b128
+// of 32 consecutive rows at one logical chunk hits every bank once per
+// 8-lane (32-bank) and per 16-lane (64-bank) service group.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, typename TOut, int EPI, bool GELU>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
-  constexpr int BK = 64;                     // 8 chunks of 8 bf16 per row
   constexpr int ROWB = BK * 2;               // bytes per LDS row
+  constexpr int CPR = BK / 8;                // 16-byte chunks per row
+  constexpr int KK = BK / 16;                // k16 steps per k tile
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_CH = BM * 8 / 256;         // 16-byte chunks per thread per stage
-  constexpr int B_CH = BN * 8 / 256;
   constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int RPI = 1024 / ROWB;           // rows per 1 KB load instruction
+  constexpr int A_DMA = BM / (4 * RPI);      // load instructions per wave per stage
+  constexpr int B_DMA = BN / (4 * RPI);
+  constexpr int N_DMA = A_DMA + B_DMA;
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  static_assert(KK % 2 == 0 && NS >= 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
   int g, tm, tn;
   map_tile(a, g, tm, tn);
@@ -199,56 +230,51 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<int64_t>(n0) * a.ldb, b_bytes);
 
   // Direct global->LDS staging (buffer_load ... lds): one instruction of a
-  // wave fills 1 KB of LDS = 8 consecutive rows of 128 B, lane L landing at
-  // byte 16 L, i.e. row L / 8, physical chunk L % 8.  The lane fetches the
-  // logical chunk that belongs there under the swizzle
-  //   physical = logical ^ f(row),  f(row) = (row & 7) ^ ((row >> 3) & 1),
-  // which makes the fragment reads below conflict-free for 8-lane (32-bank)
-  // and 16-lane (64-bank) LDS service groups alike.  For wave w and
-  // instruction p the rows are 8 (4 p + w) + L / 8, so the fetched logical
-  // chunk (L % 8) ^ (L / 8) ^ (w & 1) does not depend on p.
-  constexpr int A_DMA = BM * ROWB / (4 * 1024);   // instructions per wave per stage
-  constexpr int B_DMA = BN * ROWB / (4 * 1024);
-  const int dl_row = lane >> 3;
-  const int dl_chunk = (lane & 7) ^ dl_row ^ (wave & 1);
+  // wave fills 1 KB of LDS = RPI consecutive rows, lane L landing at byte
+  // 16 L, i.e. row L / CPR, physical chunk L % CPR.  The lane fetches the
+  // logical chunk that belongs there under the swizzle.  For wave w and
+  // instruction p the rows are RPI (4 p + w) + L / CPR, and the swizzle of
+  // those rows does not depend on p, so neither does the fetched chunk.
+  const int dl_row = lane / CPR;
+  const int dl_chunk = (lane % CPR) ^ swz<CPR>(RPI * wave + dl_row);
   uint32_t a_off[A_DMA], b_off[B_DMA];
 #pragma unroll
   for (int p = 0; p < A_DMA; ++p) {
-    const int r = 8 * (4 * p + wave) + dl_row;
+    const int r = RPI * (4 * p + wave) + dl_row;
     a_off[p] = (m0 + r < a.M) ? (r * a.lda + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
 #pragma unroll
   for (int p = 0; p < B_DMA; ++p) {
-    const int r = 8 * (4 * p + wave) + dl_row;
+    const int r = RPI * (4 * p + wave) + dl_row;
     b_off[p] = (n0 + r < a.N) ? (r * a.ldb + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
   // Rows past M / N start at kOob; chunks past K add kOob.  Operands are
   // smaller than kOob bytes, so either lands out of the buffer's range (the
   // sum stays below 2^32 because offsets within range are below 2^30); an
   // out-of-range lane writes zeros into its LDS slot.
-  auto gload = [&](int stage, int k0) {
+  auto gload = [&](int buf, int k0) {
     const uint32_t kadd = k0 * 2u + ((k0 + dl_chunk * 8) < a.K ? 0u : uint32_t(kOob));
-    char* s = smem + stage * STAGE + wave * 1024;
+    char* s = smem + buf * STAGE + wave * 1024;
 #pragma unroll
     for (int p = 0; p < A_DMA; ++p) dma16(ra, s + p * 4096, a_off[p] + kadd);
 #pragma unroll
     for (int p = 0; p < B_DMA; ++p) dma16(rb, s + BM * ROWB + p * 4096, b_off[p] + kadd);
   };
 
-  // Fragment addressing: row r = base + 32 i (+ lane & 31); chunk 2 kk + fk,
-  // swizzled with r & 7 = lane & 7.
+  // Fragment addressing: row r = base + 32 i + (lane & 31) with base a
+  // multiple of 32, so swz(r) = swz(lane & 31); chunk 2 kk + (lane >> 5).
   const int frow = lane & 31;
   const int fk = lane >> 5;
   const int fa_base = (wm * WTM + frow) * ROWB;
   const int fb_base = BM * ROWB + (wn * WTN + frow) * ROWB;
-  const int frow_sw = (frow & 7) ^ ((frow >> 3) & 1);
-  int fsw[4];
+  const int frow_sw = swz<CPR>(frow);
+  int fsw[KK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) fsw[kk] = ((2 * kk + fk) ^ frow_sw) << 4;
+  for (int kk = 0; kk < KK; ++kk) fsw[kk] = ((2 * kk + fk) ^ frow_sw) << 4;
 
   bf16x8 fa[2][FM], fb[2][FN];
-  auto fread = [&](int stage, int kk, int slot) {
-    const char* s = smem + stage * STAGE;
+  auto fread = [&](int buf, int kk, int slot) {
+    const char* s = smem + buf * STAGE;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
       fb[slot][i] = __builtin_bit_cast(
@@ -274,43 +300,46 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
                                                             0, 0, 0);
   };
 
+  // Pipeline: NS LDS buffers, one per k tile in flight.  Per k tile kt:
+  //   kk = 0..KK-2: MFMA(step kk) | LDS reads of step kk+1
+  //   wait for tile kt+1's loads (newer ones may stay in flight), barrier
+  //   kk = KK-1:    MFMA | LDS reads of step 0 of tile kt+1 | loads of tile
+  //                 kt+NS into tile kt's buffer
+  // Tile kt's buffer is free after the barrier: its last fragments (step
+  // KK-1) were read before it.  The barrier also makes every wave's loads of
+  // tile kt+1 visible before they are read.  The loop body has no branches:
+  // loads past the end of K are steered out of range and land as zeros, so
+  // the tail needs no special case.
   const int KT = (a.K + BK - 1) / BK;
   if (KT > 0) {
-    gload(0, 0);
-    gload(1, BK);
-    wait_vmcnt0();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) gload(st, st * BK);
+    wait_vmcnt<(NS - 1) * N_DMA>();
     __syncthreads();
     fread(0, 0, 0);
   }
+  int cur = 0;                  // buffer of tile kt
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    // kk = 0
-    fread(cur, 1, 1);
-    mfma(0);
-    interleave<FM * FN, FM + FN, 0, 0>();
-    // kk = 1
-    fread(cur, 2, 0);
-    mfma(1);
-    interleave<FM * FN, FM + FN, 0, 0>();
-    // kk = 2
-    fread(cur, 3, 1);
-    mfma(0);
-    interleave<FM * FN, FM + FN, 0, 0>();
-    // Wait for this wave's global->LDS loads of the next tile (the compiler
-    // does not order them before the barrier by itself), then the barrier
-    // makes every wave's loads visible.
-    wait_vmcnt0();
+    const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      fread(cur, kk + 1, (kk + 1) & 1);
+      mfma(kk & 1);
+      interleave<FM * FN, FM + FN, 0, 0>();
+    }
+    // The compiler does not order the global->LDS loads before the barrier
+    // by itself: wait for tile kt+1's (the NS-2 newer tiles may stay out).
+    wait_vmcnt<(NS - 2) * N_DMA>();
     __syncthreads();
-    // kk = 3 (+ first fragments of the next tile, loads two tiles on into
-    // the buffer just finished with)
-    fread(cur ^ 1, 0, 0);
-    gload(cur, (kt + 2) * BK);
+    fread(nxt, 0, 0);
+    gload(cur, (kt + NS) * BK);
     mfma(1);
-    interleave<FM * FN, FM + FN, 0, A_DMA + B_DMA>();
+    interleave<FM * FN, FM + FN, 0, N_DMA>();
+    cur = nxt;
   }
   // The last iterations issued loads past K (they land as zeros); drain them
   // before the workgroup's LDS can be handed to another workgroup.
-  wait_vmcnt0();
+  wait_vmcnt<0>();
 
   // Epilogue: block (i, j) holds C^T; lane owns row m, columns n..n+3 per quad.
   void* cbase = a.p.c[g];
@@ -405,13 +434,13 @@ hipError_t launch_typed(const GemmLaunch& L, KArgs& k, hipStream_t s) {
   };
   if (tiles(256, 256) >= kCUs) {
     const int t = grid_for(256, 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   } else if (tiles(256, 128) >= kCUs) {
     const int t = grid_for(256, 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 2, 2, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   } else {
     const int t = grid_for(128, 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   }
   return hipGetLastError();
 }

@@ -58,6 +58,12 @@ Op wait(StreamId s, int ev) {
   return o;
 }
 
+Op hint_wait(StreamId s, int ev) {
+  Op o = wait(s, ev);
+  o.hint = true;
+  return o;
+}
+
 }  // namespace
 
 Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
@@ -67,11 +73,12 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
   p.mode = mode;
   p.serial = serial;
   const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
-  // events: 0 fork, 2+i gemm_done[i], 2+n+i arrive[i]
-  p.n_events = 2 + 2 * n;
+  // events: 0 fork, 2+i gemm_done[i], 2+n+i arrive[i], 2+2n+i started[i]
+  p.n_events = 2 + 3 * n;
   const int EV_FORK = 0;
   auto ev_gemm = [&](int i) { return 2 + i; };
   auto ev_arrive = [&](int i) { return 2 + n + i; };
+  auto ev_started = [&](int i) { return 2 + 2 * n + i; };
   const StreamId cs = serial ? S_COMPUTE : S_COPY;
 
   auto held = [&](int r, int i) {
@@ -88,6 +95,10 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
       // WAR: the destination parity was last read by GEMM(i-1); GEMM(0)
       // reads the caller's shards, so the first two copies need no wait.
       if (!serial && i >= 2) p.ops.push_back(wait(S_COPY, ev_gemm(i - 1)));
+      // Mark that the copy stream reached this permute; GEMM(i) waits for
+      // the mark, so the copies are dispatched before the GEMM that runs
+      // beside them and are not starved of compute units by it.
+      if (!serial) p.ops.push_back(rec(S_COPY, ev_started(i)));
       Op c;
       c.kind = OP_COPY;
       c.stream = cs;
@@ -105,6 +116,7 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
     }
     // Done of the permute that brought this iteration's shard, then the GEMM.
     if (!serial && i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i)));
+    if (!serial && i + 1 < n) p.ops.push_back(hint_wait(S_COMPUTE, ev_started(i)));
     Op g;
     g.kind = OP_GEMM;
     g.stream = S_COMPUTE;
@@ -150,11 +162,17 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
   p.mode = mode;
   p.serial = serial;
   const int H = two_halves ? 2 : 1;
-  // events: 2+(2i+h) gemm_done, 2+2n+(2i+h) arrive
-  p.n_events = 2 + 4 * n;
+  // events: 2+(2i+h) gemm_done, 2+2n+(2i+h) arrive, 2+4n+(2i+h) started
+  p.n_events = 2 + 6 * n;
   auto ev_gemm = [&](int i, int h) { return 2 + 2 * i + h; };
   auto ev_arrive = [&](int i, int h) { return 2 + 2 * n + 2 * i + h; };
+  auto ev_started = [&](int i, int h) { return 2 + 4 * n + 2 * i + h; };
   const StreamId cs = serial ? S_COMPUTE : S_COPY;
+  // The GEMM that runs beside half-copy (i, h) is the next half-step's.
+  auto prev_copy = [&](int i, int h, int* pi, int* ph) {
+    if (h == 1) { *pi = i; *ph = 0; } else { *pi = i - 1; *ph = H - 1; }
+    return *pi >= 0 && *pi + 1 < n;
+  };
 
   // No fork is needed either: the first copy waits for GEMM(0, 0), which is
   // ordered after the caller's earlier work on `stream`.
@@ -162,6 +180,8 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
     const bool last = (i == n - 1);
     for (int h = 0; h < H; ++h) {
       if (!serial && i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i, h)));
+      int pi, ph;
+      if (!serial && prev_copy(i, h, &pi, &ph)) p.ops.push_back(hint_wait(S_COMPUTE, ev_started(pi, ph)));
       Op g;
       g.kind = OP_GEMM;
       g.stream = S_COMPUTE;
@@ -188,6 +208,7 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
         if (!serial) {
           p.ops.push_back(rec(S_COMPUTE, ev_gemm(i, h)));
           p.ops.push_back(wait(S_COPY, ev_gemm(i, h)));
+          p.ops.push_back(rec(S_COPY, ev_started(i, h)));
         }
         Op c;
         c.kind = OP_COPY;
@@ -243,7 +264,7 @@ std::string describe_plan(const Plan& p) {
         out += line;
         break;
       case OP_WAIT:
-        std::snprintf(line, sizeof line, "wait ev=%d\n", o.event);
+        std::snprintf(line, sizeof line, "wait ev=%d%s\n", o.event, o.hint ? " hint=1" : "");
         out += line;
         break;
       case OP_GEMM:

@@ -55,8 +55,10 @@ def _with_caller(ops: list[POp]) -> list[POp]:
     return [start] + body + [end]
 
 
-def happens_before(ops: list[POp]):
-    """Return (succ adjacency, problems) for the HB graph."""
+def happens_before(ops: list[POp], hints: bool = True):
+    """Return (succ adjacency, problems) for the HB graph.  Waits marked
+    hint=1 only order dispatch; with hints=False they are left out, so a plan
+    must be race-free without them."""
     n = len(ops)
     succ = [set() for _ in range(n)]
     problems = []
@@ -70,6 +72,8 @@ def happens_before(ops: list[POp]):
         if o.kind == "record":
             last_record[o.attrs["ev"]] = o.idx
         elif o.kind == "wait":
+            if not hints and o.attrs.get("hint") == "1":
+                continue
             r = last_record.get(o.attrs["ev"])
             if r is None:
                 problems.append(f"op {o.idx}: wait on ev={o.attrs['ev']} before any record")
@@ -97,7 +101,7 @@ def _reach(succ):
 def check(text: str) -> list[str]:
     """List of problems (empty when the plan is race-free)."""
     ops = _with_caller(parse(text))
-    succ, problems = happens_before(ops)
+    succ, problems = happens_before(ops, hints=False)
     reach = _reach(succ)
     acc = [o for o in ops if o.kind in ("gemm", "copy", "caller")]
     for i, x in enumerate(acc):

@@ -145,14 +145,23 @@ def test_serial_plan_has_no_copy_stream():
 
 @pytest.mark.parametrize("kind,mode", [(0, 0), (0, 2), (1, 0), (1, 1)])
 def test_checker_flags_every_dropped_wait(kind, mode):
-    """Each wait of the overlapped plan is necessary: removing any single one
-    (a mistake planted in the description, on the CPU) is flagged."""
+    """Each ordering wait of the overlapped plan is necessary: removing any
+    single one (a mistake planted in the description, on the CPU) is flagged.
+    Waits marked hint=1 only order dispatch (a GEMM waits until the permute
+    beside it has started) and are exempt."""
     lines = _plan(kind, 4, mode, 1).strip().splitlines()
-    waits = [i for i, l in enumerate(lines) if " wait " in l]
+    waits = [i for i, l in enumerate(lines) if " wait " in l and "hint=1" not in l]
     assert waits
     for w in waits:
         broken = "\n".join(l for i, l in enumerate(lines) if i != w)
         assert plan_check.check(broken), f"dropping line {w} went unnoticed"
+
+
+@pytest.mark.parametrize("kind,mode,n,expect", [(0, 1, 4, 3), (1, 0, 4, 6), (0, 1, 1, 0)])
+def test_gemms_wait_for_the_permute_beside_them_to_start(kind, mode, n, expect):
+    hints = [l for l in _plan(kind, n, mode, 1).splitlines() if "hint=1" in l]
+    assert len(hints) == expect
+    assert all(l.startswith("compute wait") for l in hints)
 
 
 def test_checker_flags_wait_before_record():
