@@ -10,6 +10,13 @@ Einsum-ReduceScatter out of the W2 shards with an fp32 travelling
 accumulator, and the fused bias + dropout + residual epilogue on every rank's
 shard.  All 8 logical ranks are separate HBM buffers on the one GPU.
 
+The timed step uses the fused permute by default (each partial GEMM sends
+the data itself: the AllGather forwards the shard it stages through LDS, the
+ReduceScatter's accumulate epilogue stores into the next rank's
+accumulator); --permute stream times the form with async copies on a second
+stream instead.  Both, and the same kernels serialised on one stream, are
+reported.
+
 Prints one JSON line: whole-step bf16 TFLOP/s (value), the dominant kernel's
 roofline, the epilogue's HBM rate, the looped-vs-serial comparison with the
 hidden copy fraction, and the CPU oracle timed on a bounded sample (rank 0,
@@ -338,6 +345,12 @@ def main(argv=None):
     ap.add_argument("--workload", default="gpt3_ffn_n8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true", help="skip the unoverlapped comparison")
+    ap.add_argument("--permute", choices=("fused", "stream"), default="fused",
+                    help="fused: each partial GEMM sends the data itself; stream: async "
+                         "copies on a second stream ordered by events")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run `steps` plain device copies of MiB mebibytes (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -351,16 +364,29 @@ def main(argv=None):
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = "cuda:0"
+    if a.calibrate_copy:
+        nb = a.calibrate_copy * 2**20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / a.steps
+        print(json.dumps({"calibrate_copy_bytes": nb, "read_bytes": nb, "write_bytes": nb,
+                          "steps": a.steps, "GB/s": round(2 * nb / dt / 1e9, 1)}), flush=True)
+        return 0
     log(f"device {torch.cuda.get_device_name(0)}; workload {a.workload}")
     step = WORKLOADS[a.workload](dev)
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     log("inputs ready; warmup")
+    main_flags = cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0
     for _ in range(a.warmup):
-        step.run(ctx, 0)
-    torch.cuda.synchronize()
-    log("timed region (overlapped)")
-    wall, recs = timed(step, ctx, a.steps, 0, profile=True)
+        step.run(ctx, main_flags)
+    log(f"timed region (permute {a.permute})")
+    wall, recs = timed(step, ctx, a.steps, main_flags, profile=True)
     ms_per_step = wall / a.steps * 1e3
     value = step.flops * a.steps / wall / 1e12
     roof, per_shape = gemm_roofline(recs, step.dtype, a.steps)
@@ -375,23 +401,37 @@ def main(argv=None):
                     "launches": len(epi), "avg_launch_ms": round(tm / len(epi), 4),
                     "bytes_per_launch": tb / len(epi)}
     gemm_ms = sum(r["ms"] for r in recs if r["kind"] == "gemm") / a.steps
-    copy_recs = [r for r in recs if r["kind"] == "copy"]
 
     overlap = None
-    if not a.no_serial and copy_recs:
-        log("timed region (serial: same kernels, copies on the compute stream)")
-        for _ in range(max(1, a.warmup // 2)):
-            step.run(ctx, cce.CCE_FLAG_SERIAL)
-        swall, srecs = timed(step, ctx, a.steps, cce.CCE_FLAG_SERIAL, profile=True)
-        s_ms = swall / a.steps * 1e3
+    has_permute = a.workload not in ("attn_outproj_n8",)
+    if not a.no_serial and has_permute:
+        log("timed regions: copies on a second stream; the same kernels serialised")
+        res = {}
+        for name, fl in (("stream", 0), ("serial", cce.CCE_FLAG_SERIAL)):
+            for _ in range(max(1, a.warmup // 2)):
+                step.run(ctx, fl)
+            w, r = timed(step, ctx, a.steps, fl, profile=True)
+            res[name] = (w / a.steps * 1e3, r)
+        fused_ms = ms_per_step if a.permute == "fused" else None
+        if fused_ms is None:
+            for _ in range(max(1, a.warmup // 2)):
+                step.run(ctx, cce.CCE_FLAG_FUSED_PERMUTE)
+            w, _ = timed(step, ctx, a.steps, cce.CCE_FLAG_FUSED_PERMUTE, profile=False)
+            fused_ms = w / a.steps * 1e3
+        s_ms, srecs = res["serial"]
+        st_ms = res["stream"][0]
         copy_ms = sum(r["ms"] for r in srecs if r["kind"] == "copy") / a.steps
         copy_bytes = sum(r["bytes"] for r in srecs if r["kind"] == "copy") / a.steps
-        hidden = 1.0 - (ms_per_step - (s_ms - copy_ms)) / copy_ms if copy_ms > 0 else 1.0
-        overlap = {"overlapped_ms": round(ms_per_step, 3), "serial_ms": round(s_ms, 3),
-                   "speedup_vs_serial": round(s_ms / ms_per_step, 4),
-                   "copy_ms_serial": round(copy_ms, 3),
+        base = s_ms - copy_ms            # the same GEMMs and epilogues without the copies
+
+        def hidden(t):
+            return round(min(1.0, max(0.0, 1.0 - (t - base) / copy_ms)), 4) if copy_ms > 0 else None
+        overlap = {"serial_ms": round(s_ms, 3), "stream_ms": round(st_ms, 3),
+                   "fused_ms": round(fused_ms, 3), "copy_ms_serial": round(copy_ms, 3),
                    "copy_GB/s_serial": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
-                   "hidden_copy_frac": round(min(1.0, max(0.0, hidden)), 4)}
+                   "hidden_copy_frac_stream": hidden(st_ms),
+                   "hidden_copy_frac_fused": hidden(fused_ms),
+                   "speedup_vs_serial": round(s_ms / ms_per_step, 4)}
 
     cpu = None
     parity = None
@@ -422,7 +462,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": step.dtype,
         "data": "synthetic (seeded torch generators; no dataset)",
-        "config": step.config(),
+        "config": dict(step.config(), permute=a.permute),
         "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -16,7 +16,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_COPY_DMA, CCE_FLAG_GELU, CCE_FLAG_SERIAL,
+from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
+                   CCE_FLAG_SERIAL,
                    AG_MODES, RS_MODES,
                    cce_mat, check, lib, ptr_array)
 
@@ -25,7 +26,8 @@ __all__ = [
     "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
     "cce_looped_einsum_reducescatter_workspace", "cce_grouped_gemm",
     "cce_fused_reduce_epilogue", "cce_describe_plan", "cce_version",
-    "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "AG_MODES", "RS_MODES",
+    "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
+    "AG_MODES", "RS_MODES",
 ]
 
 _DT = {torch.float32: CCE_F32, torch.bfloat16: CCE_BF16}

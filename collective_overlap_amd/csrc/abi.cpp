@@ -248,11 +248,13 @@ struct RsGeom {
   int64_t shard = 0;              // m_s (rows) or n_s (cols)
   int64_t other = 0;              // N (cols) or M (rows)
   int64_t h0 = 0, h1 = 0;         // half extents along the sliced dim
+  int H = 2;                      // accumulator chains (halves) per shard
   int64_t acc_ld = 0, half_bytes = 0;
-  int64_t total = 0;
+  int64_t total = 0;              // enough for every flag combination
 };
 
-cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsGeom& g) {
+cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsGeom& g,
+                       bool fused = false) {
   if (n < 1 || n > CCE_MAX_RANKS)
     return fail(n < 1 ? CCE_EINVAL : CCE_EUNSUPPORTED, "n_ranks out of range: " + std::to_string(n));
   if (mode != CCE_RS_SLICE_LHS_ROWS && mode != CCE_RS_SLICE_RHS_COLS)
@@ -262,23 +264,45 @@ cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsG
   CCE_TRY(check_mat("out_shard", out));
   g.n = n;
   g.mode = mode;
-  if (mode == CCE_RS_SLICE_LHS_ROWS) {
-    g.shard = out.rows;
-    g.other = out.cols;
-    g.h0 = (g.shard + 1) / 2;
-    g.h1 = g.shard - g.h0;
-    g.acc_ld = round8(g.other);
-    g.half_bytes = align256(g.h0 * g.acc_ld * 4);
+  const bool rows = (mode == CCE_RS_SLICE_LHS_ROWS);
+  g.shard = rows ? out.rows : out.cols;
+  g.other = rows ? out.cols : out.rows;
+  // The split of a shard into two chains: rows split at ceil(m/2); columns
+  // split at a multiple of 8 so that the second half stays 16-byte aligned.
+  auto split = [&](int64_t* h0, int64_t* h1) {
+    if (rows) {
+      *h0 = (g.shard + 1) / 2;
+    } else {
+      *h0 = round8((g.shard + 1) / 2);
+      if (*h0 >= g.shard) *h0 = g.shard;
+    }
+    *h1 = g.shard - *h0;
+  };
+  auto layout = [&](int64_t h0, int64_t* ld, int64_t* slot) {
+    *ld = rows ? round8(g.other) : round8(h0);
+    *slot = rows ? align256(h0 * *ld * 4) : align256(g.other * *ld * 4);
+  };
+  // Two chains of half shards (copies beside the GEMMs), or one chain of
+  // whole shards (permute fused into the GEMM epilogue).
+  int64_t s0, s1, ld2, slot2, ld1, slot1;
+  split(&s0, &s1);
+  layout(s0, &ld2, &slot2);
+  layout(g.shard, &ld1, &slot1);
+  const int64_t total2 = 2LL * n * 2 * slot2, total1 = 2LL * n * slot1;
+  g.total = (n > 1) ? std::max(total1, total2) : 0;
+  if (fused) {
+    g.h0 = g.shard;
+    g.h1 = 0;
+    g.H = 1;
+    g.acc_ld = ld1;
+    g.half_bytes = slot1;
   } else {
-    g.shard = out.cols;
-    g.other = out.rows;
-    g.h0 = round8((g.shard + 1) / 2);
-    if (g.h0 >= g.shard) g.h0 = g.shard;
-    g.h1 = g.shard - g.h0;
-    g.acc_ld = round8(g.h0);
-    g.half_bytes = align256(g.other * g.acc_ld * 4);
+    g.h0 = s0;
+    g.h1 = s1;
+    g.H = 2;
+    g.acc_ld = ld2;
+    g.half_bytes = slot2;
   }
-  g.total = (n > 1) ? 2LL * n * 2 * g.half_bytes : 0;
   return CCE_OK;
 }
 
@@ -411,6 +435,14 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
           break;
       }
       L.p.c[r] = cptr;
+      if (it.has_fwd) {
+        const PtrLd f = ag_resolve(c, it.fwd);
+        L.fwd = (c.g.mode == CCE_AG_LHS_ROWS || c.g.mode == CCE_AG_LHS_COLS) ? FWD_A : FWD_B;
+        L.p.fwd[r] = f.p;
+        L.ldfwd = f.ld;
+      } else {
+        L.p.fwd[r] = nullptr;
+      }
       if (it.has_cin) {
         const PtrLd cin = ag_resolve(c, it.cin);
         L.p.cin[r] = reinterpret_cast<const float*>(cin.p);
@@ -453,7 +485,7 @@ PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
       return {p, c.oshape.ld};
     }
     case B_ACC:
-      return {c.ws + ((static_cast<int64_t>(b.parity) * c.g.n + r) * 2 + b.half) * c.g.half_bytes,
+      return {c.ws + ((static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.H + b.half) * c.g.half_bytes,
               c.g.acc_ld};
   }
   return {nullptr, 0};
@@ -650,7 +682,7 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
                                        cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA))
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
     return fail(CCE_EINVAL, "unknown flags");
   if (!looped || !local || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   AgGeom g;
@@ -681,7 +713,8 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
 
   DeviceGuard guard(ctx->device);
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
-  const Plan plan = build_allgather_plan(n_ranks, mode, g.case2_ws, serial);
+  const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
+  const Plan plan = build_allgather_plan(n_ranks, mode, g.case2_ws, serial, fused);
   CCE_TRY(ensure_events(ctx, plan.n_events));
   AgCall c{g, in_t, out_t, looped, looped_shard, local, local_shape, out, out_shape,
            static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0, copy_kind(flags)};
@@ -707,12 +740,13 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
                                            cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA))
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
     return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
+  const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
   if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   RsGeom g;
-  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g));
+  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g, fused));
   CCE_TRY(check_mat("a_shape", a_shape));
   CCE_TRY(check_mat("b_shape", b_shape));
   const int64_t nn = n_ranks;
@@ -752,7 +786,7 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
 
   DeviceGuard guard(ctx->device);
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
-  const Plan plan = build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial);
+  const Plan plan = build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
   CCE_TRY(ensure_events(ctx, plan.n_events));
   RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
            copy_kind(flags)};
@@ -913,16 +947,19 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
   clear_error();
   if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
   if (!dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU)) return fail(CCE_EINVAL, "unknown flags");
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
+    return fail(CCE_EINVAL, "unknown flags");
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
+  const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
   Plan p;
   if (kind == 0) {
     if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
     const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
-    p = build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1, serial);
+    p = build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1, serial,
+                             fused);
   } else if (kind == 1) {
     if (mode != 0 && mode != 1) return fail(CCE_EINVAL, "bad ReduceScatter mode");
-    p = build_reducescatter_plan(n_ranks, mode, true, serial);
+    p = build_reducescatter_plan(n_ranks, mode, true, serial, fused);
   } else {
     return fail(CCE_EINVAL, "kind must be 0 or 1");
   }

@@ -33,7 +33,11 @@ struct GemmGroupPtrs {
   const void* b[kMaxGroups];
   void* c[kMaxGroups];
   const float* cin[kMaxGroups];
+  void* fwd[kMaxGroups];      // forward destination of the looped operand
 };
+
+// Operand a fused-permute GEMM forwards (writes once, as it stages it).
+enum Fwd : int { FWD_NONE = 0, FWD_A = 1, FWD_B = 2 };
 
 struct GemmLaunch {
   int groups = 0;
@@ -43,6 +47,8 @@ struct GemmLaunch {
   cce_dtype out_t = CCE_BF16;
   int epi = EPI_STORE;
   bool gelu = false;
+  int fwd = FWD_NONE;          // forward A or B of every group to p.fwd[g]
+  int64_t ldfwd = 0;
   GemmGroupPtrs p{};
 };
 
@@ -105,7 +111,9 @@ struct Item {            // one rank's share of a GEMM or copy
   int shard = 0;         // shard / slice ID worked on
   BufRef a, b, cin, c;   // gemm: reads a, b (and cin if has_cin), writes c
                          // copy: reads a, writes c
+  BufRef fwd;            // gemm with a fused permute: writes the looped operand here
   bool has_cin = false;
+  bool has_fwd = false;
 };
 
 enum OpKind : uint8_t { OP_GEMM = 0, OP_COPY = 1, OP_RECORD = 2, OP_WAIT = 3 };
@@ -129,6 +137,7 @@ struct Plan {
   int mode = 0;
   int n_events = 0;
   bool serial = false;
+  bool fused = false;    // permutes fused into the GEMMs (no copy ops)
   std::vector<Op> ops;
 };
 
@@ -139,8 +148,8 @@ inline int rs_slice(int n, int r, int i) { return (r + i + 1) % n; }
 // Build the plan of a looped call.  `case2_ws` selects the workspace fp32
 // accumulator for AllGather case 2 (bf16 output); `two_halves` is false when
 // the ReduceScatter shard has a single row/column (no second chain).
-Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial);
-Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial);
+Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial, bool fused = false);
+Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial, bool fused = false);
 
 std::string describe_plan(const Plan& p);
 

@@ -81,6 +81,7 @@ struct KArgs {
   int M, N, K;
   int lda, ldb, ldc, ldcin;   // elements
   int tiles_m, tiles_n, tiles_per_group, total_tiles;
+  int fwd, ldfwd;             // fused permute: operand to forward, its destination ld
   GemmGroupPtrs p;
 };
 
@@ -285,6 +286,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
           bf16x8, *reinterpret_cast<const u32x4*>(s + fa_base + fsw[kk] + j * 32 * ROWB));
   };
 
+  // Fused permute: the looped operand (A or B) is written once to the next
+  // rank's receive buffer while it sits in LDS.  k tile kt of a row block is
+  // written by the one workgroup of that block whose other tile index equals
+  // kt modulo the number of such workgroups, which spreads the stores evenly.
+  const bool fwd_a = a.fwd == FWD_A, fwd_b = a.fwd == FWD_B;
+  __bf16* fdst = reinterpret_cast<__bf16*>(a.p.fwd[g]);
+  auto forward = [&](int buf, int kt) {
+    const int mine = fwd_a ? tn : tm;
+    const int span = fwd_a ? a.tiles_n : a.tiles_m;
+    if (!(fwd_a || fwd_b) || kt % span != mine) return;
+    const char* s = smem + buf * STAGE + (fwd_a ? 0 : BM * ROWB);
+    const int row0 = fwd_a ? m0 : n0;
+    const int rows = fwd_a ? BM : BN;
+    const int lim = fwd_a ? a.M : a.N;
+    constexpr int RP = 256 / CPR;                // rows per pass
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int k = kt * BK + c * 8;
+    if (k >= a.K) return;
+    for (int r = r0; r < rows; r += RP) {
+      if (row0 + r >= lim) break;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(s + r * ROWB + ((c ^ swz<CPR>(r)) << 4));
+      *reinterpret_cast<u32x4*>(fdst + static_cast<int64_t>(row0 + r) * a.ldfwd + k) = v;
+    }
+  };
+
   f32x16 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -316,6 +342,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     for (int st = 0; st < NS; ++st) gload(st, st * BK);
     wait_vmcnt<(NS - 1) * N_DMA>();
     __syncthreads();
+    forward(0, 0);
     fread(0, 0, 0);
   }
   int cur = 0;                  // buffer of tile kt
@@ -329,8 +356,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     }
     // The compiler does not order the global->LDS loads before the barrier
     // by itself: wait for tile kt+1's (the NS-2 newer tiles may stay out).
-    wait_vmcnt<(NS - 2) * N_DMA>();
+    // (With NS > 2 the forward stores would upset this count: wait for all.)
+    if (NS > 2 && (fwd_a || fwd_b)) wait_vmcnt<0>();
+    else wait_vmcnt<(NS - 2) * N_DMA>();
     __syncthreads();
+    if (kt + 1 < KT) forward(nxt, kt + 1);
     fread(nxt, 0, 0);
     gload(cur, (kt + NS) * BK);
     mfma(1);
@@ -390,6 +420,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
       f32x4 w = f32x4{};
       if (n < a.N && k < a.K) w = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(n) * a.ldb + k);
       for (int e = 0; e < 4; ++e) sb[lr * LDK + lc + e] = w[e];
+      // fused permute: forward the looped operand's k tile (once per row block)
+      const int kt = k0 / BK;
+      float* fd = reinterpret_cast<float*>(a.p.fwd[g]);
+      if (a.fwd == FWD_A && kt % a.tiles_n == tn && m < a.M && k < a.K)
+        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(m) * a.ldfwd + k) = v;
+      if (a.fwd == FWD_B && kt % a.tiles_m == tm && n < a.N && k < a.K)
+        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(n) * a.ldfwd + k) = w;
     }
     __syncthreads();
 #pragma unroll
@@ -467,6 +504,8 @@ cce_status launch_grouped_gemm(const GemmLaunch& L, void* stream) {
   k.ldb = static_cast<int>(L.ldb);
   k.ldc = static_cast<int>(L.ldc);
   k.ldcin = static_cast<int>(L.ldcin);
+  k.fwd = L.fwd;
+  k.ldfwd = static_cast<int>(L.ldfwd);
   k.p = L.p;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (L.out_t == CCE_F32) ? launch_out<float>(L, k, s) : launch_out<__bf16>(L, k, s);

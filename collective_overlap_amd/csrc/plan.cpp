@@ -66,12 +66,14 @@ Op hint_wait(StreamId s, int ev) {
 
 }  // namespace
 
-Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
+Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial, bool fused) {
   Plan p;
   p.kind = 0;
   p.n = n;
   p.mode = mode;
-  p.serial = serial;
+  p.serial = serial || fused;
+  p.fused = fused;
+  serial = p.serial;
   const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
   // events: 0 fork, 2+i gemm_done[i], 2+n+i arrive[i], 2+2n+i started[i]
   p.n_events = 2 + 3 * n;
@@ -90,8 +92,9 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
     p.ops.push_back(wait(S_COPY, EV_FORK));
   }
   for (int i = 0; i < n; ++i) {
-    // Start of the permute that brings the shard of iteration i+1.
-    if (i + 1 < n) {
+    // Start of the permute that brings the shard of iteration i+1 (in the
+    // fused form the GEMM of iteration i forwards its shard itself).
+    if (i + 1 < n && !fused) {
       // WAR: the destination parity was last read by GEMM(i-1); GEMM(0)
       // reads the caller's shards, so the first two copies need no wait.
       if (!serial && i >= 2) p.ops.push_back(wait(S_COPY, ev_gemm(i - 1)));
@@ -135,6 +138,10 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
       it.shard = ag_shard(n, r, i);
       it.a = held(r, i);
       it.b = ref(B_LOCAL, r);
+      if (fused && i + 1 < n) {
+        it.fwd = ref(B_RECV, (r - 1 + n) % n, (i + 1) % 2);
+        it.has_fwd = true;
+      }
       const BufRef acc = case2_ws ? ref(B_CASE2, r) : ref(B_OUT, r);
       if (!case2) {
         it.c = ref(B_OUT, r);
@@ -155,13 +162,17 @@ Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial) {
   return p;
 }
 
-Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
+Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial, bool fused) {
   Plan p;
   p.kind = 1;
   p.n = n;
   p.mode = mode;
-  p.serial = serial;
-  const int H = two_halves ? 2 : 1;
+  p.serial = serial || fused;
+  p.fused = fused;
+  serial = p.serial;
+  // Fused: the accumulate epilogue stores into the next rank's accumulator,
+  // so there is no copy to overlap and no need for two chains.
+  const int H = (two_halves && !fused) ? 2 : 1;
   // events: 2+(2i+h) gemm_done, 2+2n+(2i+h) arrive, 2+4n+(2i+h) started
   p.n_events = 2 + 6 * n;
   auto ev_gemm = [&](int i, int h) { return 2 + 2 * i + h; };
@@ -196,7 +207,9 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
         it.a = ref(B_A, r);
         it.b = ref(B_B, r);
         const BufRef acc = ref(B_ACC, r, i % 2, h);
-        it.c = last ? ref(B_OUT, r, 0, h) : acc;
+        // fused: send the new accumulator straight to rank r - 1
+        const BufRef dst = fused ? ref(B_ACC, (r - 1 + n) % n, (i + 1) % 2, h) : acc;
+        it.c = last ? ref(B_OUT, r, 0, h) : dst;
         if (i > 0) {
           it.cin = acc;   // the accumulator received from rank r + 1
           it.has_cin = true;
@@ -204,7 +217,7 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial) {
         g.items.push_back(it);
       }
       p.ops.push_back(g);
-      if (!last) {
+      if (!last && !fused) {
         if (!serial) {
           p.ops.push_back(rec(S_COMPUTE, ev_gemm(i, h)));
           p.ops.push_back(wait(S_COPY, ev_gemm(i, h)));
@@ -273,18 +286,24 @@ std::string describe_plan(const Plan& p) {
                       o.kind == OP_GEMM ? "gemm" : "copy", o.iter, o.half, o.epi,
                       o.final_store ? 1 : 0);
         out += line;
-        std::string rd, wr, sh;
+        std::string rd, wr, sh, xs;
         for (const Item& it : o.items) {
+          std::string ir = bufname(it.a), iw = bufname(it.c);
+          if (o.kind == OP_GEMM) ir += "+" + bufname(it.b);
+          if (it.has_cin) ir += "+" + bufname(it.cin);
+          if (it.has_fwd) iw += "+" + bufname(it.fwd);
           if (!rd.empty()) rd += ",";
-          rd += bufname(it.a);
-          if (o.kind == OP_GEMM) rd += "," + bufname(it.b);
-          if (it.has_cin) rd += "," + bufname(it.cin);
+          rd += ir;
           if (!wr.empty()) wr += ",";
-          wr += bufname(it.c);
+          wr += iw;
+          if (!xs.empty()) xs += ",";
+          xs += ir + ">" + iw;
           if (!sh.empty()) sh += ",";
           sh += std::to_string(it.rank) + ":" + std::to_string(it.shard);
         }
-        out += " r=" + rd + " w=" + wr + " shard=" + sh + "\n";
+        for (char& ch : rd) if (ch == '+') ch = ',';
+        for (char& ch : wr) if (ch == '+') ch = ',';
+        out += " r=" + rd + " w=" + wr + " x=" + xs + " shard=" + sh + "\n";
         break;
       }
     }

@@ -83,6 +83,13 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
                                  grouped GEMM only) */
 #define CCE_FLAG_COPY_DMA 0x4u /* run the permute copies on the DMA engines
                                   (no compute units) instead of copy kernels */
+#define CCE_FLAG_FUSED_PERMUTE 0x8u /* no copy stream: each partial GEMM sends
+                                  the data itself.  AllGather: the GEMM writes
+                                  the looped shard it stages through LDS to the
+                                  next rank's receive buffer (each k tile once);
+                                  ReduceScatter: the GEMM's accumulate epilogue
+                                  stores into the next rank's accumulator.  Same
+                                  results, bit for bit; no extra reads. */
 
 /* Status text; never NULL. */
 const char* cce_status_string(cce_status s);
@@ -162,7 +169,7 @@ cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
  * out_t: CCE_BF16 or CCE_F32 (round to nearest even on the final store).
  * Case 2 accumulates across iterations in fp32 (in `out` itself when out_t is
  * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU,
- * CCE_FLAG_COPY_DMA.
+ * CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE.
  * workspace: device memory of at least the size the query returns (two
  * receive buffers per rank, plus the fp32 accumulators of case 2 with a bf16
  * output); its contents on entry do not matter.
@@ -205,8 +212,9 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
  * of out[s] the sum runs over the partials of ranks s-1, s-2, ..., s+1, s
  * (mod n) in that order, in fp32, whatever the flags.
  * in_t: CCE_BF16 or CCE_F32; acc_t: CCE_F32 only; out_t: CCE_F32 or CCE_BF16.
- * flags: CCE_FLAG_SERIAL, CCE_FLAG_COPY_DMA.
- * workspace: two fp32 accumulators per rank (the query returns the size).
+ * flags: CCE_FLAG_SERIAL, CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE.
+ * workspace: two fp32 accumulators per rank (the query returns the size,
+ * which covers every flag combination).
  * ---------------------------------------------------------------------- */
 typedef enum cce_rs_mode { CCE_RS_SLICE_LHS_ROWS = 0, CCE_RS_SLICE_RHS_COLS = 1 } cce_rs_mode;
 

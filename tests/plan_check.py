@@ -26,6 +26,7 @@ class POp:
     attrs: dict = field(default_factory=dict)
     reads: set = field(default_factory=set)
     writes: set = field(default_factory=set)
+    items: list = field(default_factory=list)   # per rank: (reads, writes)
 
 
 def parse(text: str) -> list[POp]:
@@ -41,6 +42,8 @@ def parse(text: str) -> list[POp]:
         if kind in ("gemm", "copy"):
             op.reads = set(attrs["r"].split(","))
             op.writes = set(attrs["w"].split(","))
+            op.items = [(set(x.split(">")[0].split("+")), set(x.split(">")[1].split("+")))
+                        for x in attrs.get("x", "").split(",") if x]
         ops.append(op)
     return ops
 
@@ -98,10 +101,30 @@ def _reach(succ):
     return reach
 
 
+def intra_op_conflicts(op: POp) -> list[str]:
+    """The items of one operation run concurrently (one kernel, or one
+    batch of copies): no item may write what another item touches, and an
+    item may overlap its own reads only by updating a buffer in place
+    (its accumulator input is its output)."""
+    out = []
+    for i, (ri, wi) in enumerate(op.items):
+        for j, (rj, wj) in enumerate(op.items):
+            if i != j and wi & (rj | wj):
+                out.append(f"op {op.idx}: item {i} writes {sorted(wi & (rj | wj))} used by item {j}")
+        own = wi & ri
+        if own and not (op.kind == "gemm" and len(own) == 1 and len(ri) == 3):
+            out.append(f"op {op.idx}: item {i} reads and writes {sorted(own)}")
+    return out
+
+
 def check(text: str) -> list[str]:
     """List of problems (empty when the plan is race-free)."""
+    problems = []
+    for op in parse(text):
+        problems += intra_op_conflicts(op)
     ops = _with_caller(parse(text))
-    succ, problems = happens_before(ops, hints=False)
+    succ, hb_problems = happens_before(ops, hints=False)
+    problems += hb_problems
     reach = _reach(succ)
     acc = [o for o in ops if o.kind in ("gemm", "copy", "caller")]
     for i, x in enumerate(acc):

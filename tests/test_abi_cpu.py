@@ -229,3 +229,55 @@ def test_null_context_rejected_before_any_work(cce):
     assert cce.cce_looped_allgather_einsum(None, 2, 1, 1, 1, arr, m, arr, m, arr,
                                            cce_mat(8, 16, 16), None, 0, 0, None) == 1
     assert cce.cce_grouped_gemm(None, 2, 1, 1, arr, m, arr, m, arr, m, 0, None) == 1
+
+
+# ---------------------------------------------------------------------------
+# Fused permute: the GEMM sends the data itself (no copy stream)
+# ---------------------------------------------------------------------------
+FUSED = 0x8
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0), (1, 1)])
+def test_fused_plans_race_free_and_copy_free(n, kind, mode):
+    text = _plan(kind, n, mode, 1, FUSED)
+    assert plan_check.check(text) == []
+    ops = plan_check.parse(text)
+    assert all(o.kind == "gemm" and o.stream == "compute" for o in ops)
+    assert len(ops) == n
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_fused_allgather_forwards_what_the_ring_moves(n):
+    ops = plan_check.parse(_plan(0, n, 0, 1, FUSED))
+    looped = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, transfers = ring.simulate_allgather_einsum("lhs_rows", looped, looped)
+    for o in ops:
+        i = int(o.attrs["it"])
+        fwds = [w - {f"out{r}.h0"} for r, (_, w) in enumerate(o.items)]
+        if i == n - 1:
+            assert all(not f for f in fwds)
+            continue
+        for src, dst, sid in transfers[i]:
+            # rank src computes on shard sid and forwards it to rank dst
+            assert sched[i][src] == sid
+            assert fwds[src] == {f"recv{dst}.p{(i + 1) % 2}"}
+
+
+def test_fused_reducescatter_sends_accumulators_down_the_ring():
+    n = 4
+    ops = plan_check.parse(_plan(1, n, 0, 1, FUSED))
+    for o in ops[:-1]:
+        i = int(o.attrs["it"])
+        for r, (_, w) in enumerate(o.items):
+            assert w == {f"acc{(r - 1) % n}.p{(i + 1) % 2}.h0"}
+    for r, (_, w) in enumerate(ops[-1].items):
+        assert w == {f"out{r}.h0"}
+
+
+def test_checker_flags_intra_launch_conflict():
+    """Plant a forward into the buffer another rank reads in the same launch."""
+    lines = _plan(0, 4, 0, 1, FUSED).strip().splitlines()
+    bad = lines[1].replace(">out0.h0+recv3.p0", ">out0.h0+recv1.p1")
+    assert bad != lines[1]
+    assert plan_check.check("\n".join([lines[0], bad] + lines[2:]))

@@ -274,3 +274,43 @@ def test_invalid_arguments_enqueue_nothing(ctx):
         cce.cce_grouped_gemm(ctx, [x], [x], [x])
     assert e.value.status == 1
     assert torch.count_nonzero(x) == 0
+
+
+# ---------------------------------------------------------------------------
+# Fused permute (the GEMM sends the data itself): bit-identical to the
+# copy-stream form, which the tests above compare with the oracle.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode,dims", AG_CASES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_allgather_fused_permute_matches(ctx, mode, dims, n, in_dt):
+    import collective_overlap_amd as cce
+    idt = torch.bfloat16 if in_dt == "bf16" else torch.float32
+    looped, local, oshape, ol, oc = _ag_inputs(mode, n, dims, idt, False, seed=20 + n)
+    outs = []
+    for flags in (0, cce.CCE_FLAG_FUSED_PERMUTE):
+        out = [torch.full(oshape, float("nan"), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+        cce.cce_looped_allgather_einsum(ctx, mode, looped, local, out, flags=flags)
+        outs.append(out)
+    sync()
+    ref = oe.allgather_einsum(mode, ol, oc)
+    for r in range(n):
+        assert torch.equal(outs[0][r], outs[1][r]), f"rank {r}"
+        assert_bf16_close(np64(outs[1][r]), ref[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("mode,dims", RS_CASES)
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_reducescatter_fused_permute_matches(ctx, mode, dims, n):
+    import collective_overlap_amd as cce
+    a, b, oshape, oa, ob = _rs_inputs(mode, n, dims, torch.bfloat16, False, seed=30 + n)
+    outs = []
+    for flags in (0, cce.CCE_FLAG_FUSED_PERMUTE):
+        out = [torch.full(oshape, float("nan"), device=DEV) for _ in range(n)]
+        cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out, flags=flags)
+        outs.append(out)
+    sync()
+    ref = oe.einsum_reducescatter(mode, oa, ob)
+    for r in range(n):
+        assert torch.equal(outs[0][r], outs[1][r]), f"rank {r}"
+        assert_f32_close(np64(outs[1][r]), ref[r], f"rank {r}")
