@@ -337,6 +337,25 @@ def gemm_roofline(recs, dtype, steps):
     return roof, per
 
 
+def measured_traffic(workload, permute):
+    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE
+    counter runs (profiles/traffic_<workload>.json), scaled by the factors a
+    plain copy of known size gave.  None when no such run exists for this
+    workload and permute form, or when the GEMM source has changed since the
+    counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    with open(os.path.join(ROOT, t["kernel_source"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != t["kernel_source_sha256"] or t.get("permute") != permute:
+        return None
+    return t["gemm_bytes_per_launch"]["mean"]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +409,10 @@ def main(argv=None):
     ms_per_step = wall / a.steps * 1e3
     value = step.flops * a.steps / wall / 1e12
     roof, per_shape = gemm_roofline(recs, step.dtype, a.steps)
+    if roof is not None:
+        roof["traffic"] = measured_traffic(a.workload, a.permute)
+        if roof["traffic"] is not None:
+            roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 counters)"
 
     epi = [r for r in recs if r["kind"] == "epilogue"]
     epi_info = None
