@@ -69,7 +69,7 @@ def compile_one(src: str, extra=(), build_dir: str = BUILD) -> str:
 def build(jobs: int = 4, verbose: bool = False, extra=(), out: str = LIB,
           build_dir: str = BUILD) -> str:
     """Compile every source and link `out`.  `extra` adds compiler flags
-    (e.g. the GEMM pipeline knobs -DCCE_GEMM_BK=.. -DCCE_GEMM_NS=..)."""
+    (e.g. the GEMM k-tile knob -DCCE_GEMM_BK=..)."""
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda src: compile_one(src, extra, build_dir), SOURCES))

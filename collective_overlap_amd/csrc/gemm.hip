@@ -48,33 +48,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kOob = 0x40000000;
 
-// Pipeline shape of the bf16 kernel: k-tile depth and LDS stages (build-time
-// tuning knobs; 256x256 tiles need NS * (BM + BN) * BK * 2 <= 160 KB).
+// k-tile depth of the bf16 kernel (build-time tuning knob; 256x256 tiles need
+// 2 * (BM + BN) * BK * 2 <= 160 KB of LDS).
 #ifndef CCE_GEMM_BK
 #define CCE_GEMM_BK 64
 #endif
-#ifndef CCE_GEMM_NS
-#define CCE_GEMM_NS 2
-#endif
 constexpr int kBK = CCE_GEMM_BK;
-constexpr int kNS = CCE_GEMM_NS;           // added to steer a load past num_records
+constexpr int kNS = 2;                     // LDS stages
+// added to steer a load past num_records
 constexpr int64_t kMaxRsrcBytes = kOob - 256;
-
-// Interleave groups of the scheduling region: for every MFMA one DS read,
-// one DS write and one VMEM load while any of those remain.
-template <int NMF, int NRD, int NWR, int NGL>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int q = 0; q < NMF; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    if (q < NWR) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-    if (q < NGL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-  }
-  if (NRD > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
-  if (NWR > NMF) __builtin_amdgcn_sched_group_barrier(0x200, NWR - NMF, 0);
-  if (NGL > NMF) __builtin_amdgcn_sched_group_barrier(0x020, NGL - NMF, 0);
-}
 
 struct KArgs {
   int groups;
@@ -208,9 +190,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   constexpr int B_DMA = BN / (4 * RPI);
   constexpr int N_DMA = A_DMA + B_DMA;
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(KK % 2 == 0 && NS >= 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+  static_assert(KK % 2 == 0 && NS == 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
+  static_assert(N_DMA < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
@@ -219,7 +201,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform (an SGPR), so that LDS destinations of the direct loads are
+  // scalar additions into M0 rather than VGPR reads.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   const __bf16* A = reinterpret_cast<const __bf16*>(a.p.a[g]);
@@ -262,6 +246,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     for (int p = 0; p < B_DMA; ++p) dma16(rb, s + BM * ROWB + p * 4096, b_off[p] + kadd);
   };
 
+  auto kadd_of = [&](int k0) {
+    return k0 * 2u + ((k0 + dl_chunk * 8) < a.K ? 0u : uint32_t(kOob));
+  };
+  // Load instruction d of the wave's N_DMA (A first, then B).
+  auto dma_one = [&](int buf, uint32_t kadd, int d) {
+    char* s = smem + buf * STAGE + wave * 1024;
+    if (d < A_DMA) dma16(ra, s + d * 4096, a_off[d] + kadd);
+    else dma16(rb, s + BM * ROWB + (d - A_DMA) * 4096, b_off[d - A_DMA] + kadd);
+  };
+
   // Fragment addressing: row r = base + 32 i + (lane & 31) with base a
   // multiple of 32, so swz(r) = swz(lane & 31); chunk 2 kk + (lane >> 5).
   const int frow = lane & 31;
@@ -284,6 +278,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     for (int j = 0; j < FM; ++j)
       fa[slot][j] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(s + fa_base + fsw[kk] + j * 32 * ROWB));
+  };
+
+  // Fragment q of step kk: B^T blocks 0..FN-1, then A blocks.
+  auto fread_one = [&](int buf, int kk, int slot, int q) {
+    const char* s = smem + buf * STAGE;
+    if (q < FN)
+      fb[slot][q] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(s + fb_base + fsw[kk] + q * 32 * ROWB));
+    else
+      fa[slot][q - FN] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(s + fa_base + fsw[kk] + (q - FN) * 32 * ROWB));
   };
 
   // Fused permute: the looped operand (A or B) is written once to the next
@@ -317,54 +322,77 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
 
-  auto mfma = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][i], fa[slot][j], acc[i][j],
-                                                            0, 0, 0);
+  auto mfma_one = [&](int slot, int q) {
+    const int i = q / FM, j = q % FM;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][i], fa[slot][j], acc[i][j], 0, 0, 0);
   };
 
-  // Pipeline: NS LDS buffers, one per k tile in flight.  Per k tile kt:
-  //   kk = 0..KK-2: MFMA(step kk) | LDS reads of step kk+1
-  //   wait for tile kt+1's loads (newer ones may stay in flight), barrier
-  //   kk = KK-1:    MFMA | LDS reads of step 0 of tile kt+1 | loads of tile
-  //                 kt+NS into tile kt's buffer
+  // Pipeline: two LDS buffers; tile kt in buffer kt % 2.  Per k tile kt:
+  //   kk = 0 .. KK-2: MFMA(step kk) | LDS reads of step kk+1
+  //   wait for this wave's loads, barrier
+  //   kk = KK-1:      MFMA | LDS reads of step 0 of tile kt+1
   // Tile kt's buffer is free after the barrier: its last fragments (step
-  // KK-1) were read before it.  The barrier also makes every wave's loads of
-  // tile kt+1 visible before they are read.  The loop body has no branches:
-  // loads past the end of K are steered out of range and land as zeros, so
-  // the tail needs no special case.
+  // KK-1) were read before it, and the barrier makes every wave's loads of
+  // tile kt+1 visible.  The loads of tile kt+2 into that buffer are spread
+  // over two steps: the first half during step KK-1 of iteration kt, the
+  // second half during step 0 of iteration kt+1, one instruction per
+  // NMF / C MFMAs, so that the vector memory path sees a steady stream
+  // instead of one burst per k tile.  Each step is issued in a fixed order
+  // (MFMA, fragment read, load), fenced by scheduling barriers.  The loop
+  // body has no branches on the data path: loads past the end of K are
+  // steered out of range and land as zeros, so the tail needs no special
+  // case.
+  constexpr int NMF = FM * FN;
+  constexpr int C = (N_DMA + 1) / 2;         // loads per half
   const int KT = (a.K + BK - 1) / BK;
   if (KT > 0) {
-#pragma unroll
-    for (int st = 0; st < NS; ++st) gload(st, st * BK);
-    wait_vmcnt<(NS - 1) * N_DMA>();
+    gload(0, 0);
+    gload(1, BK);
+    wait_vmcnt<N_DMA>();
     __syncthreads();
     forward(0, 0);
-    fread(0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < FM + FN; ++q) fread_one(0, 0, 0, q);
   }
   int cur = 0;                  // buffer of tile kt
   for (int kt = 0; kt < KT; ++kt) {
-    const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+    const int nxt = cur ^ 1;
+    // Second half of tile kt+1's loads.  At kt = 0 this repeats loads of the
+    // prologue: the same bytes to the same place, first read after barrier 0.
+    const uint32_t kadd1 = kadd_of((kt + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk + 1 < KK; ++kk) {
-      fread(cur, kk + 1, (kk + 1) & 1);
-      mfma(kk & 1);
-      interleave<FM * FN, FM + FN, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        mfma_one(kk & 1, q);
+        if (q < FM + FN) fread_one(cur, kk + 1, (kk + 1) & 1, q);
+#pragma unroll
+        for (int d = C; d < N_DMA; ++d)
+          if (kk == 0 && (d - C) * NMF / C == q) dma_one(nxt, kadd1, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // The compiler does not order the global->LDS loads before the barrier
-    // by itself: wait for tile kt+1's (the NS-2 newer tiles may stay out).
-    // (With NS > 2 the forward stores would upset this count: wait for all.)
-    if (NS > 2 && (fwd_a || fwd_b)) wait_vmcnt<0>();
-    else wait_vmcnt<(NS - 2) * N_DMA>();
+    // by itself: wait for all of this wave's (tile kt+1's, and forwarded
+    // stores).
+    wait_vmcnt<0>();
     __syncthreads();
+    {
+      const uint32_t kadd = kadd_of((kt + NS) * BK);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        mfma_one((KK - 1) & 1, q);
+        if (q < FM + FN) fread_one(nxt, 0, 0, q);
+#pragma unroll
+        for (int d = 0; d < C; ++d)
+          if (d * NMF / C == q) dma_one(cur, kadd, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Forward tile kt+1 (fused permute) after this step's work is issued.
     if (kt + 1 < KT) forward(nxt, kt + 1);
-    fread(nxt, 0, 0);
-    gload(cur, (kt + NS) * BK);
-    mfma(1);
-    interleave<FM * FN, FM + FN, 0, N_DMA>();
     cur = nxt;
   }
   // The last iterations issued loads past K (they land as zeros); drain them
