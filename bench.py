@@ -88,10 +88,11 @@ class Gpt3Ffn:
                                         flags=flags | cce.CCE_FLAG_GELU)
         cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", self.H, self.W2, self.acc,
                                             self.ws_rs, flags=flags)
-        for r in range(self.n):
-            cce.cce_fused_reduce_epilogue(ctx, [self.acc[r]], self.b, self.R[r], self.out[r],
-                                          self.p, 0, 0, mask_row0=r * self.ts, mask_col0=0,
-                                          mask_ld=self.Hd)
+        # One launch for the 8 ranks' shards (each rank's slice of the
+        # reduced tensor gets bias, dropout and residual).
+        cce.cce_fused_reduce_epilogue_batched(
+            ctx, [[a] for a in self.acc], self.b, self.R, self.out, self.p, 0, 0,
+            mask_row0=[r * self.ts for r in range(self.n)], mask_col0=0, mask_ld=self.Hd)
 
     def oracle_sample(self, t=8):
         """The oracle end to end on t tokens of every shard; returns

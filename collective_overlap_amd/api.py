@@ -25,7 +25,8 @@ __all__ = [
     "Context", "cce_shard_schedule", "cce_looped_allgather_einsum",
     "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
     "cce_looped_einsum_reducescatter_workspace", "cce_grouped_gemm",
-    "cce_fused_reduce_epilogue", "cce_describe_plan", "cce_version",
+    "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched", "cce_describe_plan",
+    "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
     "AG_MODES", "RS_MODES",
 ]
@@ -242,3 +243,35 @@ def cce_fused_reduce_epilogue(ctx: Context, partials, bias, residual, out, p_dro
         mask_out.data_ptr() if mask_out is not None else None, 0,
         _stream(stream, out.device)), "cce_fused_reduce_epilogue")
     return out
+
+
+def cce_fused_reduce_epilogue_batched(ctx: Context, partials, bias, residuals, outs,
+                                      p_drop: float, seed: int = 0, offset: int = 0,
+                                      mask_row0=None, mask_col0: int = 0,
+                                      mask_ld: int | None = None, mask_outs=None, stream=None):
+    """outs[b] = residuals[b] + keep * (sum(partials[b]) + bias) / (1 - p_drop), one launch.
+    partials: list of n_batch lists of equal length; residuals, mask_outs: lists or None;
+    mask_row0: list of n_batch row bases (default 0 for every entry)."""
+    nb = len(outs)
+    if len(partials) != nb or len({len(p) for p in partials}) != 1:
+        raise ValueError("partials must be n_batch lists of equal length")
+    flat = [t for ps in partials for t in ps]
+    pm = _same(flat, "partial")
+    om = _same(outs, "out")
+    rm = _same(residuals, "residual") if residuals is not None else None
+    if mask_ld is None:
+        mask_ld = mask_col0 + pm.cols
+    rows0 = list(mask_row0) if mask_row0 is not None else [0] * nb
+    bias_t = _dtype(bias.dtype) if bias is not None else _dtype(outs[0].dtype)
+    res_t = _dtype(residuals[0].dtype) if residuals is not None else _dtype(outs[0].dtype)
+    check(lib().cce_fused_reduce_epilogue_batched(
+        ctx.handle, nb, len(partials[0]), _dtype(flat[0].dtype),
+        ptr_array([t.data_ptr() for t in flat]), pm,
+        bias.data_ptr() if bias is not None else None, bias_t,
+        ptr_array([t.data_ptr() for t in residuals]) if residuals is not None else None, res_t,
+        rm.ld if rm is not None else pm.cols,
+        float(p_drop), int(seed), int(offset), (ctypes.c_int64 * nb)(*rows0), int(mask_col0),
+        int(mask_ld), ptr_array([t.data_ptr() for t in outs]), _dtype(outs[0].dtype), om.ld,
+        ptr_array([t.data_ptr() for t in mask_outs]) if mask_outs is not None else None, 0,
+        _stream(stream, outs[0].device)), "cce_fused_reduce_epilogue_batched")
+    return outs

@@ -854,70 +854,88 @@ cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtyp
   return prof_end(ctx, hs, slot);
 }
 
-cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype part_t,
-                                     const void* const* partials, cce_mat shape, const void* bias,
-                                     cce_dtype bias_t, const void* residual, cce_dtype res_t,
-                                     int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
-                                     int64_t mask_row0, int64_t mask_col0, int64_t mask_ld,
-                                     void* out, cce_dtype out_t, int64_t ld_out, uint8_t* mask_out,
-                                     uint32_t flags, cce_stream stream) {
-  clear_error();
+// Shared by the single and the batched epilogue entry points.  residuals and
+// mask_outs are NULL or arrays of n_batch non-NULL pointers.
+static cce_status epilogue_impl(cce_ctx* ctx, int n_batch, int n_partials, cce_dtype part_t,
+                                const void* const* partials, cce_mat shape, const void* bias,
+                                cce_dtype bias_t, const void* const* residuals, cce_dtype res_t,
+                                int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
+                                const int64_t* mask_row0, int64_t mask_col0, int64_t mask_ld,
+                                void* const* outs, cce_dtype out_t, int64_t ld_out,
+                                uint8_t* const* mask_outs, uint32_t flags, cce_stream stream) {
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags != 0) return fail(CCE_EINVAL, "flags must be 0");
+  if (n_batch < 1) return fail(CCE_EINVAL, "n_batch < 1");
   if (n_partials < 1) return fail(CCE_EINVAL, "n_partials < 1");
-  if (n_partials > CCE_MAX_RANKS) return fail(CCE_EUNSUPPORTED, "n_partials > CCE_MAX_RANKS");
+  if (static_cast<int64_t>(n_partials) * n_batch > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "n_batch * n_partials > CCE_MAX_RANKS");
   if (!partials) return fail(CCE_EINVAL, "partials is NULL");
-  if (!dtype_ok(part_t) || !dtype_ok(out_t) || (bias && !dtype_ok(bias_t)) || (residual && !dtype_ok(res_t)))
+  if (!outs) return fail(CCE_EINVAL, "out is NULL");
+  if (!mask_row0) return fail(CCE_EINVAL, "mask_row0 is NULL");
+  if (!dtype_ok(part_t) || !dtype_ok(out_t) || (bias && !dtype_ok(bias_t)) ||
+      (residuals && !dtype_ok(res_t)))
     return fail(CCE_EINVAL, "bad dtype");
-  if ((bias && bias_t != out_t) || (residual && res_t != out_t))
+  if ((bias && bias_t != out_t) || (residuals && res_t != out_t))
     return fail(CCE_EUNSUPPORTED, "bias and residual must have the output dtype");
   if (std::isnan(p_drop)) return fail(CCE_EINVAL, "p_drop is NaN");
   CCE_TRY(check_mat("shape", shape));
   const cce_mat rmat{shape.rows, shape.cols, ld_res}, omat{shape.rows, shape.cols, ld_out};
-  if (residual) CCE_TRY(check_mat("residual", rmat));
+  if (residuals) CCE_TRY(check_mat("residual", rmat));
   CCE_TRY(check_mat("out", omat));
-  if (mask_row0 < 0 || mask_col0 < 0 || mask_ld < mask_col0 + shape.cols)
-    return fail(CCE_EINVAL, "mask index base must satisfy 0 <= row0, 0 <= col0, col0 + cols <= mask_ld");
+  if (mask_col0 < 0 || mask_ld < mask_col0 + shape.cols)
+    return fail(CCE_EINVAL, "mask index base must satisfy 0 <= col0, col0 + cols <= mask_ld");
+  for (int b = 0; b < n_batch; ++b)
+    if (mask_row0[b] < 0) return fail(CCE_EINVAL, "mask row base must be >= 0");
   const size_t ep = esize(part_t), eo = esize(out_t);
-  const int64_t ps = span_bytes(shape, ep), rs = residual ? span_bytes(rmat, eo) : 0,
+  const int64_t ps = span_bytes(shape, ep), rs = residuals ? span_bytes(rmat, eo) : 0,
                 os = span_bytes(omat, eo), bs = bias ? shape.cols * static_cast<int64_t>(eo) : 0,
-                ms = mask_out ? shape.rows * shape.cols : 0;
+                ms = mask_outs ? shape.rows * shape.cols : 0;
   std::vector<Range> ranges;
-  for (int k = 0; k < n_partials; ++k) {
+  for (int k = 0; k < n_partials * n_batch; ++k) {
     const std::string ks = std::to_string(k);
     CCE_TRY(check_ptr(("partials[" + ks + "]").c_str(), partials[k], ps));
     ranges.push_back(range_of(partials[k], ps, "partials[" + ks + "]", false));
   }
   if (bias) CCE_TRY(check_ptr("bias", bias, bs));
-  if (residual) CCE_TRY(check_ptr("residual", residual, rs));
-  CCE_TRY(check_ptr("out", out, os));
-  if (mask_out) CCE_TRY(check_ptr("mask_out", mask_out, ms));
   ranges.push_back(range_of(bias, bs, "bias", false));
-  ranges.push_back(range_of(residual, rs, "residual", false));
-  ranges.push_back(range_of(out, os, "out", true));
-  if (mask_out) ranges.push_back(range_of(mask_out, ms, "mask_out", true));
+  for (int b = 0; b < n_batch; ++b) {
+    const std::string bsx = "[" + std::to_string(b) + "]";
+    if (residuals) {
+      CCE_TRY(check_ptr(("residual" + bsx).c_str(), residuals[b], rs));
+      ranges.push_back(range_of(residuals[b], rs, "residual" + bsx, false));
+    }
+    CCE_TRY(check_ptr(("out" + bsx).c_str(), outs[b], os));
+    ranges.push_back(range_of(outs[b], os, "out" + bsx, true));
+    if (mask_outs) {
+      CCE_TRY(check_ptr(("mask_out" + bsx).c_str(), mask_outs[b], ms));
+      ranges.push_back(range_of(mask_outs[b], ms, "mask_out" + bsx, true));
+    }
+  }
   CCE_TRY(check_overlaps(ranges));
   if (shape.rows == 0 || shape.cols == 0) return CCE_OK;
 
   EpilogueLaunch L;
   L.n = n_partials;
+  L.batch = n_batch;
   L.part_t = part_t;
-  for (int k = 0; k < n_partials; ++k) L.parts[k] = partials[k];
+  for (int k = 0; k < n_partials * n_batch; ++k) L.parts[k] = partials[k];
+  for (int b = 0; b < n_batch; ++b) {
+    L.res[b] = residuals ? residuals[b] : nullptr;
+    L.out[b] = outs[b];
+    L.mask[b] = mask_outs ? mask_outs[b] : nullptr;
+    L.mrow0[b] = mask_row0[b];
+  }
   L.rows = shape.rows;
   L.cols = shape.cols;
   L.ld_part = shape.ld;
   L.bias = bias;
   L.bias_t = bias_t;
-  L.res = residual;
   L.res_t = res_t;
   L.ld_res = ld_res;
-  L.out = out;
   L.out_t = out_t;
   L.ld_out = ld_out;
-  L.mask = mask_out;
   L.seed = seed;
   L.offset = offset;
-  L.mrow0 = mask_row0;
   L.mcol0 = mask_col0;
   L.mld = mask_ld;
   if (p_drop <= 0.0) {
@@ -933,13 +951,51 @@ cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype par
   }
   DeviceGuard guard(ctx->device);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const double ebytes = static_cast<double>(shape.rows) * shape.cols *
-                            (static_cast<double>(n_partials) * ep + (residual ? eo : 0) + eo) +
-                        (bias ? static_cast<double>(shape.cols) * eo : 0.0);
+  const double ebytes =
+      n_batch * (static_cast<double>(shape.rows) * shape.cols *
+                 (static_cast<double>(n_partials) * ep + (residuals ? eo : 0) + eo)) +
+      (bias ? static_cast<double>(shape.cols) * eo : 0.0);
   int slot;
   CCE_TRY(prof_begin(ctx, hs, 2, -1, 0.0, ebytes, &slot));
   CCE_TRY(launch_fused_epilogue(L, stream));
   return prof_end(ctx, hs, slot);
+}
+
+cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype part_t,
+                                     const void* const* partials, cce_mat shape, const void* bias,
+                                     cce_dtype bias_t, const void* residual, cce_dtype res_t,
+                                     int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
+                                     int64_t mask_row0, int64_t mask_col0, int64_t mask_ld,
+                                     void* out, cce_dtype out_t, int64_t ld_out, uint8_t* mask_out,
+                                     uint32_t flags, cce_stream stream) {
+  clear_error();
+  const void* res1[1] = {residual};
+  void* out1[1] = {out};
+  uint8_t* mask1[1] = {mask_out};
+  const int64_t row1[1] = {mask_row0};
+  return epilogue_impl(ctx, 1, n_partials, part_t, partials, shape, bias, bias_t,
+                       residual ? res1 : nullptr, res_t, ld_res, p_drop, seed, offset, row1,
+                       mask_col0, mask_ld, out1, out_t, ld_out, mask_out ? mask1 : nullptr, flags,
+                       stream);
+}
+
+cce_status cce_fused_reduce_epilogue_batched(
+    cce_ctx* ctx, int n_batch, int n_partials, cce_dtype part_t, const void* const* partials,
+    cce_mat shape, const void* bias, cce_dtype bias_t, const void* const* residuals,
+    cce_dtype res_t, int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
+    const int64_t* mask_row0, int64_t mask_col0, int64_t mask_ld, void* const* outs,
+    cce_dtype out_t, int64_t ld_out, uint8_t* const* mask_outs, uint32_t flags,
+    cce_stream stream) {
+  clear_error();
+  if (residuals)
+    for (int b = 0; b < n_batch && b < CCE_MAX_RANKS; ++b)
+      if (!residuals[b]) return fail(CCE_EINVAL, "residuals[b] is NULL (pass a NULL array for none)");
+  if (mask_outs)
+    for (int b = 0; b < n_batch && b < CCE_MAX_RANKS; ++b)
+      if (!mask_outs[b]) return fail(CCE_EINVAL, "mask_outs[b] is NULL (pass a NULL array for none)");
+  return epilogue_impl(ctx, n_batch, n_partials, part_t, partials, shape, bias, bias_t, residuals,
+                       res_t, ld_res, p_drop, seed, offset, mask_row0, mask_col0, mask_ld, outs,
+                       out_t, ld_out, mask_outs, flags, stream);
 }
 
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, uint32_t flags,

@@ -60,25 +60,27 @@ cce_status launch_grouped_gemm(const GemmLaunch& g, void* stream);
 // Fused reduce epilogue launch.
 // ---------------------------------------------------------------------------
 struct EpilogueLaunch {
-  int n = 0;
+  int n = 0;                  // partials per output
+  int batch = 1;              // outputs in the launch (batch * n <= kMaxGroups)
   cce_dtype part_t = CCE_F32;
-  const void* parts[kMaxGroups];
+  const void* parts[kMaxGroups];   // [b * n + k]
   int64_t rows = 0, cols = 0, ld_part = 0;
   const void* bias = nullptr;
   cce_dtype bias_t = CCE_F32;
-  const void* res = nullptr;
+  const void* res[kMaxGroups];     // per output; NULL entries: no residual
   cce_dtype res_t = CCE_F32;
   int64_t ld_res = 0;
-  void* out = nullptr;
+  void* out[kMaxGroups];
   cce_dtype out_t = CCE_F32;
   int64_t ld_out = 0;
-  uint8_t* mask = nullptr;
+  uint8_t* mask[kMaxGroups];       // per output; NULL entries: no mask output
+  int64_t mrow0[kMaxGroups];
   uint32_t threshold = 0;     // keep iff word >= threshold (when !drop_all)
   bool drop_all = false;
   bool dropout = false;       // p > 0
   float scale = 1.0f;
   uint64_t seed = 0, offset = 0;
-  int64_t mrow0 = 0, mcol0 = 0, mld = 0;
+  int64_t mcol0 = 0, mld = 0;
 };
 
 cce_status launch_fused_epilogue(const EpilogueLaunch& e, void* stream);

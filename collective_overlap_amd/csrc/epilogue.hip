@@ -40,19 +40,20 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct EArgs {
-  const void* parts[kMaxGroups];
+  const void* parts[kMaxGroups];   // [batch * n + k]
+  const void* res[kMaxGroups];     // per batch entry (NULL: no residual)
+  void* out[kMaxGroups];
+  uint8_t* mask[kMaxGroups];       // per batch entry (NULL: no mask output)
+  int64_t mrow0[kMaxGroups];
   int n;
   int rows, cols;
   int64_t ld_part, ld_res, ld_out;
   const void* bias;
-  const void* res;
-  void* out;
-  uint8_t* mask;
   uint32_t threshold;
   int mode;                 // 0: no dropout, 1: dropout, 2: drop everything
   float scale;
   uint32_t key0, key1, off0, off1;
-  int64_t mrow0, mcol0, mld;
+  int64_t mcol0, mld;
   bool aligned;             // 4 | mld and 4 | mcol0: two Philox blocks per vector
 };
 
@@ -91,15 +92,29 @@ __device__ __forceinline__ Philox4 block_for(const EArgs& a, uint64_t blk) {
 }
 
 // ---- typed loads / stores -------------------------------------------------
-template <typename T>
+// Partials, residual and output are touched exactly once: their vector loads
+// and stores are nontemporal (streamed past the caches).  The bias, reused by
+// every row, takes plain loads.
+template <typename T, bool NT>
 __device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
   if constexpr (sizeof(T) == 4) {
     const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
-    const f32x4 x = p[0], y = p[1];
+    f32x4 x, y;
+    if constexpr (NT) {
+      x = __builtin_nontemporal_load(p);
+      y = __builtin_nontemporal_load(p + 1);
+    } else {
+      x = p[0];
+      y = p[1];
+    }
     v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
     v[4] = y[0]; v[5] = y[1]; v[6] = y[2]; v[7] = y[3];
   } else {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + idx);
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(base) + idx);
+    u32x4 w;
+    if constexpr (NT) w = __builtin_nontemporal_load(p);
+    else w = *p;
+    const bf16x8 x = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(x[e]);
   }
@@ -115,13 +130,14 @@ template <typename T>
 __device__ __forceinline__ void store8(void* base, int64_t idx, const float (&v)[8]) {
   if constexpr (sizeof(T) == 4) {
     f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx);
-    p[0] = f32x4{v[0], v[1], v[2], v[3]};
-    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, p);
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, p + 1);
   } else {
     bf16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = static_cast<__bf16>(v[e]);
-    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(base) + idx) = h;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h),
+                                reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(base) + idx));
   }
 }
 
@@ -144,35 +160,42 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
   if (jv >= vpr) return;
   const int j = jv * 8;
   const bool full = (j + 8 <= a.cols);
+  const int bz = blockIdx.z;
+  const int n = NP > 0 ? NP : a.n;
+  const void* const* parts = a.parts + bz * n;
+  const void* res = a.res[bz];
+  void* out = a.out[bz];
+  uint8_t* mask = a.mask[bz];
+  const int64_t mrow0 = a.mrow0[bz];
   for (int i = blockIdx.y; i < a.rows; i += gridDim.y) {
     float s[8];
     bool keep[8];
-    const int64_t e0 = (a.mrow0 + i) * a.mld + a.mcol0 + j;
+    const int64_t e0 = (mrow0 + i) * a.mld + a.mcol0 + j;
     if (full) {
       // ---- vector path: 8 columns ----
       const int64_t ip = static_cast<int64_t>(i) * a.ld_part + j;
       float r[8];
-      if (a.res) load8<TR>(a.res, static_cast<int64_t>(i) * a.ld_res + j, r);
-      load8<TP>(a.parts[0], ip, s);
+      if (res) load8<TR, true>(res, static_cast<int64_t>(i) * a.ld_res + j, r);
+      load8<TP, true>(parts[0], ip, s);
       if constexpr (NP > 0) {
         float t[NP > 1 ? NP - 1 : 1][8];
 #pragma unroll
-        for (int k = 1; k < NP; ++k) load8<TP>(a.parts[k], ip, t[k - 1]);
+        for (int k = 1; k < NP; ++k) load8<TP, true>(parts[k], ip, t[k - 1]);
 #pragma unroll
         for (int k = 1; k < NP; ++k)
 #pragma unroll
           for (int e = 0; e < 8; ++e) s[e] = s[e] + t[k - 1][e];
       } else {
-        for (int k = 1; k < a.n; ++k) {
+        for (int k = 1; k < n; ++k) {
           float t[8];
-          load8<TP>(a.parts[k], ip, t);
+          load8<TP, true>(parts[k], ip, t);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s[e] = s[e] + t[e];
         }
       }
       if (a.bias) {
         float b[8];
-        load8<TB>(a.bias, j, b);
+        load8<TB, false>(a.bias, j, b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = s[e] + b[e];
       }
@@ -205,16 +228,16 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) keep[e] = true;
       }
-      if (a.res) {
+      if (res) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = s[e] + r[e];
       }
-      store8<TO>(a.out, static_cast<int64_t>(i) * a.ld_out + j, s);
-      if (a.mask) {
+      store8<TO>(out, static_cast<int64_t>(i) * a.ld_out + j, s);
+      if (mask) {
         uint64_t bits = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) bits |= static_cast<uint64_t>(keep[e] ? 1 : 0) << (8 * e);
-        uint8_t* mp = a.mask + static_cast<int64_t>(i) * a.cols + j;
+        uint8_t* mp = mask + static_cast<int64_t>(i) * a.cols + j;
         if ((a.cols & 7) == 0) {
           *reinterpret_cast<uint64_t*>(mp) = bits;
         } else {
@@ -227,9 +250,8 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
       for (int e = 0; j + e < a.cols; ++e) {
         const int c = j + e;
         const int64_t ip = static_cast<int64_t>(i) * a.ld_part + c;
-        float v = load1<TP>(a.parts[0], ip);
-        const int n = NP > 0 ? NP : a.n;
-        for (int k = 1; k < n; ++k) v = v + load1<TP>(a.parts[k], ip);
+        float v = load1<TP>(parts[0], ip);
+        for (int k = 1; k < n; ++k) v = v + load1<TP>(parts[k], ip);
         if (a.bias) v = v + load1<TB>(a.bias, c);
         bool kp = true;
         if (a.mode == 1) {
@@ -241,9 +263,9 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
           kp = false;
           v = 0.0f;
         }
-        if (a.res) v = v + load1<TR>(a.res, static_cast<int64_t>(i) * a.ld_res + c);
-        store1<TO>(a.out, static_cast<int64_t>(i) * a.ld_out + c, v);
-        if (a.mask) a.mask[static_cast<int64_t>(i) * a.cols + c] = kp ? 1 : 0;
+        if (res) v = v + load1<TR>(res, static_cast<int64_t>(i) * a.ld_res + c);
+        store1<TO>(out, static_cast<int64_t>(i) * a.ld_out + c, v);
+        if (mask) mask[static_cast<int64_t>(i) * a.cols + c] = kp ? 1 : 0;
       }
     }
   }
@@ -268,9 +290,15 @@ hipError_t launch_t(const EArgs& k, dim3 grid, hipStream_t s) {
 }  // namespace
 
 cce_status launch_fused_epilogue(const EpilogueLaunch& L, void* stream) {
-  if (L.rows <= 0 || L.cols <= 0) return CCE_OK;
+  if (L.rows <= 0 || L.cols <= 0 || L.batch <= 0) return CCE_OK;
   EArgs k{};
-  for (int i = 0; i < L.n; ++i) k.parts[i] = L.parts[i];
+  for (int i = 0; i < L.n * L.batch; ++i) k.parts[i] = L.parts[i];
+  for (int b = 0; b < L.batch; ++b) {
+    k.res[b] = L.res[b];
+    k.out[b] = L.out[b];
+    k.mask[b] = L.mask[b];
+    k.mrow0[b] = L.mrow0[b];
+  }
   k.n = L.n;
   k.rows = static_cast<int>(L.rows);
   k.cols = static_cast<int>(L.cols);
@@ -278,9 +306,6 @@ cce_status launch_fused_epilogue(const EpilogueLaunch& L, void* stream) {
   k.ld_res = L.ld_res;
   k.ld_out = L.ld_out;
   k.bias = L.bias;
-  k.res = L.res;
-  k.out = L.out;
-  k.mask = L.mask;
   k.threshold = L.threshold;
   k.mode = L.drop_all ? 2 : (L.dropout ? 1 : 0);
   k.scale = L.scale;
@@ -288,12 +313,12 @@ cce_status launch_fused_epilogue(const EpilogueLaunch& L, void* stream) {
   k.key1 = static_cast<uint32_t>(L.seed >> 32);
   k.off0 = static_cast<uint32_t>(L.offset);
   k.off1 = static_cast<uint32_t>(L.offset >> 32);
-  k.mrow0 = L.mrow0;
   k.mcol0 = L.mcol0;
   k.mld = L.mld;
   k.aligned = (L.mld % 4 == 0) && (L.mcol0 % 4 == 0);
   const int vpr = static_cast<int>((L.cols + 7) / 8);
-  dim3 grid((vpr + 255) / 256, static_cast<unsigned>(L.rows < 65535 ? L.rows : 65535));
+  dim3 grid((vpr + 255) / 256, static_cast<unsigned>(L.rows < 65535 ? L.rows : 65535),
+            static_cast<unsigned>(L.batch));
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bias and residual share the output type (checked by the caller).
   hipError_t e;

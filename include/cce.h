@@ -279,6 +279,29 @@ cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype par
                                      uint8_t* mask_out, uint32_t flags, cce_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Batched fused reduce epilogue: n_batch independent epilogues of one shape
+ * in a single launch, e.g. one per rank of a ReduceScatter whose shards each
+ * receive bias, dropout and residual ([CC] fused collectives: the pointwise
+ * tail applied to every rank's slice of the reduced tensor).
+ *
+ * Output b is computed exactly as cce_fused_reduce_epilogue computes it from
+ *   partials[b * n_partials + k] (k < n_partials), the shared bias,
+ *   residuals[b], mask row base mask_row0[b] (shared mask_col0, mask_ld),
+ *   written to outs[b] (and mask_outs[b]),
+ * so results are bit-identical to n_batch single calls.  residuals and
+ * mask_outs are NULL (none) or host arrays of n_batch non-NULL device
+ * pointers; mask_row0 is a host array of n_batch values.
+ * 1 <= n_batch, n_batch * n_partials <= CCE_MAX_RANKS.  flags: must be 0.
+ * ---------------------------------------------------------------------- */
+cce_status cce_fused_reduce_epilogue_batched(
+    cce_ctx* ctx, int n_batch, int n_partials, cce_dtype part_t, const void* const* partials,
+    cce_mat shape, const void* bias, cce_dtype bias_t, const void* const* residuals,
+    cce_dtype res_t, int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
+    const int64_t* mask_row0, int64_t mask_col0, int64_t mask_ld, void* const* outs,
+    cce_dtype out_t, int64_t ld_out, uint8_t* const* mask_outs, uint32_t flags,
+    cce_stream stream);
+
+/* ------------------------------------------------------------------------
  * Plan description, host-only (no device, no context): writes the ordered
  * list of operations that a looped call with these arguments would enqueue,
  * one per line, into buf (NUL-terminated; *needed receives the full length

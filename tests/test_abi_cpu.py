@@ -229,6 +229,11 @@ def test_null_context_rejected_before_any_work(cce):
     assert cce.cce_looped_allgather_einsum(None, 2, 1, 1, 1, arr, m, arr, m, arr,
                                            cce_mat(8, 16, 16), None, 0, 0, None) == 1
     assert cce.cce_grouped_gemm(None, 2, 1, 1, arr, m, arr, m, arr, m, 0, None) == 1
+    import ctypes
+    rows0 = (ctypes.c_int64 * 2)(0, 8)
+    assert cce.cce_fused_reduce_epilogue_batched(None, 2, 1, 0, arr, m, None, 0, None, 0, 8,
+                                                 0.1, 0, 0, rows0, 0, 8, arr, 0, 8, None, 0,
+                                                 None) == 1
 
 
 # ---------------------------------------------------------------------------

@@ -96,3 +96,56 @@ def test_keep_rate_full_size_mask(ctx):
     for r in (0, 1, 4095, 8191):
         want = philox.keep_mask(1, cols, 0.1, 0, 0, row0=r, col0=0, ld=cols)[0]
         assert np.array_equal(mask[r].cpu().numpy().astype(bool), want)
+
+
+BATCHED = [
+    # n_batch, n_partials, rows, cols, ld, part, out, p, seed, offset, mask_ld
+    (3, 2, 45, 264, None, "bf16", "bf16", 0.1, 17, 3, 264),
+    (8, 1, 16, 96, None, "f32", "bf16", 0.1, 0, 0, 96),
+    (4, 3, 9, 61, 64, "f32", "f32", 0.4, 5, 1, 61),      # ragged columns, odd mask index
+    (2, 32, 7, 40, None, "bf16", "f32", 0.2, 8, 0, 40),  # n_batch * n_partials == 64
+]
+
+
+@pytest.mark.parametrize("case", BATCHED)
+def test_batched_equals_single_calls_and_oracle(ctx, case):
+    """One batched launch gives, bit for bit, what n_batch single calls give,
+    and each output matches the oracle (mask bit-exact) with its own row base."""
+    import collective_overlap_amd as cce
+    nb, n, rows, cols, ld, pt, ot, p, seed, off, mld = case
+    print(f"[gpu] batched epilogue {case}", flush=True)
+    pdt = torch.float32 if pt == "f32" else torch.bfloat16
+    odt = torch.float32 if ot == "f32" else torch.bfloat16
+    parts = [[_mk((rows, cols), 100 + 10 * b + k, pdt, ld) for k in range(n)] for b in range(nb)]
+    bias = W.normal((cols,), 0.02, 90, device=DEV, dtype=odt)
+    res = [_mk((rows, cols), 200 + b, odt, ld) for b in range(nb)]
+    row0 = [b * rows for b in range(nb)]
+    outs = [torch.full((rows, ld or cols), float("nan"), device=DEV, dtype=odt)[:, :cols]
+            for _ in range(nb)]
+    masks = [torch.full((rows, cols), 7, device=DEV, dtype=torch.uint8) for _ in range(nb)]
+    cce.cce_fused_reduce_epilogue_batched(ctx, parts, bias, res, outs, p, seed, off,
+                                          mask_row0=row0, mask_col0=0, mask_ld=mld,
+                                          mask_outs=masks)
+    single = [torch.empty((rows, ld or cols), device=DEV, dtype=odt)[:, :cols] for _ in range(nb)]
+    for b in range(nb):
+        cce.cce_fused_reduce_epilogue(ctx, parts[b], bias, res[b], single[b], p, seed, off,
+                                      row0[b], 0, mld)
+    sync()
+    for b in range(nb):
+        it = torch.int16 if odt == torch.bfloat16 else torch.int32
+        assert torch.equal(outs[b].contiguous().view(it), single[b].contiguous().view(it))
+        ref, keep = oep.fused_reduce_epilogue([np64(x) for x in parts[b]], np64(bias),
+                                              np64(res[b]), p, seed, off, row0[b], 0, mld)
+        assert np.array_equal(masks[b].cpu().numpy().astype(bool), keep), f"mask {b}"
+        if ot == "f32":
+            assert_f32_close(np64(outs[b]), ref, f"batched {b}", tol=1e-6)
+        else:
+            assert_bf16_close(np64(outs[b]), ref, f"batched {b}")
+
+
+def test_batched_rejects_too_many_operands(ctx):
+    import collective_overlap_amd as cce
+    parts = [[torch.zeros((4, 8), device=DEV) for _ in range(33)] for _ in range(2)]
+    outs = [torch.empty((4, 8), device=DEV) for _ in range(2)]
+    with pytest.raises(RuntimeError):
+        cce.cce_fused_reduce_epilogue_batched(ctx, parts, None, None, outs, 0.0)
