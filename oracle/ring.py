@@ -16,7 +16,11 @@ Section 4 (Figures 4 and 5, golden fixtures), the ring pair list of [OV]
 Section 5.1, the alignment rules stated there (AllGather at loop start,
 ReduceScatter at loop end), agreement with the monolithic collectives for
 N = 1..16 on exact-integer inputs, and AllReduce = ReduceScatter + AllGather
-([OV] Section 2.1; CoCoNet's AllReduce split).
+([OV] Section 2.1; CoCoNet's AllReduce split).  The bidirectional variant of
+[OV] Section 5.4.2 (whose figures are not in the text) is pinned by exact
+agreement with the monolithic definitions for N = 1..16, by the halved
+iteration count that section states, by every rank still sending N-1 shards
+to ring neighbours only, and by every shard / slice being covered once.
 """
 
 from __future__ import annotations
@@ -236,3 +240,135 @@ def simulate_einsum_reducescatter(mode: str, a: list[np.ndarray],
         acc = [recv[r] + parts[r] for r in range(n)]               # Done + Add
     assert labels == list(range(n)), "ReduceScatter loop not aligned at end"
     return acc, schedule, transfers
+
+
+# --------------------------------------------------------------------------
+# Bidirectional data transfer ([OV] Section 5.4.2)
+#
+# Reading of the section (its Figures 9 and 10 are not in the text): every
+# rank keeps two looped buffers (AllGather) or two accumulators
+# (ReduceScatter), one travelling each way round the ring: "cw" along the
+# loop's pairs of Section 5.1 (rank r sends to r-1) and "ccw" along the
+# reversed pairs (rank r sends to r+1).  Each iteration computes the two
+# partial einsums, one per direction, as one operation, so the loop has
+# ceil(N/2) iterations instead of N.  The AllGather needs a prologue -- one
+# ccw permute before the loop, so that the ccw buffer starts one shard away
+# from the cw buffer -- and the ReduceScatter an epilogue -- one ccw permute
+# after the loop that brings each ccw accumulator to the rank of its shard,
+# followed by the sum of the two accumulators.  Both move N-1 shards per
+# rank in total, like the one-way loop.
+# --------------------------------------------------------------------------
+
+def reversed_ring_pairs(n: int) -> list[tuple[int, int]]:
+    """The loop's pairs with source and destination swapped: r -> r+1."""
+    return [(d, s) for s, d in ring_pairs(n)]
+
+
+def bidir_lengths(n: int) -> tuple[int, int]:
+    """Iterations of the cw and the ccw stream: ceil(N/2) and floor(N/2)."""
+    return (n + 1) // 2, n // 2
+
+
+def simulate_allgather_einsum_bidir(mode: str, looped: list[np.ndarray],
+                                    local: list[np.ndarray]):
+    """Bidirectional looped AllGather-Einsum, rank by rank.
+
+    Prologue: the ccw buffer of every rank receives its ccw neighbour's
+    shard.  Iteration i computes the partial einsum on the cw buffer's shard
+    and, while i < floor(N/2), on the ccw buffer's shard; then, unless the
+    stream is done, each buffer is sent on in its direction.
+
+    Returns (outputs, schedule, transfers):
+      schedule[i][r]  -- (cw shard ID, ccw shard ID or None) of rank r;
+      transfers       -- list of (phase, direction, src, dst, shard_id),
+                         phase "prologue" or the iteration index.
+    """
+    n = len(looped)
+    assert mode in AG_MODES and len(local) == n
+    k_cw, k_ccw = bidir_lengths(n)
+    cw_pairs, ccw_pairs = ring_pairs(n), reversed_ring_pairs(n)
+    own = [(looped[r], r) for r in range(n)]
+    cw = list(own)                                   # aligned at loop start
+    transfers = []
+    ccw = [None] * n
+    if k_ccw > 0:                                    # prologue
+        ccw = collective_permute(own, ccw_pairs)
+        transfers += [("prologue", "ccw", s, d, own[s][1]) for s, d in ccw_pairs]
+    outs = [np.zeros(_ag_out_shape(mode, n, looped[0], local[r])) for r in range(n)]
+    schedule = []
+    for i in range(k_cw):
+        do_ccw = i < k_ccw
+        schedule.append([(cw[r][1], ccw[r][1] if do_ccw else None) for r in range(n)])
+        for r in range(n):
+            for buf, sid in ([cw[r], ccw[r]] if do_ccw else [cw[r]]):
+                part = _ag_partial(mode, buf, local[r], sid)
+                outs[r] = _ag_update(mode, outs[r], part, sid)
+        if i + 1 < k_cw:
+            transfers += [(i, "cw", s, d, cw[s][1]) for s, d in cw_pairs]
+            cw = collective_permute(cw, cw_pairs)
+        if i + 1 < k_ccw:
+            transfers += [(i, "ccw", s, d, ccw[s][1]) for s, d in ccw_pairs]
+            ccw = collective_permute(ccw, ccw_pairs)
+    return outs, schedule, transfers
+
+
+def _start_labels(n: int, pairs, hops: int) -> list[int]:
+    """Shard ID each rank must start an accumulator with so that after
+    `hops` permutes along `pairs` the accumulator sits on the rank of its
+    ID (markers pushed through the permutes, as reducescatter_start_ids)."""
+    markers = list(range(n))
+    for _ in range(hops):
+        markers = collective_permute(markers, pairs)
+    start = [None] * n
+    for landing_rank, starting_rank in enumerate(markers):
+        start[starting_rank] = landing_rank
+    return start
+
+
+def simulate_einsum_reducescatter_bidir(mode: str, a: list[np.ndarray],
+                                        b: list[np.ndarray]):
+    """Bidirectional looped Einsum-ReduceScatter, rank by rank.
+
+    The cw accumulator of a shard makes ceil(N/2) - 1 hops and ends on the
+    rank of its shard at loop end; the ccw accumulator makes floor(N/2) - 1
+    hops in the loop and one more in the epilogue.  Each accumulator starts
+    as its first partial (no zero buffer is sent) and adds one partial per
+    rank it visits.  Epilogue: out[r] = cw[r] + ccw[r] after the ccw hop.
+
+    Returns (outputs, schedule, transfers) with schedule[i][r] =
+    (cw slice ID, ccw slice ID or None) and transfers as in
+    simulate_allgather_einsum_bidir (phase "epilogue" for the last hop).
+    """
+    n = len(a)
+    assert mode in RS_MODES and len(b) == n
+    k_cw, k_ccw = bidir_lengths(n)
+    cw_pairs, ccw_pairs = ring_pairs(n), reversed_ring_pairs(n)
+    lab_cw = _start_labels(n, cw_pairs, k_cw - 1)
+    lab_ccw = _start_labels(n, ccw_pairs, k_ccw) if k_ccw > 0 else [None] * n
+    acc_cw, acc_ccw = [None] * n, [None] * n
+    schedule, transfers = [], []
+    for i in range(k_cw):
+        do_ccw = i < k_ccw
+        schedule.append([(lab_cw[r], lab_ccw[r] if do_ccw else None) for r in range(n)])
+        for r in range(n):
+            p = _rs_partial(mode, a[r], b[r], n, lab_cw[r])
+            acc_cw[r] = p if i == 0 else acc_cw[r] + p
+            if do_ccw:
+                q = _rs_partial(mode, a[r], b[r], n, lab_ccw[r])
+                acc_ccw[r] = q if i == 0 else acc_ccw[r] + q
+        if i + 1 < k_cw:
+            transfers += [(i, "cw", s, d, lab_cw[s]) for s, d in cw_pairs]
+            acc_cw = collective_permute(acc_cw, cw_pairs)
+            lab_cw = collective_permute(lab_cw, cw_pairs)
+        if do_ccw:                                   # in the loop or the epilogue
+            phase = i if i + 1 < k_ccw else "epilogue"
+            transfers += [(phase, "ccw", s, d, lab_ccw[s]) for s, d in ccw_pairs]
+            acc_ccw = collective_permute(acc_ccw, ccw_pairs)
+            lab_ccw = collective_permute(lab_ccw, ccw_pairs)
+    assert lab_cw == list(range(n)), "cw accumulators not aligned at loop end"
+    if k_ccw > 0:
+        assert lab_ccw == list(range(n)), "ccw accumulators not aligned after the epilogue"
+        outs = [acc_cw[r] + acc_ccw[r] for r in range(n)]
+    else:
+        outs = acc_cw
+    return outs, schedule, transfers

@@ -129,3 +129,84 @@ def test_collective_permute_is_a_ring_shift():
     got = ring.collective_permute(list(range(n)), ring.ring_pairs(n))
     # rank r receives what rank r+1 held
     assert got == [(r + 1) % n for r in range(n)]
+
+
+# ---------------------------------------------------------------------------
+# Bidirectional transfer (Section 5.4.2 of the same page)
+# ---------------------------------------------------------------------------
+def _rs_tiny(n, mode):
+    rng = np.random.default_rng(321 + n)
+    if mode == "slice_lhs_rows":
+        a = [rng.integers(-3, 4, (2 * n, 5)).astype(float) for _ in range(n)]
+        b = [rng.integers(-3, 4, (5, 3)).astype(float) for _ in range(n)]
+    else:
+        a = [rng.integers(-3, 4, (3, 5)).astype(float) for _ in range(n)]
+        b = [rng.integers(-3, 4, (5, 2 * n)).astype(float) for _ in range(n)]
+    return a, b
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+@pytest.mark.parametrize("mode", ring.AG_MODES)
+def test_bidir_allgather_equals_monolithic_exact(n, mode):
+    looped, local = _tiny(n, mode)
+    outs, _, _ = ring.simulate_allgather_einsum_bidir(mode, looped, local)
+    ref = einsum.allgather_einsum(mode, looped, local)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o, r)
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+@pytest.mark.parametrize("mode", ring.RS_MODES)
+def test_bidir_reducescatter_equals_monolithic_exact(n, mode):
+    a, b = _rs_tiny(n, mode)
+    outs, _, _ = ring.simulate_einsum_reducescatter_bidir(mode, a, b)
+    ref = einsum.einsum_reducescatter(mode, a, b)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o, r)
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_bidir_halves_iterations_and_keeps_the_bytes(n):
+    """Two partial einsums per iteration: ceil(N/2) iterations; every rank
+    still sends N-1 shards, each to a ring neighbour, cw ones to r-1 and ccw
+    ones to r+1."""
+    looped, local = _tiny(n, "lhs_rows")
+    a, b = _rs_tiny(n, "slice_lhs_rows")
+    for sim, args in ((ring.simulate_allgather_einsum_bidir, ("lhs_rows", looped, local)),
+                      (ring.simulate_einsum_reducescatter_bidir, ("slice_lhs_rows", a, b))):
+        _, sched, transfers = sim(*args)
+        assert len(sched) == (n + 1) // 2
+        for r in range(n):
+            assert sum(1 for t in transfers if t[2] == r) == n - 1
+            assert sum(1 for t in transfers if t[3] == r) == n - 1
+        for phase, direction, src, dst, _ in transfers:
+            assert dst == ((src - 1) % n if direction == "cw" else (src + 1) % n)
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_bidir_every_shard_once(n):
+    """AllGather: each rank computes on every shard exactly once.
+    ReduceScatter: each slice gets exactly one partial from every rank."""
+    looped, local = _tiny(n, "rhs_cols")
+    _, sched, _ = ring.simulate_allgather_einsum_bidir("rhs_cols", looped, local)
+    for r in range(n):
+        seen = [s for row in sched for s in row[r] if s is not None]
+        assert sorted(seen) == list(range(n))
+    a, b = _rs_tiny(n, "slice_rhs_cols")
+    _, sched, _ = ring.simulate_einsum_reducescatter_bidir("slice_rhs_cols", a, b)
+    for s in range(n):
+        ranks = [r for row in sched for r in range(n) for t in row[r] if t == s]
+        assert sorted(ranks) == list(range(n))
+
+
+def test_bidir_2way_is_one_swap_each_way():
+    """N = 2: the prologue (AllGather) or epilogue (ReduceScatter) is the
+    only transfer, and the single iteration computes both shards."""
+    looped, local = _tiny(2, "lhs_rows")
+    _, sched, tr = ring.simulate_allgather_einsum_bidir("lhs_rows", looped, local)
+    assert sched == [[(0, 1), (1, 0)]]
+    assert [t[0] for t in tr] == ["prologue", "prologue"]
+    a, b = _rs_tiny(2, "slice_lhs_rows")
+    _, sched, tr = ring.simulate_einsum_reducescatter_bidir("slice_lhs_rows", a, b)
+    assert sched == [[(0, 1), (1, 0)]]
+    assert [t[0] for t in tr] == ["epilogue", "epilogue"]
