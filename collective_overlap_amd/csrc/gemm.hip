@@ -48,13 +48,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kOob = 0x40000000;
 
-// k-tile depth of the bf16 kernel (build-time tuning knob; 256x256 tiles need
-// 2 * (BM + BN) * BK * 2 <= 160 KB of LDS).
+// Pipeline shape of the bf16 kernel: k-tile depth and LDS stages (build-time
+// tuning knobs; 256x256 tiles need NS * (BM + BN) * BK * 2 <= 160 KB of LDS).
 #ifndef CCE_GEMM_BK
 #define CCE_GEMM_BK 64
 #endif
+#ifndef CCE_GEMM_NS
+#define CCE_GEMM_NS 2
+#endif
 constexpr int kBK = CCE_GEMM_BK;
-constexpr int kNS = 2;                     // LDS stages
+constexpr int kNS = CCE_GEMM_NS;
 // added to steer a load past num_records
 constexpr int64_t kMaxRsrcBytes = kOob - 256;
 
@@ -190,9 +193,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   constexpr int B_DMA = BN / (4 * RPI);
   constexpr int N_DMA = A_DMA + B_DMA;
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(KK % 2 == 0 && NS == 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+  static_assert(KK % 2 == 0 && NS >= 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  static_assert(N_DMA < 64, "vmcnt range");
+  static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
@@ -327,13 +330,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][i], fa[slot][j], acc[i][j], 0, 0, 0);
   };
 
-  // Pipeline: two LDS buffers; tile kt in buffer kt % 2.  Per k tile kt:
+  // Pipeline: NS LDS buffers; tile kt in buffer kt % NS.  Per k tile kt:
   //   kk = 0 .. KK-2: MFMA(step kk) | LDS reads of step kk+1
-  //   wait for this wave's loads, barrier
+  //   wait for tile kt+1's loads, barrier
   //   kk = KK-1:      MFMA | LDS reads of step 0 of tile kt+1
   // Tile kt's buffer is free after the barrier: its last fragments (step
   // KK-1) were read before it, and the barrier makes every wave's loads of
-  // tile kt+1 visible.  The loads of tile kt+2 into that buffer are spread
+  // tile kt+1 visible.  The loads of tile kt+NS into that buffer are spread
   // over two steps: the first half during step KK-1 of iteration kt, the
   // second half during step 0 of iteration kt+1, one instruction per
   // NMF / C MFMAs, so that the vector memory path sees a steady stream
@@ -346,9 +349,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   constexpr int C = (N_DMA + 1) / 2;         // loads per half
   const int KT = (a.K + BK - 1) / BK;
   if (KT > 0) {
-    gload(0, 0);
-    gload(1, BK);
-    wait_vmcnt<N_DMA>();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) gload(st, st * BK);
+    wait_vmcnt<(NS - 1) * N_DMA>();
     __syncthreads();
     forward(0, 0);
 #pragma unroll
@@ -356,10 +359,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   }
   int cur = 0;                  // buffer of tile kt
   for (int kt = 0; kt < KT; ++kt) {
-    const int nxt = cur ^ 1;
-    // Second half of tile kt+1's loads.  At kt = 0 this repeats loads of the
-    // prologue: the same bytes to the same place, first read after barrier 0.
-    const uint32_t kadd1 = kadd_of((kt + 1) * BK);
+    const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
+    const int prv = (cur == 0) ? NS - 1 : cur - 1;   // buffer of tile kt+NS-1
+    // Second half of tile kt+NS-1's loads.  At kt = 0 this repeats loads of
+    // the prologue: the same bytes to the same place, first read after
+    // barrier NS-2.
+    const uint32_t kadd1 = kadd_of((kt + NS - 1) * BK);
 #pragma unroll
     for (int kk = 0; kk + 1 < KK; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
@@ -369,14 +374,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
         if (q < FM + FN) fread_one(cur, kk + 1, (kk + 1) & 1, q);
 #pragma unroll
         for (int d = C; d < N_DMA; ++d)
-          if (kk == 0 && (d - C) * NMF / C == q) dma_one(nxt, kadd1, d);
+          if (kk == 0 && (d - C) * NMF / C == q) dma_one(prv, kadd1, d);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // The compiler does not order the global->LDS loads before the barrier
-    // by itself: wait for all of this wave's (tile kt+1's, and forwarded
-    // stores).
-    wait_vmcnt<0>();
+    // by itself: wait until tile kt+1's have landed.  The loads of tiles
+    // kt+2 .. kt+NS-1 ((NS-2) * N_DMA instructions) may stay in flight;
+    // forwarded stores issued after them only make the wait stricter.
+    wait_vmcnt<(NS - 2) * N_DMA>();
     __syncthreads();
     {
       const uint32_t kadd = kadd_of((kt + NS) * BK);
