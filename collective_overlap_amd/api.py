@@ -16,7 +16,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
+from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_BIDIRECTIONAL, CCE_FLAG_COPY_DMA,
+                   CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
                    CCE_FLAG_SERIAL,
                    AG_MODES, RS_MODES,
                    cce_mat, check, lib, ptr_array)
@@ -28,6 +29,7 @@ __all__ = [
     "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched", "cce_describe_plan",
     "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
+    "CCE_FLAG_BIDIRECTIONAL",
     "AG_MODES", "RS_MODES",
 ]
 
@@ -118,9 +120,17 @@ def cce_version() -> str:
     return lib().cce_version().decode()
 
 
-def cce_shard_schedule(n_ranks: int, kind: int) -> list[list[int]]:
+def cce_shard_schedule(n_ranks: int, kind: int) -> list[list]:
     """table[i][r]: shard ID rank r works on in iteration i (kind 0
-    AllGather, 1 ReduceScatter)."""
+    AllGather, 1 ReduceScatter); for the bidirectional kinds 2 / 3 a pair
+    (clockwise shard, counter-clockwise shard or None)."""
+    if kind in (2, 3):
+        iters = (n_ranks + 1) // 2
+        buf = (ctypes.c_int32 * (iters * n_ranks * 2))()
+        check(lib().cce_shard_schedule(n_ranks, kind, buf), "cce_shard_schedule")
+        cell = lambda v: None if v < 0 else v    # noqa: E731
+        return [[(buf[(i * n_ranks + r) * 2], cell(buf[(i * n_ranks + r) * 2 + 1]))
+                 for r in range(n_ranks)] for i in range(iters)]
     buf = (ctypes.c_int32 * (n_ranks * n_ranks))()
     check(lib().cce_shard_schedule(n_ranks, kind, buf), "cce_shard_schedule")
     return [[buf[i * n_ranks + r] for r in range(n_ranks)] for i in range(n_ranks)]

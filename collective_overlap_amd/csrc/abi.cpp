@@ -185,7 +185,8 @@ struct AgGeom {
   int64_t M = 0, N = 0, K = 0;          // per-iteration GEMM
   int64_t recv_bytes = 0;               // one receive buffer (packed)
   int64_t acc_ld = 0, acc_bytes = 0;    // case-2 fp32 accumulator
-  int64_t total = 0;
+  int64_t ccw_off = 0;                  // counter-clockwise receive buffers (bidirectional)
+  int64_t total = 0;                    // enough for every flag combination
 };
 
 cce_status ag_geometry(int n, int mode, cce_dtype in_t, cce_dtype out_t, const cce_mat& looped,
@@ -234,7 +235,9 @@ cce_status ag_geometry(int n, int mode, cce_dtype in_t, cce_dtype out_t, const c
     g.acc_ld = round8(out.cols);
     g.acc_bytes = align256(out.rows * g.acc_ld * 4);
   }
-  g.total = 2 * nn * g.recv_bytes + (g.case2_ws ? nn * g.acc_bytes : 0);
+  g.ccw_off = 2 * nn * g.recv_bytes + (g.case2_ws ? nn * g.acc_bytes : 0);
+  // The bidirectional form (case 1 only) adds two ccw receive buffers per rank.
+  g.total = g.ccw_off + (g.case2 ? 0 : 2 * nn * g.recv_bytes);
   return CCE_OK;
 }
 
@@ -250,6 +253,7 @@ struct RsGeom {
   int64_t h0 = 0, h1 = 0;         // half extents along the sliced dim
   int H = 2;                      // accumulator chains (halves) per shard
   int64_t acc_ld = 0, half_bytes = 0;
+  int64_t region = 0;             // one set of accumulators (cw); the ccw set follows
   int64_t total = 0;              // enough for every flag combination
 };
 
@@ -289,7 +293,10 @@ cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsG
   layout(s0, &ld2, &slot2);
   layout(g.shard, &ld1, &slot1);
   const int64_t total2 = 2LL * n * 2 * slot2, total1 = 2LL * n * slot1;
-  g.total = (n > 1) ? std::max(total1, total2) : 0;
+  g.region = std::max(total1, total2);
+  // The bidirectional form needs a second (counter-clockwise) set; with one
+  // rank there are no accumulators at all.
+  g.total = (n > 1) ? 2 * g.region : 0;
   if (fused) {
     g.h0 = g.shard;
     g.h1 = 0;
@@ -364,6 +371,9 @@ PtrLd ag_resolve(const AgCall& c, const BufRef& b) {
       return {c.ws + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes, c.lshape.cols};
     case B_CASE2:
       return {c.ws + 2LL * c.g.n * c.g.recv_bytes + r * c.g.acc_bytes, c.g.acc_ld};
+    case B_RECV_CCW:
+      return {c.ws + c.g.ccw_off + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes,
+              c.lshape.cols};
   }
   return {nullptr, 0};
 }
@@ -396,7 +406,7 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
     }
     // GEMM
     GemmLaunch L;
-    L.groups = plan.n;
+    L.groups = static_cast<int>(o.items.size());   // one group per item (rank, direction)
     L.M = c.g.M;
     L.N = c.g.N;
     L.K = c.g.K;
@@ -404,8 +414,9 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
     L.epi = o.epi;
     const bool last = (o.iter == plan.n - 1);
     L.gelu = c.gelu && (!c.g.case2 || last);
+    int gi = 0;
     for (const Item& it : o.items) {
-      const int r = it.rank;
+      const int r = gi++;
       const int64_t s_id = it.shard;
       const PtrLd held = ag_resolve(c, it.a);
       const PtrLd loc = ag_resolve(c, it.b);
@@ -487,6 +498,10 @@ PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
     case B_ACC:
       return {c.ws + ((static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.H + b.half) * c.g.half_bytes,
               c.g.acc_ld};
+    case B_ACC_CCW:
+      return {c.ws + c.g.region +
+                  ((static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.H + b.half) * c.g.half_bytes,
+              c.g.acc_ld};
   }
   return {nullptr, 0};
 }
@@ -501,6 +516,39 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       continue;
     }
     const int64_t ext = (o.half == 0) ? c.g.h0 : c.g.h1;   // extent along the sliced dim
+    if (o.kind == OP_SUM) {
+      // Align-and-sum of the bidirectional form: out = cw + ccw, one batched
+      // epilogue launch (two fp32 partials per rank, no bias, no dropout).
+      EpilogueLaunch E;
+      E.n = 2;
+      E.batch = static_cast<int>(o.items.size());
+      E.part_t = CCE_F32;
+      E.rows = rows_mode ? ext : c.g.other;
+      E.cols = rows_mode ? c.g.other : ext;
+      E.ld_part = c.g.acc_ld;
+      E.out_t = c.out_t;
+      E.ld_out = c.oshape.ld;
+      E.mcol0 = 0;
+      E.mld = E.cols;
+      int b = 0;
+      for (const Item& it : o.items) {
+        E.parts[2 * b] = rs_resolve(c, it.a).p;
+        E.parts[2 * b + 1] = rs_resolve(c, it.cin).p;
+        E.res[b] = nullptr;
+        E.out[b] = rs_resolve(c, it.c).p;
+        E.mask[b] = nullptr;
+        E.mrow0[b] = 0;
+        ++b;
+      }
+      if (E.rows == 0 || E.cols == 0) continue;
+      int slot;
+      CCE_TRY(prof_begin(ctx, compute, 3, o.iter, 0.0,
+                         static_cast<double>(E.rows) * E.cols * (8.0 + esize(c.out_t)) * E.batch,
+                         &slot));
+      CCE_TRY(launch_fused_epilogue(E, compute));
+      CCE_TRY(prof_end(ctx, compute, slot));
+      continue;
+    }
     if (o.kind == OP_COPY) {
       const int64_t bytes = (rows_mode ? ext * c.g.acc_ld : c.g.other * c.g.acc_ld) * 4;
       if (bytes == 0) continue;
@@ -514,7 +562,7 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       continue;
     }
     GemmLaunch L;
-    L.groups = plan.n;
+    L.groups = static_cast<int>(o.items.size());   // one group per item (rank, direction)
     L.K = c.g.K;
     L.in_t = c.in_t;
     L.epi = o.epi;
@@ -526,8 +574,9 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       L.M = c.g.other;
       L.N = ext;
     }
+    int gi = 0;
     for (const Item& it : o.items) {
-      const int r = it.rank;
+      const int r = gi++;
       const int64_t t = it.shard;
       const PtrLd A = rs_resolve(c, it.a), B = rs_resolve(c, it.b), D = rs_resolve(c, it.c);
       L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
@@ -651,14 +700,35 @@ cce_status cce_ctx_read_profile(cce_ctx* ctx, int max_records, cce_prof_record* 
 cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table) {
   clear_error();
   if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
-  if (kind != 0 && kind != 1) return fail(CCE_EINVAL, "kind must be 0 or 1");
+  if (kind < 0 || kind > 3) return fail(CCE_EINVAL, "kind must be 0, 1, 2 or 3");
   if (!table) return fail(CCE_EINVAL, "table is NULL");
+  if ((kind == 2 || kind == 3) && 2 * n_ranks > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   // The schedule the plans use: read it back from the built plan itself.
-  const Plan p = (kind == 0) ? build_allgather_plan(n_ranks, CCE_AG_LHS_ROWS, false, true)
-                             : build_reducescatter_plan(n_ranks, CCE_RS_SLICE_LHS_ROWS, false, true);
+  Plan p;
+  switch (kind) {
+    case 0: p = build_allgather_plan(n_ranks, CCE_AG_LHS_ROWS, false, true); break;
+    case 1: p = build_reducescatter_plan(n_ranks, CCE_RS_SLICE_LHS_ROWS, false, true); break;
+    case 2: p = build_allgather_plan_bidir(n_ranks, CCE_AG_LHS_ROWS, true, false); break;
+    default: p = build_reducescatter_plan_bidir(n_ranks, CCE_RS_SLICE_LHS_ROWS, false, true, false);
+  }
+  if (kind >= 2) {
+    const int iters = bidir_cw_len(n_ranks);
+    for (int k = 0; k < iters * n_ranks * 2; ++k) table[k] = -1;
+  }
   for (const Op& o : p.ops) {
     if (o.kind != OP_GEMM) continue;
-    for (const Item& it : o.items) table[o.iter * n_ranks + it.rank] = it.shard;
+    if (kind < 2) {
+      for (const Item& it : o.items) table[o.iter * n_ranks + it.rank] = it.shard;
+    } else {
+      // items: the n clockwise ones first, then (while it runs) the n
+      // counter-clockwise ones
+      for (size_t k = 0; k < o.items.size(); ++k) {
+        const Item& it = o.items[k];
+        const int d = k < static_cast<size_t>(n_ranks) ? 0 : 1;
+        table[(o.iter * n_ranks + it.rank) * 2 + d] = it.shard;
+      }
+    }
   }
   return CCE_OK;
 }
@@ -682,11 +752,17 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
                                        cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
+                CCE_FLAG_BIDIRECTIONAL))
     return fail(CCE_EINVAL, "unknown flags");
   if (!looped || !local || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   AgGeom g;
   CCE_TRY(ag_geometry(n_ranks, mode, in_t, out_t, looped_shard, &local_shape, out_shape, g));
+  const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
+  if (bidir && g.case2)
+    return fail(CCE_EUNSUPPORTED, "the bidirectional form takes the case-1 modes only");
+  if (bidir && 2 * n_ranks > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   const size_t ein = esize(in_t), eout = esize(out_t);
   const int64_t ls = span_bytes(looped_shard, ein), cs = span_bytes(local_shape, ein),
                 os = span_bytes(out_shape, eout);
@@ -714,7 +790,8 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
   DeviceGuard guard(ctx->device);
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
-  const Plan plan = build_allgather_plan(n_ranks, mode, g.case2_ws, serial, fused);
+  const Plan plan = bidir ? build_allgather_plan_bidir(n_ranks, mode, serial, fused)
+                          : build_allgather_plan(n_ranks, mode, g.case2_ws, serial, fused);
   CCE_TRY(ensure_events(ctx, plan.n_events));
   AgCall c{g, in_t, out_t, looped, looped_shard, local, local_shape, out, out_shape,
            static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0, copy_kind(flags)};
@@ -740,9 +817,13 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
                                            cce_stream stream) {
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
+                CCE_FLAG_BIDIRECTIONAL))
     return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
+  const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
+  if (bidir && 2 * n_ranks > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   RsGeom g;
@@ -786,7 +867,8 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
 
   DeviceGuard guard(ctx->device);
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
-  const Plan plan = build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
+  const Plan plan = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, g.h1 > 0, serial, fused)
+                          : build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
   CCE_TRY(ensure_events(ctx, plan.n_events));
   RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
            copy_kind(flags)};
@@ -1003,19 +1085,27 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
   clear_error();
   if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
   if (!dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
-  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE))
+  if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
+                CCE_FLAG_BIDIRECTIONAL))
     return fail(CCE_EINVAL, "unknown flags");
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
+  const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
+  if (bidir && 2 * n_ranks > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   Plan p;
   if (kind == 0) {
     if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
     const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
-    p = build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1, serial,
-                             fused);
+    if (bidir && case2)
+      return fail(CCE_EUNSUPPORTED, "the bidirectional form takes the case-1 modes only");
+    p = bidir ? build_allgather_plan_bidir(n_ranks, mode, serial, fused)
+              : build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1,
+                                     serial, fused);
   } else if (kind == 1) {
     if (mode != 0 && mode != 1) return fail(CCE_EINVAL, "bad ReduceScatter mode");
-    p = build_reducescatter_plan(n_ranks, mode, true, serial, fused);
+    p = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, true, serial, fused)
+              : build_reducescatter_plan(n_ranks, mode, true, serial, fused);
   } else {
     return fail(CCE_EINVAL, "kind must be 0 or 1");
   }

@@ -99,6 +99,8 @@ enum BufKind : uint8_t {
   B_CASE2 = 5,    // workspace fp32 accumulator (rank) AllGather case 2, bf16 out
   B_A = 6,        // caller's left factor (ReduceScatter)
   B_B = 7,        // caller's right factor (ReduceScatter)
+  B_RECV_CCW = 8, // workspace receive buffer of the counter-clockwise stream (rank, parity)
+  B_ACC_CCW = 9,  // workspace counter-clockwise accumulator (rank, parity, half)
 };
 
 struct BufRef {
@@ -118,7 +120,9 @@ struct Item {            // one rank's share of a GEMM or copy
   bool has_fwd = false;
 };
 
-enum OpKind : uint8_t { OP_GEMM = 0, OP_COPY = 1, OP_RECORD = 2, OP_WAIT = 3 };
+// OP_SUM: out = a + c-side input per item (the bidirectional ReduceScatter's
+// align-and-sum epilogue); reads a and cin, writes c.
+enum OpKind : uint8_t { OP_GEMM = 0, OP_COPY = 1, OP_RECORD = 2, OP_WAIT = 3, OP_SUM = 4 };
 enum StreamId : uint8_t { S_COMPUTE = 0, S_COPY = 1 };
 
 struct Op {
@@ -140,6 +144,7 @@ struct Plan {
   int n_events = 0;
   bool serial = false;
   bool fused = false;    // permutes fused into the GEMMs (no copy ops)
+  bool bidir = false;    // two-way ring: items of both directions per op
   std::vector<Op> ops;
 };
 
@@ -147,11 +152,28 @@ struct Plan {
 inline int ag_shard(int n, int r, int i) { return (r + i) % n; }
 inline int rs_slice(int n, int r, int i) { return (r + i + 1) % n; }
 
+// Bidirectional ring ([OV] 5.4.2): the clockwise stream (rank r sends to
+// r - 1) runs ceil(n/2) iterations, the counter-clockwise one (r sends to
+// r + 1) floor(n/2).  AllGather: the cw buffer starts with the own shard,
+// the ccw buffer with the shard of rank r - 1 (prologue permute).
+// ReduceScatter: the cw accumulator of a slice ends on its rank at loop end,
+// the ccw accumulator one rank short of it (one epilogue permute).
+inline int bidir_cw_len(int n) { return (n + 1) / 2; }
+inline int bidir_ccw_len(int n) { return n / 2; }
+inline int mod_n(int x, int n) { return ((x % n) + n) % n; }
+inline int ag_shard_cw(int n, int r, int i) { return mod_n(r + i, n); }
+inline int ag_shard_ccw(int n, int r, int i) { return mod_n(r - 1 - i, n); }
+inline int rs_slice_cw(int n, int r, int i) { return mod_n(r + i + 1 - bidir_cw_len(n), n); }
+inline int rs_slice_ccw(int n, int r, int i) { return mod_n(r - i + bidir_ccw_len(n), n); }
+
 // Build the plan of a looped call.  `case2_ws` selects the workspace fp32
 // accumulator for AllGather case 2 (bf16 output); `two_halves` is false when
 // the ReduceScatter shard has a single row/column (no second chain).
 Plan build_allgather_plan(int n, int mode, bool case2_ws, bool serial, bool fused = false);
 Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial, bool fused = false);
+// Bidirectional forms ([OV] 5.4.2).  AllGather: case 1 modes only.
+Plan build_allgather_plan_bidir(int n, int mode, bool serial, bool fused);
+Plan build_reducescatter_plan_bidir(int n, int mode, bool two_halves, bool serial, bool fused);
 
 std::string describe_plan(const Plan& p);
 

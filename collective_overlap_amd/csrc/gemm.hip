@@ -303,7 +303,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   auto forward = [&](int buf, int kt) {
     const int mine = fwd_a ? tn : tm;
     const int span = fwd_a ? a.tiles_n : a.tiles_m;
-    if (!(fwd_a || fwd_b) || kt % span != mine) return;
+    // Groups without a destination (a stream that has ended) forward nothing.
+    if (!(fwd_a || fwd_b) || fdst == nullptr || kt % span != mine) return;
     const char* s = smem + buf * STAGE + (fwd_a ? 0 : BM * ROWB);
     const int row0 = fwd_a ? m0 : n0;
     const int rows = fwd_a ? BM : BN;
@@ -457,9 +458,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
       // fused permute: forward the looped operand's k tile (once per row block)
       const int kt = k0 / BK;
       float* fd = reinterpret_cast<float*>(a.p.fwd[g]);
-      if (a.fwd == FWD_A && kt % a.tiles_n == tn && m < a.M && k < a.K)
+      if (a.fwd == FWD_A && fd != nullptr && kt % a.tiles_n == tn && m < a.M && k < a.K)
         *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(m) * a.ldfwd + k) = v;
-      if (a.fwd == FWD_B && kt % a.tiles_m == tm && n < a.N && k < a.K)
+      if (a.fwd == FWD_B && fd != nullptr && kt % a.tiles_m == tm && n < a.N && k < a.K)
         *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(n) * a.ldfwd + k) = w;
     }
     __syncthreads();

@@ -246,6 +246,277 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial, boo
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// Bidirectional transfer ([OV] Section 5.4.2): two partial einsums per
+// iteration, one per direction round the ring, in one GEMM launch (2n
+// groups), so the loop has ceil(n/2) iterations.  Every rank still sends
+// n-1 shards.  The AllGather's counter-clockwise buffer is filled by a
+// prologue permute before the loop; the ReduceScatter's counter-clockwise
+// accumulator takes one epilogue permute after its last partial, and an
+// align-and-sum adds the two accumulators of each shard.
+// ---------------------------------------------------------------------------
+Plan build_allgather_plan_bidir(int n, int mode, bool serial, bool fused) {
+  Plan p;
+  p.kind = 0;
+  p.n = n;
+  p.mode = mode;
+  p.serial = serial || fused;
+  p.fused = fused;
+  p.bidir = true;
+  serial = p.serial;
+  const int KC = bidir_cw_len(n), KW = bidir_ccw_len(n);
+  // events: 0 fork, 1 prologue arrival, 2+i gemm_done[i], 2+n+i arrive[i],
+  // 2+2n+i started[i]
+  p.n_events = 2 + 3 * n;
+  const int EV_FORK = 0, EV_PRO = 1;
+  auto ev_gemm = [&](int i) { return 2 + i; };
+  auto ev_arrive = [&](int i) { return 2 + n + i; };
+  auto ev_started = [&](int i) { return 2 + 2 * n + i; };
+  const StreamId cs = serial ? S_COMPUTE : S_COPY;
+  auto held_cw = [&](int r, int i) {
+    return i == 0 ? ref(B_LOOPED, r) : ref(B_RECV, r, i % 2);
+  };
+  auto held_ccw = [&](int r, int i) { return ref(B_RECV_CCW, r, i % 2); };
+  // The copy op of iteration i brings the shards of iteration i+1.
+  auto cw_copy = [&](int i) { return i + 1 < KC; };
+  auto ccw_copy = [&](int i) { return i + 1 < KW; };
+  // WAR: its destinations were last read by GEMM(i-1) -- the cw parity from
+  // iteration 2 on (GEMM(0) reads the caller's shard), the ccw parity from
+  // iteration 1 on (GEMM(0) reads the prologue's buffer).
+  auto copy_waits = [&](int i) { return (cw_copy(i) && i >= 2) || (ccw_copy(i) && i >= 1); };
+
+  if (!serial && n > 1) {
+    p.ops.push_back(rec(S_COMPUTE, EV_FORK));
+    p.ops.push_back(wait(S_COPY, EV_FORK));
+  }
+  if (KW > 0) {            // prologue: rank r's ccw buffer gets rank r-1's shard
+    Op c;
+    c.kind = OP_COPY;
+    c.stream = cs;
+    c.iter = -1;
+    for (int r = 0; r < n; ++r) {
+      Item it;
+      it.rank = r;
+      it.shard = ag_shard_ccw(n, r, 0);
+      it.a = ref(B_LOOPED, mod_n(r - 1, n));
+      it.c = ref(B_RECV_CCW, r, 0);
+      c.items.push_back(it);
+    }
+    p.ops.push_back(c);
+    if (!serial) p.ops.push_back(rec(S_COPY, EV_PRO));
+  }
+  for (int i = 0; i < KC; ++i) {
+    if (cw_copy(i) && !fused) {
+      if (!serial && copy_waits(i)) p.ops.push_back(wait(S_COPY, ev_gemm(i - 1)));
+      if (!serial) p.ops.push_back(rec(S_COPY, ev_started(i)));
+      Op c;
+      c.kind = OP_COPY;
+      c.stream = cs;
+      c.iter = i;
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = ag_shard_cw(n, r, i + 1);
+        it.a = held_cw(mod_n(r + 1, n), i);
+        it.c = ref(B_RECV, r, (i + 1) % 2);
+        c.items.push_back(it);
+      }
+      if (ccw_copy(i)) {
+        for (int r = 0; r < n; ++r) {
+          Item it;
+          it.rank = r;
+          it.shard = ag_shard_ccw(n, r, i + 1);
+          it.a = held_ccw(mod_n(r - 1, n), i);
+          it.c = ref(B_RECV_CCW, r, (i + 1) % 2);
+          c.items.push_back(it);
+        }
+      }
+      p.ops.push_back(c);
+      if (!serial) p.ops.push_back(rec(S_COPY, ev_arrive(i + 1)));
+    }
+    if (!serial) {
+      if (i == 0 && KW > 0) p.ops.push_back(wait(S_COMPUTE, EV_PRO));
+      if (i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i)));
+      if (cw_copy(i)) p.ops.push_back(hint_wait(S_COMPUTE, ev_started(i)));
+    }
+    Op g;
+    g.kind = OP_GEMM;
+    g.stream = S_COMPUTE;
+    g.iter = i;
+    g.epi = EPI_STORE;
+    g.final_store = true;
+    for (int r = 0; r < n; ++r) {
+      Item it;
+      it.rank = r;
+      it.shard = ag_shard_cw(n, r, i);
+      it.a = held_cw(r, i);
+      it.b = ref(B_LOCAL, r);
+      it.c = ref(B_OUT, r);
+      if (fused && cw_copy(i)) {
+        it.fwd = ref(B_RECV, mod_n(r - 1, n), (i + 1) % 2);
+        it.has_fwd = true;
+      }
+      g.items.push_back(it);
+    }
+    if (i < KW) {
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = ag_shard_ccw(n, r, i);
+        it.a = held_ccw(r, i);
+        it.b = ref(B_LOCAL, r);
+        it.c = ref(B_OUT, r);
+        if (fused && ccw_copy(i)) {
+          it.fwd = ref(B_RECV_CCW, mod_n(r + 1, n), (i + 1) % 2);
+          it.has_fwd = true;
+        }
+        g.items.push_back(it);
+      }
+    }
+    p.ops.push_back(g);
+    if (!serial && i + 1 < KC && copy_waits(i + 1)) p.ops.push_back(rec(S_COMPUTE, ev_gemm(i)));
+  }
+  return p;
+}
+
+Plan build_reducescatter_plan_bidir(int n, int mode, bool two_halves, bool serial, bool fused) {
+  Plan p;
+  p.kind = 1;
+  p.n = n;
+  p.mode = mode;
+  p.serial = serial || fused;
+  p.fused = fused;
+  p.bidir = true;
+  serial = p.serial;
+  const int KC = bidir_cw_len(n), KW = bidir_ccw_len(n);
+  const int H = (two_halves && !fused) ? 2 : 1;
+  p.n_events = 2 + 6 * n;
+  auto ev_gemm = [&](int i, int h) { return 2 + 2 * i + h; };
+  auto ev_arrive = [&](int i, int h) { return 2 + 2 * n + 2 * i + h; };
+  auto ev_started = [&](int i, int h) { return 2 + 4 * n + 2 * i + h; };
+  const StreamId cs = serial ? S_COMPUTE : S_COPY;
+  // After GEMM(i, h): the cw accumulators move on unless the chain ended;
+  // the ccw ones move after every partial, the last move being the epilogue
+  // permute that brings them to the rank of their slice.
+  auto cw_moves = [&](int i) { return i + 1 < KC; };
+  auto ccw_moves = [&](int i) { return i < KW; };
+  auto copy_exists = [&](int i) { return cw_moves(i) || ccw_moves(i); };
+  auto prev_copy = [&](int i, int h, int* pi, int* ph) {
+    if (h == 1) { *pi = i; *ph = 0; } else { *pi = i - 1; *ph = H - 1; }
+    return *pi >= 0 && copy_exists(*pi);
+  };
+  const bool only_cw = (KW == 0);   // n == 1: the single GEMM writes the output
+
+  for (int i = 0; i < KC; ++i) {
+    const bool last_cw = (i == KC - 1);
+    for (int h = 0; h < H; ++h) {
+      if (!serial && i >= 1) p.ops.push_back(wait(S_COMPUTE, ev_arrive(i, h)));
+      int pi, ph;
+      if (!serial && prev_copy(i, h, &pi, &ph)) p.ops.push_back(hint_wait(S_COMPUTE, ev_started(pi, ph)));
+      Op g;
+      g.kind = OP_GEMM;
+      g.stream = S_COMPUTE;
+      g.iter = i;
+      g.half = h;
+      g.epi = (i == 0) ? EPI_STORE : EPI_ACCUM;
+      g.final_store = only_cw;
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = rs_slice_cw(n, r, i);
+        it.a = ref(B_A, r);
+        it.b = ref(B_B, r);
+        const BufRef acc = ref(B_ACC, r, i % 2, h);
+        if (only_cw) it.c = ref(B_OUT, r, 0, h);
+        else if (fused && !last_cw) it.c = ref(B_ACC, mod_n(r - 1, n), (i + 1) % 2, h);
+        else it.c = acc;
+        if (i > 0) {
+          it.cin = acc;
+          it.has_cin = true;
+        }
+        g.items.push_back(it);
+      }
+      if (i < KW) {
+        for (int r = 0; r < n; ++r) {
+          Item it;
+          it.rank = r;
+          it.shard = rs_slice_ccw(n, r, i);
+          it.a = ref(B_A, r);
+          it.b = ref(B_B, r);
+          const BufRef acc = ref(B_ACC_CCW, r, i % 2, h);
+          it.c = fused ? ref(B_ACC_CCW, mod_n(r + 1, n), (i + 1) % 2, h) : acc;
+          if (i > 0) {
+            it.cin = acc;
+            it.has_cin = true;
+          }
+          g.items.push_back(it);
+        }
+      }
+      p.ops.push_back(g);
+      if (copy_exists(i) && !fused) {
+        if (!serial) {
+          p.ops.push_back(rec(S_COMPUTE, ev_gemm(i, h)));
+          p.ops.push_back(wait(S_COPY, ev_gemm(i, h)));
+          p.ops.push_back(rec(S_COPY, ev_started(i, h)));
+        }
+        Op c;
+        c.kind = OP_COPY;
+        c.stream = cs;
+        c.iter = i;
+        c.half = h;
+        if (cw_moves(i)) {
+          for (int r = 0; r < n; ++r) {
+            Item it;
+            it.rank = r;
+            it.shard = rs_slice_cw(n, mod_n(r + 1, n), i);
+            it.a = ref(B_ACC, mod_n(r + 1, n), i % 2, h);
+            it.c = ref(B_ACC, r, (i + 1) % 2, h);
+            c.items.push_back(it);
+          }
+        }
+        if (ccw_moves(i)) {
+          for (int r = 0; r < n; ++r) {
+            Item it;
+            it.rank = r;
+            it.shard = rs_slice_ccw(n, mod_n(r - 1, n), i);
+            it.a = ref(B_ACC_CCW, mod_n(r - 1, n), i % 2, h);
+            it.c = ref(B_ACC_CCW, r, (i + 1) % 2, h);
+            c.items.push_back(it);
+          }
+        }
+        p.ops.push_back(c);
+        if (!serial) p.ops.push_back(rec(S_COPY, ev_arrive(i + 1, h)));
+      }
+    }
+  }
+  // Align-and-sum: out[r] = cw[r] + ccw[r] (the ccw accumulator arrived with
+  // the epilogue permute of iteration KW-1).
+  if (!only_cw) {
+    for (int h = 0; h < H; ++h) {
+      // (With n odd, GEMM(KW, h) already waited for this arrival.)
+      if (!serial && KW == KC) p.ops.push_back(wait(S_COMPUTE, ev_arrive(KW, h)));
+      Op sm;
+      sm.kind = OP_SUM;
+      sm.stream = S_COMPUTE;
+      sm.iter = KC;
+      sm.half = h;
+      sm.final_store = true;
+      for (int r = 0; r < n; ++r) {
+        Item it;
+        it.rank = r;
+        it.shard = r;
+        it.a = ref(B_ACC, r, (KC - 1) % 2, h);
+        it.cin = ref(B_ACC_CCW, r, KW % 2, h);
+        it.has_cin = true;
+        it.c = ref(B_OUT, r, 0, h);
+        sm.items.push_back(it);
+      }
+      p.ops.push_back(sm);
+    }
+  }
+  return p;
+}
+
 namespace {
 
 std::string bufname(const BufRef& b) {
@@ -259,6 +530,8 @@ std::string bufname(const BufRef& b) {
     case B_CASE2: std::snprintf(s, sizeof s, "c2acc%d", b.rank); break;
     case B_A: std::snprintf(s, sizeof s, "a%d", b.rank); break;
     case B_B: std::snprintf(s, sizeof s, "b%d", b.rank); break;
+    case B_RECV_CCW: std::snprintf(s, sizeof s, "recvccw%d.p%d", b.rank, b.parity); break;
+    case B_ACC_CCW: std::snprintf(s, sizeof s, "accccw%d.p%d.h%d", b.rank, b.parity, b.half); break;
     default: std::snprintf(s, sizeof s, "?%d", b.rank); break;
   }
   return s;
@@ -281,14 +554,20 @@ std::string describe_plan(const Plan& p) {
         out += line;
         break;
       case OP_GEMM:
-      case OP_COPY: {
-        std::snprintf(line, sizeof line, "%s it=%d h=%d epi=%d final=%d",
-                      o.kind == OP_GEMM ? "gemm" : "copy", o.iter, o.half, o.epi,
-                      o.final_store ? 1 : 0);
+      case OP_COPY:
+      case OP_SUM: {
+        const char* kname = o.kind == OP_GEMM ? "gemm" : (o.kind == OP_COPY ? "copy" : "sum");
+        std::snprintf(line, sizeof line, "%s it=%d h=%d epi=%d final=%d", kname, o.iter, o.half,
+                      o.epi, o.final_store ? 1 : 0);
         out += line;
+        // AllGather case 1 writes the slice of its shard: name it, so that
+        // two items writing different slices of one output do not collide.
+        const bool slice_out = p.kind == 0 && o.kind == OP_GEMM &&
+                               (p.mode == CCE_AG_LHS_ROWS || p.mode == CCE_AG_RHS_COLS);
         std::string rd, wr, sh, xs;
         for (const Item& it : o.items) {
           std::string ir = bufname(it.a), iw = bufname(it.c);
+          if (slice_out && it.c.kind == B_OUT) iw += ".s" + std::to_string(it.shard);
           if (o.kind == OP_GEMM) ir += "+" + bufname(it.b);
           if (it.has_cin) ir += "+" + bufname(it.cin);
           if (it.has_fwd) iw += "+" + bufname(it.fwd);

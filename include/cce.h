@@ -90,6 +90,20 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
                                   ReduceScatter: the GEMM's accumulate epilogue
                                   stores into the next rank's accumulator.  Same
                                   results, bit for bit; no extra reads. */
+#define CCE_FLAG_BIDIRECTIONAL 0x10u /* [OV] Section 5.4.2: two looped buffers
+                                  (AllGather) or accumulators (ReduceScatter)
+                                  per rank travel the ring in opposite
+                                  directions and each iteration computes both
+                                  partial einsums in one launch, so the loop
+                                  runs ceil(n/2) iterations; each rank still
+                                  sends n-1 shards.  The AllGather fills its
+                                  second buffer with a prologue transfer; the
+                                  ReduceScatter ends with an epilogue transfer
+                                  and an align-and-sum of the two
+                                  accumulators.  AllGather case 1 modes and
+                                  both ReduceScatter modes; n_ranks <= 32.
+                                  Combines with SERIAL, GELU, COPY_DMA and
+                                  FUSED_PERMUTE. */
 
 /* Status text; never NULL. */
 const char* cce_status_string(cce_status s);
@@ -113,7 +127,8 @@ cce_status cce_ctx_destroy(cce_ctx* ctx);
  * returns up to max_records records in enqueue order, and clears the list.
  * Enabling (enable != 0) also clears it.  Host memory only; no allocation on
  * the device.
- *   kind: 0 GEMM launch, 1 permute step (copies), 2 fused epilogue launch
+ *   kind: 0 GEMM launch, 1 permute step (copies), 2 fused epilogue launch,
+ *         3 align-and-sum launch (bidirectional ReduceScatter)
  *   iter: loop iteration (GEMM, copies), -1 otherwise
  *   ms:   event-to-event time on the device
  *   flops: 2*M*N*K summed over the launch's groups (GEMM), else 0
@@ -138,6 +153,11 @@ cce_status cce_ctx_read_profile(cce_ctx* ctx, int max_records, cce_prof_record* 
  * end).  Transfers always go from rank r to rank (r - 1) mod n, the
  * {source, destination} pairs {0, N-1}, {1, 0}, ..., {N-1, N-2}.
  * table is host memory of n_ranks * n_ranks int32.  Host-only; no device.
+ * kind 2 / 3: the bidirectional forms (CCE_FLAG_BIDIRECTIONAL) of the
+ * AllGather / ReduceScatter loop: table[(i * n_ranks + r) * 2 + d] is the
+ * shard of rank r in iteration i for direction d (0: clockwise, sent to
+ * r - 1; 1: counter-clockwise, sent to r + 1), -1 when that stream has
+ * ended; table holds ceil(n_ranks / 2) * n_ranks * 2 int32; n_ranks <= 32.
  * ---------------------------------------------------------------------- */
 cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
 
@@ -169,10 +189,11 @@ cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
  * out_t: CCE_BF16 or CCE_F32 (round to nearest even on the final store).
  * Case 2 accumulates across iterations in fp32 (in `out` itself when out_t is
  * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU,
- * CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE.
+ * CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_BIDIRECTIONAL (case 1).
  * workspace: device memory of at least the size the query returns (two
- * receive buffers per rank, plus the fp32 accumulators of case 2 with a bf16
- * output); its contents on entry do not matter.
+ * receive buffers per rank and direction, plus the fp32 accumulators of
+ * case 2 with a bf16 output; the size covers every flag combination); its
+ * contents on entry do not matter.
  * ---------------------------------------------------------------------- */
 typedef enum cce_ag_mode {
   CCE_AG_LHS_ROWS = 0,
@@ -210,11 +231,15 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
  * accumulator is split into two halves that form two interleaved chains, so
  * the transfer of one half overlaps the GEMM of the other.  For every element
  * of out[s] the sum runs over the partials of ranks s-1, s-2, ..., s+1, s
- * (mod n) in that order, in fp32, whatever the flags.
+ * (mod n) in that order, in fp32, whatever the flags -- except with
+ * CCE_FLAG_BIDIRECTIONAL, where out[s] = cw + ccw: cw sums the partials of
+ * ranks s+c-1, ..., s+1, s and ccw those of ranks s-w, ..., s-1 (c =
+ * ceil(n/2), w = floor(n/2), indices mod n), each chain in that order.
  * in_t: CCE_BF16 or CCE_F32; acc_t: CCE_F32 only; out_t: CCE_F32 or CCE_BF16.
- * flags: CCE_FLAG_SERIAL, CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE.
- * workspace: two fp32 accumulators per rank (the query returns the size,
- * which covers every flag combination).
+ * flags: CCE_FLAG_SERIAL, CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE,
+ * CCE_FLAG_BIDIRECTIONAL.
+ * workspace: two fp32 accumulators per rank and direction (the query
+ * returns the size, which covers every flag combination).
  * ---------------------------------------------------------------------- */
 typedef enum cce_rs_mode { CCE_RS_SLICE_LHS_ROWS = 0, CCE_RS_SLICE_RHS_COLS = 1 } cce_rs_mode;
 

@@ -39,7 +39,7 @@ def parse(text: str) -> list[POp]:
             k, v = p.split("=", 1)
             attrs[k] = v
         op = POp(len(ops), stream, kind, attrs)
-        if kind in ("gemm", "copy"):
+        if kind in ("gemm", "copy", "sum"):
             op.reads = set(attrs["r"].split(","))
             op.writes = set(attrs["w"].split(","))
             op.items = [(set(x.split(">")[0].split("+")), set(x.split(">")[1].split("+")))
@@ -126,7 +126,7 @@ def check(text: str) -> list[str]:
     succ, hb_problems = happens_before(ops, hints=False)
     problems += hb_problems
     reach = _reach(succ)
-    acc = [o for o in ops if o.kind in ("gemm", "copy", "caller")]
+    acc = [o for o in ops if o.kind in ("gemm", "copy", "sum", "caller")]
     for i, x in enumerate(acc):
         for y in acc[i + 1:]:
             conflict = (x.writes & (y.reads | y.writes)) or (y.writes & x.reads)

@@ -183,8 +183,9 @@ def _ws_ag(cce, n, mode, in_t, out_t, looped, out):
 
 def test_allgather_workspace_sizes(cce):
     # case 1, bf16, rhs_cols: two receive buffers of [512, 256] bf16 per rank
+    # and direction (the size covers the bidirectional form)
     s, nb = _ws_ag(cce, 4, 1, 1, 1, (512, 256, 256), (64, 2048, 2048))
-    assert s == 0 and nb == 2 * 4 * 512 * 256 * 2
+    assert s == 0 and nb == 2 * 2 * 4 * 512 * 256 * 2
     # case 2 with bf16 output adds an fp32 accumulator per rank
     s, nb2 = _ws_ag(cce, 4, 2, 1, 1, (64, 256, 256), (64, 512, 512))
     assert s == 0 and nb2 == 2 * 4 * 64 * 256 * 2 + 4 * 64 * 512 * 4
@@ -214,7 +215,7 @@ def test_reducescatter_workspace_and_validation(cce):
     nb = ctypes.c_size_t()
     assert cce.cce_looped_einsum_reducescatter_workspace(
         8, 0, 0, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 0
-    assert nb.value == 2 * 8 * 2 * 1024 * 4096 * 4
+    assert nb.value == 2 * 2 * 8 * 2 * 1024 * 4096 * 4    # two chains, two directions
     # bf16 travelling accumulator is not offered
     assert cce.cce_looped_einsum_reducescatter_workspace(
         8, 0, 1, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 2
@@ -259,7 +260,7 @@ def test_fused_allgather_forwards_what_the_ring_moves(n):
     _, sched, transfers = ring.simulate_allgather_einsum("lhs_rows", looped, looped)
     for o in ops:
         i = int(o.attrs["it"])
-        fwds = [w - {f"out{r}.h0"} for r, (_, w) in enumerate(o.items)]
+        fwds = [{x for x in w if not x.startswith("out")} for _, w in o.items]
         if i == n - 1:
             assert all(not f for f in fwds)
             continue
@@ -283,6 +284,113 @@ def test_fused_reducescatter_sends_accumulators_down_the_ring():
 def test_checker_flags_intra_launch_conflict():
     """Plant a forward into the buffer another rank reads in the same launch."""
     lines = _plan(0, 4, 0, 1, FUSED).strip().splitlines()
-    bad = lines[1].replace(">out0.h0+recv3.p0", ">out0.h0+recv1.p1")
+    bad = lines[1].replace(">out0.h0.s1+recv3.p0", ">out0.h0.s1+recv1.p1")
     assert bad != lines[1]
     assert plan_check.check("\n".join([lines[0], bad] + lines[2:]))
+
+
+# ---------------------------------------------------------------------------
+# Bidirectional transfer (Wang et al. ASPLOS'23, Section 5.4.2)
+# ---------------------------------------------------------------------------
+BIDIR = 0x10
+
+
+def _items(op):
+    """(rank, shard) of each item of a gemm / copy / sum op, in order."""
+    return [tuple(int(v) for v in p.split(":")) for p in op.attrs["shard"].split(",")]
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)) + [31, 32])
+def test_bidir_shard_schedule_is_the_oracles(n):
+    from collective_overlap_amd import cce_shard_schedule
+    looped = [np.zeros((1, 1)) for _ in range(n)]
+    _, ag, _ = ring.simulate_allgather_einsum_bidir("lhs_rows", looped, looped)
+    assert cce_shard_schedule(n, 2) == ag
+    a = [np.zeros((n, 1)) for _ in range(n)]
+    b = [np.zeros((1, 1)) for _ in range(n)]
+    _, rs, _ = ring.simulate_einsum_reducescatter_bidir("slice_lhs_rows", a, b)
+    assert cce_shard_schedule(n, 3) == rs
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 16, 32])
+@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("extra", [0, 1, 8])
+def test_bidir_plans_race_free(n, kind, mode, extra):
+    text = _plan(kind, n, mode, 1, BIDIR | extra)
+    assert plan_check.check(text) == []
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("flags", [BIDIR, BIDIR | 8])
+def test_bidir_allgather_plan_matches_simulated_loop(n, flags):
+    """GEMM items follow the oracle's two-way schedule; the transfers (copies,
+    or forwards in the fused form) are the oracle's, prologue included."""
+    ops = plan_check.parse(_plan(0, n, 0, 1, flags))
+    looped = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, transfers = ring.simulate_allgather_einsum_bidir("lhs_rows", looped, looped)
+    gemms = [o for o in ops if o.kind == "gemm"]
+    assert len(gemms) == (n + 1) // 2
+    for o in gemms:
+        i = int(o.attrs["it"])
+        want = [(r, sched[i][r][0]) for r in range(n)]
+        want += [(r, sched[i][r][1]) for r in range(n) if sched[i][r][1] is not None]
+        assert _items(o) == want
+    # every (destination, shard) the oracle moves appears once: as a copy
+    # item, or (fused form) as the forward destination of a GEMM item
+    moved = sorted((t[3], t[4]) for t in transfers)
+    got = [(r, sid) for o in ops if o.kind == "copy" for r, sid in _items(o)]
+    for o in gemms:
+        for (_, w), (_, sid) in zip(o.items, _items(o)):
+            for x in w:
+                m = re.match(r"recv(?:ccw)?(\d+)\.p", x)
+                if m:
+                    got.append((int(m.group(1)), sid))
+    assert sorted(got) == moved
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+def test_bidir_reducescatter_plan_matches_simulated_loop(n):
+    ops = plan_check.parse(_plan(1, n, 0, 1, BIDIR))
+    a = [np.zeros((n, 1)) for _ in range(n)]
+    b = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, transfers = ring.simulate_einsum_reducescatter_bidir("slice_lhs_rows", a, b)
+    gemms = [o for o in ops if o.kind == "gemm"]
+    assert len(gemms) == 2 * ((n + 1) // 2)                 # two chains (halves)
+    for o in gemms:
+        i = int(o.attrs["it"])
+        want = [(r, sched[i][r][0]) for r in range(n)]
+        want += [(r, sched[i][r][1]) for r in range(n) if sched[i][r][1] is not None]
+        assert _items(o) == want
+    copies = [o for o in ops if o.kind == "copy"]
+    got = sorted((r, sid) for o in copies if int(o.attrs["h"]) == 0 for r, sid in _items(o))
+    assert got == sorted((t[3], t[4]) for t in transfers)
+    sums = [o for o in ops if o.kind == "sum"]
+    assert len(sums) == (2 if n > 1 else 0)
+
+
+@pytest.mark.parametrize("kind,mode,n", [(0, 0, 4), (0, 1, 5), (1, 0, 4), (1, 1, 5), (1, 0, 2)])
+def test_bidir_checker_flags_every_dropped_wait(kind, mode, n):
+    lines = _plan(kind, n, mode, 1, BIDIR).strip().splitlines()
+    waits = [i for i, l in enumerate(lines) if " wait " in l and "hint=1" not in l]
+    assert waits
+    for w in waits:
+        broken = "\n".join(l for i, l in enumerate(lines) if i != w)
+        assert plan_check.check(broken), f"dropping line {w} went unnoticed"
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_bidir_copies_overlap_gemms(n):
+    text = _plan(0, n, 1, 1, BIDIR)
+    for i in range((n + 1) // 2 - 1):
+        assert plan_check.concurrent(text, _is("copy", i), _is("gemm", i))
+    text = _plan(1, n, 0, 1, BIDIR)
+    for i in range((n + 1) // 2):
+        assert plan_check.concurrent(text, _is("copy", i, 0), _is("gemm", i, 1))
+
+
+def test_bidir_rejects_case2_and_too_many_ranks(cce):
+    from collective_overlap_amd._lib import CceError
+    with pytest.raises(CceError):
+        _plan(0, 4, 2, 1, BIDIR)
+    with pytest.raises(CceError):
+        _plan(1, 33, 0, 1, BIDIR)
