@@ -368,6 +368,9 @@ def main(argv=None):
     ap.add_argument("--permute", choices=("fused", "stream"), default="fused",
                     help="fused: each partial GEMM sends the data itself; stream: async "
                          "copies on a second stream ordered by events")
+    ap.add_argument("--bidir", action="store_true",
+                    help="bidirectional ring: two partial einsums per iteration, one per "
+                         "direction, ceil(n/2) iterations")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -402,7 +405,8 @@ def main(argv=None):
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     log("inputs ready; warmup")
-    main_flags = cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0
+    bid = cce.CCE_FLAG_BIDIRECTIONAL if a.bidir else 0
+    main_flags = (cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0) | bid
     for _ in range(a.warmup):
         step.run(ctx, main_flags)
     log(f"timed region (permute {a.permute})")
@@ -431,7 +435,7 @@ def main(argv=None):
     if not a.no_serial and has_permute:
         log("timed regions: copies on a second stream; the same kernels serialised")
         res = {}
-        for name, fl in (("stream", 0), ("serial", cce.CCE_FLAG_SERIAL)):
+        for name, fl in (("stream", bid), ("serial", cce.CCE_FLAG_SERIAL | bid)):
             for _ in range(max(1, a.warmup // 2)):
                 step.run(ctx, fl)
             w, r = timed(step, ctx, a.steps, fl, profile=True)
@@ -439,8 +443,8 @@ def main(argv=None):
         fused_ms = ms_per_step if a.permute == "fused" else None
         if fused_ms is None:
             for _ in range(max(1, a.warmup // 2)):
-                step.run(ctx, cce.CCE_FLAG_FUSED_PERMUTE)
-            w, _ = timed(step, ctx, a.steps, cce.CCE_FLAG_FUSED_PERMUTE, profile=False)
+                step.run(ctx, cce.CCE_FLAG_FUSED_PERMUTE | bid)
+            w, _ = timed(step, ctx, a.steps, cce.CCE_FLAG_FUSED_PERMUTE | bid, profile=False)
             fused_ms = w / a.steps * 1e3
         s_ms, srecs = res["serial"]
         st_ms = res["stream"][0]
@@ -486,7 +490,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": step.dtype,
         "data": "synthetic (seeded torch generators; no dataset)",
-        "config": dict(step.config(), permute=a.permute),
+        "config": dict(step.config(), permute=a.permute,
+                       transfer="bidirectional" if a.bidir else "one-way"),
         "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),
         "roofline": roof,
         "cpu_baseline": cpu,
