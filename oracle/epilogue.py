@@ -21,7 +21,11 @@ caller's comparison.
 
 Parity pins (tests/test_oracle_epilogue.py): a per-element pure-Python loop on
 small shapes, p = 0 (exactly sum + bias + residual), p = 1 (exactly the
-residual), linearity in the partials, and the N = 1 case.
+residual), linearity in the partials, and the N = 1 case.  The step-by-step
+FusedAllReduce (ReduceScatter, epilogue per slice, AllGather) is pinned to the
+whole-tensor epilogue of the AllReduce sum (the collective identity
+AllReduce = ReduceScatter + AllGather, with the pointwise tail commuting with
+the row split), bit for bit in float64, for ragged row splits as well.
 """
 
 from __future__ import annotations
@@ -55,3 +59,36 @@ def fused_reduce_epilogue(partials, bias, residual, p: float, seed: int,
     if residual is not None:
         d = d + np.asarray(residual, dtype=np.float64)
     return d, keep
+
+
+def fused_allreduce(partials, bias, residual, p: float, seed: int, offset: int,
+                    col0: int = 0, mask_ld: int | None = None):
+    """CoCoNet's FusedAllReduce across n ranks, step by step ([CC], fused
+    collective communication): the AllReduce is split into a ReduceScatter
+    and an AllGather, and the bias add, dropout and residual add run on each
+    rank's reduced slice between the two.
+
+    partials[r]: rank r's [rows, cols] partial.  Rank r reduces row block r
+    (numpy's array_split of the rows into n nearly equal blocks: the
+    collective's shard r) over all ranks in rank order, applies the epilogue
+    with the block's global row base (so the mask is the one of the whole
+    tensor), and the AllGather concatenates the blocks in rank order for
+    every rank.  Returns (outputs: one float64 array per rank, keep mask)."""
+    n = len(partials)
+    parts = [np.asarray(x, dtype=np.float64) for x in partials]
+    rows, cols = parts[0].shape
+    bounds = np.cumsum([0] + [len(b) for b in np.array_split(np.arange(rows), n)])
+    res = None if residual is None else np.asarray(residual, dtype=np.float64)
+    blocks, keeps = [], []
+    for r in range(n):                                     # ReduceScatter + epilogue
+        lo, hi = bounds[r], bounds[r + 1]
+        acc = parts[0][lo:hi].copy()
+        for q in range(1, n):
+            acc = acc + parts[q][lo:hi]
+        out_r, keep_r = fused_reduce_epilogue(
+            [acc], bias, None if res is None else res[lo:hi], p, seed, offset,
+            row0=lo, col0=col0, mask_ld=mask_ld if mask_ld is not None else col0 + cols)
+        blocks.append(out_r)
+        keeps.append(keep_r)
+    full = np.concatenate(blocks, axis=0)                  # AllGather
+    return [full.copy() for _ in range(n)], np.concatenate(keeps, axis=0)

@@ -69,3 +69,19 @@ def test_linear_in_partials_and_kept_scale():
     s = parts[0] + parts[1]
     np.testing.assert_allclose(y1[k1], s[k1] / 0.75, rtol=1e-15)
     assert np.all(y1[~k1] == 0)
+
+
+@pytest.mark.parametrize("n,rows,cols", [(1, 5, 7), (2, 6, 9), (4, 10, 16), (8, 8, 12), (3, 7, 5)])
+@pytest.mark.parametrize("p", [0.0, 0.1, 1.0])
+def test_fused_allreduce_is_epilogue_of_allreduce(n, rows, cols, p):
+    """ReduceScatter -> epilogue on each rank's slice -> AllGather gives the
+    whole-tensor epilogue of the AllReduce sum on every rank, bit for bit."""
+    rng = np.random.default_rng(n * 100 + rows)
+    parts = [rng.standard_normal((rows, cols)) for _ in range(n)]
+    bias, res = rng.standard_normal(cols), rng.standard_normal((rows, cols))
+    outs, keep = epilogue.fused_allreduce(parts, bias, res, p, 9, 2, col0=3, mask_ld=cols + 5)
+    whole, wkeep = epilogue.fused_reduce_epilogue(parts, bias, res, p, 9, 2, row0=0, col0=3,
+                                             mask_ld=cols + 5)
+    assert np.array_equal(keep, wkeep)
+    for o in outs:
+        assert np.array_equal(o, whole)
