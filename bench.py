@@ -142,10 +142,18 @@ class AttnOutProj:
         return {"workload": self.name, "n_ranks": self.n, "tokens": self.M, "in_shard": self.K,
                 "hidden": self.N, "p_drop": self.p, "global_batch": self.M}
 
+    def use_allreduce(self):
+        """FusedAllReduce form: the result lands on all 8 ranks (8 replicas)."""
+        import torch
+        self.outs = [self.out] + [torch.empty_like(self.out) for _ in range(self.n - 1)]
+
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
         cce.cce_grouped_gemm(ctx, self.IN, self.Wt, self.P)
-        cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, self.p, 0, 0)
+        if getattr(self, "outs", None):
+            cce.cce_fused_allreduce_epilogue(ctx, self.P, self.b, self.R, self.outs, self.p, 0, 0)
+        else:
+            cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, self.p, 0, 0)
 
     def oracle_sample(self, t=16):
         import numpy as np
@@ -371,6 +379,8 @@ def main(argv=None):
     ap.add_argument("--bidir", action="store_true",
                     help="bidirectional ring: two partial einsums per iteration, one per "
                          "direction, ceil(n/2) iterations")
+    ap.add_argument("--allreduce", action="store_true",
+                    help="attn_outproj_n8: FusedAllReduce epilogue, the result on every rank")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -402,6 +412,10 @@ def main(argv=None):
         return 0
     log(f"device {torch.cuda.get_device_name(0)}; workload {a.workload}")
     step = WORKLOADS[a.workload](dev)
+    if a.allreduce:
+        if not hasattr(step, "use_allreduce"):
+            raise SystemExit("--allreduce applies to attn_outproj_n8 only")
+        step.use_allreduce()
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     log("inputs ready; warmup")
@@ -491,6 +505,7 @@ def main(argv=None):
         "dtype": step.dtype,
         "data": "synthetic (seeded torch generators; no dataset)",
         "config": dict(step.config(), permute=a.permute,
+                       **({"epilogue": "fused_allreduce"} if a.allreduce else {}),
                        transfer="bidirectional" if a.bidir else "one-way"),
         "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),
         "roofline": roof,

@@ -26,7 +26,8 @@ __all__ = [
     "Context", "cce_shard_schedule", "cce_looped_allgather_einsum",
     "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
     "cce_looped_einsum_reducescatter_workspace", "cce_grouped_gemm",
-    "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched", "cce_describe_plan",
+    "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched",
+    "cce_fused_allreduce_epilogue", "cce_describe_plan",
     "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
     "CCE_FLAG_BIDIRECTIONAL",
@@ -284,4 +285,31 @@ def cce_fused_reduce_epilogue_batched(ctx: Context, partials, bias, residuals, o
         int(mask_ld), ptr_array([t.data_ptr() for t in outs]), _dtype(outs[0].dtype), om.ld,
         ptr_array([t.data_ptr() for t in mask_outs]) if mask_outs is not None else None, 0,
         _stream(stream, outs[0].device)), "cce_fused_reduce_epilogue_batched")
+    return outs
+
+
+def cce_fused_allreduce_epilogue(ctx: Context, partials, bias, residual, outs, p_drop: float,
+                                 seed: int = 0, offset: int = 0, mask_row0: int = 0,
+                                 mask_col0: int = 0, mask_ld: int | None = None, mask_out=None,
+                                 stream=None):
+    """FusedAllReduce: every outs[r] = residual + keep * (sum(partials) + bias) / (1 - p)."""
+    pm = _same(partials, "partial")
+    om = _same(outs, "out")
+    if len(outs) != len(partials):
+        raise ValueError("one output per rank")
+    rm = _mat(residual) if residual is not None else None
+    if mask_ld is None:
+        mask_ld = mask_col0 + pm.cols
+    bias_t = _dtype(bias.dtype) if bias is not None else _dtype(outs[0].dtype)
+    res_t = _dtype(residual.dtype) if residual is not None else _dtype(outs[0].dtype)
+    check(lib().cce_fused_allreduce_epilogue(
+        ctx.handle, len(partials), _dtype(partials[0].dtype),
+        ptr_array([t.data_ptr() for t in partials]), pm,
+        bias.data_ptr() if bias is not None else None, bias_t,
+        residual.data_ptr() if residual is not None else None, res_t,
+        rm.ld if rm is not None else pm.cols,
+        float(p_drop), int(seed), int(offset), int(mask_row0), int(mask_col0), int(mask_ld),
+        ptr_array([t.data_ptr() for t in outs]), _dtype(outs[0].dtype), om.ld,
+        mask_out.data_ptr() if mask_out is not None else None, 0,
+        _stream(stream, outs[0].device)), "cce_fused_allreduce_epilogue")
     return outs

@@ -943,14 +943,16 @@ static cce_status epilogue_impl(cce_ctx* ctx, int n_batch, int n_partials, cce_d
                                 cce_dtype bias_t, const void* const* residuals, cce_dtype res_t,
                                 int64_t ld_res, double p_drop, uint64_t seed, uint64_t offset,
                                 const int64_t* mask_row0, int64_t mask_col0, int64_t mask_ld,
-                                void* const* outs, cce_dtype out_t, int64_t ld_out,
+                                void* const* outs, int n_rep, cce_dtype out_t, int64_t ld_out,
                                 uint8_t* const* mask_outs, uint32_t flags, cce_stream stream) {
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags != 0) return fail(CCE_EINVAL, "flags must be 0");
   if (n_batch < 1) return fail(CCE_EINVAL, "n_batch < 1");
   if (n_partials < 1) return fail(CCE_EINVAL, "n_partials < 1");
-  if (static_cast<int64_t>(n_partials) * n_batch > CCE_MAX_RANKS)
-    return fail(CCE_EUNSUPPORTED, "n_batch * n_partials > CCE_MAX_RANKS");
+  if (n_rep < 1) return fail(CCE_EINVAL, "n_rep < 1");
+  if (static_cast<int64_t>(n_partials) * n_batch > CCE_MAX_RANKS ||
+      static_cast<int64_t>(n_rep) * n_batch > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "n_batch * n_partials (or outputs) > CCE_MAX_RANKS");
   if (!partials) return fail(CCE_EINVAL, "partials is NULL");
   if (!outs) return fail(CCE_EINVAL, "out is NULL");
   if (!mask_row0) return fail(CCE_EINVAL, "mask_row0 is NULL");
@@ -986,8 +988,11 @@ static cce_status epilogue_impl(cce_ctx* ctx, int n_batch, int n_partials, cce_d
       CCE_TRY(check_ptr(("residual" + bsx).c_str(), residuals[b], rs));
       ranges.push_back(range_of(residuals[b], rs, "residual" + bsx, false));
     }
-    CCE_TRY(check_ptr(("out" + bsx).c_str(), outs[b], os));
-    ranges.push_back(range_of(outs[b], os, "out" + bsx, true));
+    for (int q = 0; q < n_rep; ++q) {
+      const std::string oq = "out[" + std::to_string(b * n_rep + q) + "]";
+      CCE_TRY(check_ptr(oq.c_str(), outs[b * n_rep + q], os));
+      ranges.push_back(range_of(outs[b * n_rep + q], os, oq, true));
+    }
     if (mask_outs) {
       CCE_TRY(check_ptr(("mask_out" + bsx).c_str(), mask_outs[b], ms));
       ranges.push_back(range_of(mask_outs[b], ms, "mask_out" + bsx, true));
@@ -1003,10 +1008,11 @@ static cce_status epilogue_impl(cce_ctx* ctx, int n_batch, int n_partials, cce_d
   for (int k = 0; k < n_partials * n_batch; ++k) L.parts[k] = partials[k];
   for (int b = 0; b < n_batch; ++b) {
     L.res[b] = residuals ? residuals[b] : nullptr;
-    L.out[b] = outs[b];
     L.mask[b] = mask_outs ? mask_outs[b] : nullptr;
     L.mrow0[b] = mask_row0[b];
   }
+  L.n_rep = n_rep;
+  for (int q = 0; q < n_batch * n_rep; ++q) L.out[q] = outs[q];
   L.rows = shape.rows;
   L.cols = shape.cols;
   L.ld_part = shape.ld;
@@ -1035,7 +1041,8 @@ static cce_status epilogue_impl(cce_ctx* ctx, int n_batch, int n_partials, cce_d
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const double ebytes =
       n_batch * (static_cast<double>(shape.rows) * shape.cols *
-                 (static_cast<double>(n_partials) * ep + (residuals ? eo : 0) + eo)) +
+                 (static_cast<double>(n_partials) * ep + (residuals ? eo : 0) +
+                  static_cast<double>(n_rep) * eo)) +
       (bias ? static_cast<double>(shape.cols) * eo : 0.0);
   int slot;
   CCE_TRY(prof_begin(ctx, hs, 2, -1, 0.0, ebytes, &slot));
@@ -1057,8 +1064,8 @@ cce_status cce_fused_reduce_epilogue(cce_ctx* ctx, int n_partials, cce_dtype par
   const int64_t row1[1] = {mask_row0};
   return epilogue_impl(ctx, 1, n_partials, part_t, partials, shape, bias, bias_t,
                        residual ? res1 : nullptr, res_t, ld_res, p_drop, seed, offset, row1,
-                       mask_col0, mask_ld, out1, out_t, ld_out, mask_out ? mask1 : nullptr, flags,
-                       stream);
+                       mask_col0, mask_ld, out1, 1, out_t, ld_out, mask_out ? mask1 : nullptr,
+                       flags, stream);
 }
 
 cce_status cce_fused_reduce_epilogue_batched(
@@ -1077,7 +1084,25 @@ cce_status cce_fused_reduce_epilogue_batched(
       if (!mask_outs[b]) return fail(CCE_EINVAL, "mask_outs[b] is NULL (pass a NULL array for none)");
   return epilogue_impl(ctx, n_batch, n_partials, part_t, partials, shape, bias, bias_t, residuals,
                        res_t, ld_res, p_drop, seed, offset, mask_row0, mask_col0, mask_ld, outs,
-                       out_t, ld_out, mask_outs, flags, stream);
+                       1, out_t, ld_out, mask_outs, flags, stream);
+}
+
+cce_status cce_fused_allreduce_epilogue(cce_ctx* ctx, int n_ranks, cce_dtype part_t,
+                                        const void* const* partials, cce_mat shape,
+                                        const void* bias, cce_dtype bias_t, const void* residual,
+                                        cce_dtype res_t, int64_t ld_res, double p_drop,
+                                        uint64_t seed, uint64_t offset, int64_t mask_row0,
+                                        int64_t mask_col0, int64_t mask_ld, void* const* outs,
+                                        cce_dtype out_t, int64_t ld_out, uint8_t* mask_out,
+                                        uint32_t flags, cce_stream stream) {
+  clear_error();
+  const void* res1[1] = {residual};
+  uint8_t* mask1[1] = {mask_out};
+  const int64_t row1[1] = {mask_row0};
+  return epilogue_impl(ctx, 1, n_ranks, part_t, partials, shape, bias, bias_t,
+                       residual ? res1 : nullptr, res_t, ld_res, p_drop, seed, offset, row1,
+                       mask_col0, mask_ld, outs, n_ranks, out_t, ld_out,
+                       mask_out ? mask1 : nullptr, flags, stream);
 }
 
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, uint32_t flags,

@@ -70,7 +70,8 @@ struct EpilogueLaunch {
   const void* res[kMaxGroups];     // per output; NULL entries: no residual
   cce_dtype res_t = CCE_F32;
   int64_t ld_res = 0;
-  void* out[kMaxGroups];
+  void* out[kMaxGroups];           // [b * n_rep + q]
+  int n_rep = 1;                   // replicas of each output (FusedAllReduce's AllGather)
   cce_dtype out_t = CCE_F32;
   int64_t ld_out = 0;
   uint8_t* mask[kMaxGroups];       // per output; NULL entries: no mask output

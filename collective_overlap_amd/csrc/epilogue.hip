@@ -42,7 +42,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 struct EArgs {
   const void* parts[kMaxGroups];   // [batch * n + k]
   const void* res[kMaxGroups];     // per batch entry (NULL: no residual)
-  void* out[kMaxGroups];
+  void* out[kMaxGroups];           // [batch * n_rep + q]: every replica gets the result
+  int n_rep;
   uint8_t* mask[kMaxGroups];       // per batch entry (NULL: no mask output)
   int64_t mrow0[kMaxGroups];
   int n;
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
   const int n = NP > 0 ? NP : a.n;
   const void* const* parts = a.parts + bz * n;
   const void* res = a.res[bz];
-  void* out = a.out[bz];
+  void* const* outs = a.out + bz * a.n_rep;
   uint8_t* mask = a.mask[bz];
   const int64_t mrow0 = a.mrow0[bz];
   for (int i = blockIdx.y; i < a.rows; i += gridDim.y) {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = s[e] + r[e];
       }
-      store8<TO>(out, static_cast<int64_t>(i) * a.ld_out + j, s);
+      for (int q = 0; q < a.n_rep; ++q) store8<TO>(outs[q], static_cast<int64_t>(i) * a.ld_out + j, s);
       if (mask) {
         uint64_t bits = 0;
 #pragma unroll
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EArgs a) {
           v = 0.0f;
         }
         if (res) v = v + load1<TR>(res, static_cast<int64_t>(i) * a.ld_res + c);
-        store1<TO>(out, static_cast<int64_t>(i) * a.ld_out + c, v);
+        for (int q = 0; q < a.n_rep; ++q) store1<TO>(outs[q], static_cast<int64_t>(i) * a.ld_out + c, v);
         if (mask) mask[static_cast<int64_t>(i) * a.cols + c] = kp ? 1 : 0;
       }
     }
@@ -293,9 +294,10 @@ cce_status launch_fused_epilogue(const EpilogueLaunch& L, void* stream) {
   if (L.rows <= 0 || L.cols <= 0 || L.batch <= 0) return CCE_OK;
   EArgs k{};
   for (int i = 0; i < L.n * L.batch; ++i) k.parts[i] = L.parts[i];
+  for (int q = 0; q < L.batch * L.n_rep; ++q) k.out[q] = L.out[q];
+  k.n_rep = L.n_rep;
   for (int b = 0; b < L.batch; ++b) {
     k.res[b] = L.res[b];
-    k.out[b] = L.out[b];
     k.mask[b] = L.mask[b];
     k.mrow0[b] = L.mrow0[b];
   }

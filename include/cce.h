@@ -327,6 +327,31 @@ cce_status cce_fused_reduce_epilogue_batched(
     cce_stream stream);
 
 /* ------------------------------------------------------------------------
+ * FusedAllReduce across n_ranks logical ranks ([CC] fused collective
+ * communication: an AllReduce split into ReduceScatter and AllGather, with
+ * the bias add, dropout and residual add applied to each rank's reduced
+ * slice in between).  partials[r] is rank r's [rows, cols] partial; every
+ * outs[r] (r < n_ranks) receives the whole result
+ *   residual + keep * (sum_r partials[r] + bias) * c
+ * computed exactly as cce_fused_reduce_epilogue computes it (same order,
+ * same mask for the given index base), so all replicas are bit-identical to
+ * that call's output.  On one GPU the ranks share the HBM, so the
+ * ReduceScatter, the pointwise tail and the AllGather are one pass: each
+ * partial and the residual are read once and the result is stored once per
+ * rank.  The residual is the one replicated tensor (NULL for none);
+ * mask_out (NULL or [rows, cols] uint8) receives the keep decisions once.
+ * 1 <= n_ranks <= CCE_MAX_RANKS.  flags: must be 0.
+ * ---------------------------------------------------------------------- */
+cce_status cce_fused_allreduce_epilogue(cce_ctx* ctx, int n_ranks, cce_dtype part_t,
+                                        const void* const* partials, cce_mat shape,
+                                        const void* bias, cce_dtype bias_t, const void* residual,
+                                        cce_dtype res_t, int64_t ld_res, double p_drop,
+                                        uint64_t seed, uint64_t offset, int64_t mask_row0,
+                                        int64_t mask_col0, int64_t mask_ld, void* const* outs,
+                                        cce_dtype out_t, int64_t ld_out, uint8_t* mask_out,
+                                        uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
  * Plan description, host-only (no device, no context): writes the ordered
  * list of operations that a looped call with these arguments would enqueue,
  * one per line, into buf (NUL-terminated; *needed receives the full length

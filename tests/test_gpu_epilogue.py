@@ -149,3 +149,43 @@ def test_batched_rejects_too_many_operands(ctx):
     outs = [torch.empty((4, 8), device=DEV) for _ in range(2)]
     with pytest.raises(RuntimeError):
         cce.cce_fused_reduce_epilogue_batched(ctx, parts, None, None, outs, 0.0)
+
+
+ALLREDUCE = [
+    # n, rows, cols, ld, part, out, p, seed, offset
+    (8, 130, 512, None, "bf16", "bf16", 0.1, 3, 0),
+    (4, 33, 261, 272, "f32", "bf16", 0.2, 1, 7),
+    (2, 64, 96, None, "f32", "f32", 0.0, 0, 0),
+    (1, 17, 40, None, "bf16", "f32", 0.5, 2, 1),
+]
+
+
+@pytest.mark.parametrize("case", ALLREDUCE)
+def test_fused_allreduce(ctx, case):
+    """Every rank's replica equals the oracle's step-by-step FusedAllReduce
+    (ReduceScatter, epilogue per slice, AllGather), and, bit for bit, the
+    single-output fused epilogue of the same partials."""
+    import collective_overlap_amd as cce
+    n, rows, cols, ld, pt, ot, p, seed, off = case
+    print(f"[gpu] fused allreduce {case}", flush=True)
+    pdt = torch.float32 if pt == "f32" else torch.bfloat16
+    odt = torch.float32 if ot == "f32" else torch.bfloat16
+    parts = [_mk((rows, cols), 300 + r, pdt, ld) for r in range(n)]
+    bias = W.normal((cols,), 0.02, 90, device=DEV, dtype=odt)
+    res = _mk((rows, cols), 91, odt, ld)
+    outs = [torch.full((rows, ld or cols), float("nan"), device=DEV, dtype=odt)[:, :cols]
+            for _ in range(n)]
+    mask = torch.full((rows, cols), 7, device=DEV, dtype=torch.uint8)
+    cce.cce_fused_allreduce_epilogue(ctx, parts, bias, res, outs, p, seed, off, mask_out=mask)
+    single = torch.empty((rows, ld or cols), device=DEV, dtype=odt)[:, :cols]
+    cce.cce_fused_reduce_epilogue(ctx, parts, bias, res, single, p, seed, off)
+    sync()
+    ref, keep = oep.fused_allreduce([np64(x) for x in parts], np64(bias), np64(res), p, seed, off)
+    assert np.array_equal(mask.cpu().numpy().astype(bool), keep)
+    it = torch.int16 if odt == torch.bfloat16 else torch.int32
+    for r in range(n):
+        assert torch.equal(outs[r].contiguous().view(it), single.contiguous().view(it)), f"rank {r}"
+        if ot == "f32":
+            assert_f32_close(np64(outs[r]), ref[r], f"rank {r}", tol=1e-6)
+        else:
+            assert_bf16_close(np64(outs[r]), ref[r], f"rank {r}")
