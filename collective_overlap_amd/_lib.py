@@ -77,6 +77,8 @@ PROTOTYPES = {
     "cce_fused_allreduce_epilogue": (_I, [_P, _I, _I, _PP, cce_mat, _P, _I, _P, _I, _I64,
                                           ctypes.c_double, _U64, _U64, _I64, _I64, _I64, _PP, _I,
                                           _I64, _P, _U32, _P]),
+    "cce_overlap_beneficial": (_I, [ctypes.c_double] * 4),
+    "cce_overlap_choose": (_I, [ctypes.c_double] * 5),
     "cce_describe_plan": (_I, [_I, _I, _I, _I, _U32, ctypes.c_char_p, _SZ, ctypes.POINTER(_SZ)]),
 }
 

@@ -1105,6 +1105,23 @@ cce_status cce_fused_allreduce_epilogue(cce_ctx* ctx, int n_ranks, cce_dtype par
                        mask_out ? mask1 : nullptr, flags, stream);
 }
 
+int cce_overlap_beneficial(double original_comp, double original_comm, double ring_comm,
+                           double epilogue) {
+  const double v[4] = {original_comp, original_comm, ring_comm, epilogue};
+  for (double x : v)
+    if (!(x >= 0.0)) return -1;                 // negative or NaN
+  return original_comp + original_comm >= std::max(original_comp, ring_comm) + epilogue ? 1 : 0;
+}
+
+int cce_overlap_choose(double comp, double comm0, double shard_bytes0, double comm1,
+                       double shard_bytes1) {
+  const double v[5] = {comp, comm0, shard_bytes0, comm1, shard_bytes1};
+  for (double x : v)
+    if (!(x >= 0.0)) return -1;
+  if (comp < comm0 && comp < comm1) return shard_bytes1 < shard_bytes0 ? 1 : 0;
+  return comm1 > comm0 ? 1 : 0;
+}
+
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, uint32_t flags,
                              char* buf, size_t buf_len, size_t* needed) {
   clear_error();

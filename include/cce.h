@@ -352,6 +352,28 @@ cce_status cce_fused_allreduce_epilogue(cce_ctx* ctx, int n_ranks, cce_dtype par
                                         uint32_t flags, cce_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Enabling rule of [OV] Section 5.5 (host-only).  The looped form replaces a
+ * collective + einsum only when it is estimated not to be slower:
+ *   original_comp + original_comm >= max(original_comp, ring_comm) + epilogue
+ * where original_comp / original_comm are the times of the einsum and of
+ * the collective as they are, ring_comm the time of the permutes along the
+ * ring, and epilogue the cost of the loop's prologue or epilogue (all in the
+ * same unit, each >= 0).  Returns 1 to use the loop, 0 to keep the original,
+ * -1 for a negative or NaN argument.
+ *
+ * cce_overlap_choose: the same section's choice between two candidate
+ * collectives of one einsum.  If the einsum is estimated faster than both
+ * (comp < comm0 and comp < comm1) the candidate with the smaller shard
+ * (fewer bytes moved outside the loop) is chosen, else the one whose
+ * collective takes longer.  Ties go to candidate 0.  Returns 0 or 1, -1 for
+ * a negative or NaN argument.
+ * ---------------------------------------------------------------------- */
+int cce_overlap_beneficial(double original_comp, double original_comm, double ring_comm,
+                           double epilogue);
+int cce_overlap_choose(double comp, double comm0, double shard_bytes0, double comm1,
+                       double shard_bytes1);
+
+/* ------------------------------------------------------------------------
  * Plan description, host-only (no device, no context): writes the ordered
  * list of operations that a looped call with these arguments would enqueue,
  * one per line, into buf (NUL-terminated; *needed receives the full length

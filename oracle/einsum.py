@@ -13,7 +13,8 @@ factor [m, k] times right factor [k, n], float64.
 Parity pins (tests/test_oracle_einsum.py): a pure-Python triple loop on tiny
 inputs, the N = 1 reduction to a plain matmul, bit-equality with the
 brute-force loop simulation on exact-integer inputs, and the AllReduce =
-ReduceScatter + AllGather identity.
+ReduceScatter + AllGather identity.  The backward pass of the AllGather-Einsum
+is pinned to torch autograd (float64, CPU) on the monolithic forward.
 """
 
 from __future__ import annotations
@@ -68,3 +69,34 @@ def local_matmuls(a: list[np.ndarray], b: list[np.ndarray]) -> list[np.ndarray]:
     which yields one local (rank-private) partial per rank (CoCoNet, Figure 3
     program: MatMul of the sliced input and sliced weight)."""
     return [x @ y for x, y in zip(a, b)]
+
+
+def allgather_einsum_backward(mode: str, looped: list[np.ndarray],
+                              local: list[np.ndarray], d_out: list[np.ndarray]):
+    """Gradients of the case-1 AllGather-Einsum with respect to both operands.
+
+    [OV] Section 2.2: the weights are AllGathered before each einsum in the
+    forward pass, and in the backward pass that AllGather becomes a
+    ReduceScatter producing each device's partition of the weight gradient.
+    Written from the definitions (d_out[r] is dL/dY_r):
+
+      rhs_cols, Y_r = A_r @ concat_cols(B_s):
+        dB_s = sum_r (A_r^T @ dY_r)[:, cols of shard s]   (Einsum-ReduceScatter)
+        dA_r = dY_r @ concat_cols(B_s)^T                 (AllGather-Einsum, K split)
+      lhs_rows, Y_r = concat_rows(A_s) @ B_r:
+        dA_s = sum_r (dY_r @ B_r^T)[rows of shard s]     (Einsum-ReduceScatter)
+        dB_r = concat_rows(A_s)^T @ dY_r                 (AllGather-Einsum, K split)
+
+    Returns (grads of the looped shards by shard ID, grads of the local
+    operands by rank)."""
+    if mode == "rhs_cols":
+        full = allgather(looped, axis=1)
+        d_looped = reducescatter([a.T @ dy for a, dy in zip(local, d_out)], axis=1)
+        d_local = [dy @ full.T for dy in d_out]
+        return d_looped, d_local
+    if mode == "lhs_rows":
+        full = allgather(looped, axis=0)
+        d_looped = reducescatter([dy @ b.T for b, dy in zip(local, d_out)], axis=0)
+        d_local = [full.T @ dy for dy in d_out]
+        return d_looped, d_local
+    raise ValueError(mode)

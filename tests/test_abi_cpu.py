@@ -394,3 +394,46 @@ def test_bidir_rejects_case2_and_too_many_ranks(cce):
         _plan(0, 4, 2, 1, BIDIR)
     with pytest.raises(CceError):
         _plan(1, 33, 0, 1, BIDIR)
+
+
+# ---------------------------------------------------------------------------
+# Enabling rule and candidate choice (Wang et al. ASPLOS'23, Section 5.5)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("comp,comm,ring_,epi,want", [
+    (10.0, 4.0, 8.0, 1.0, 1),     # ring hidden under the einsum: 14 >= 10 + 1
+    (10.0, 4.0, 16.0, 1.0, 0),    # ring slower than einsum + collective: 14 < 17
+    (10.0, 4.0, 13.0, 1.0, 1),    # boundary: 14 >= 13 + 1 -> loop
+    (10.0, 4.0, 8.0, 4.5, 0),     # epilogue too costly: 14 < 14.5
+    (2.0, 10.0, 12.0, 0.0, 1),    # communication-bound, ring equal to the original + comp
+    (0.0, 0.0, 0.0, 0.0, 1),      # degenerate: equal times loop
+    (-1.0, 1.0, 1.0, 0.0, -1),
+    (float("nan"), 1.0, 1.0, 0.0, -1),
+])
+def test_overlap_enabling_rule(cce, comp, comm, ring_, epi, want):
+    assert cce.cce_overlap_beneficial(comp, comm, ring_, epi) == want
+
+
+def test_overlap_enabling_rule_properties(cce):
+    """Monotone in each argument: more ring time or epilogue never turns the
+    loop on; more original communication never turns it off."""
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        c, m, r, e = rng.uniform(0, 10, 4)
+        d = rng.uniform(0, 5)
+        base = cce.cce_overlap_beneficial(c, m, r, e)
+        assert cce.cce_overlap_beneficial(c, m, r + d, e) <= base
+        assert cce.cce_overlap_beneficial(c, m, r, e + d) <= base
+        assert cce.cce_overlap_beneficial(c, m + d, r, e) >= base
+
+
+@pytest.mark.parametrize("comp,c0,s0,c1,s1,want", [
+    (1.0, 5.0, 100.0, 6.0, 50.0, 1),   # einsum faster than both: smaller shard
+    (1.0, 5.0, 50.0, 6.0, 100.0, 0),
+    (1.0, 5.0, 70.0, 6.0, 70.0, 0),    # tie on shard size -> candidate 0
+    (8.0, 5.0, 50.0, 6.0, 100.0, 1),   # otherwise the longer collective
+    (8.0, 7.0, 50.0, 6.0, 10.0, 0),
+    (5.5, 5.0, 50.0, 6.0, 10.0, 1),    # faster than only one: longer collective
+    (1.0, -5.0, 50.0, 6.0, 10.0, -1),
+])
+def test_overlap_candidate_choice(cce, comp, c0, s0, c1, s1, want):
+    assert cce.cce_overlap_choose(comp, c0, s0, c1, s1) == want

@@ -141,10 +141,15 @@ def test_rs_n8_full(ctx):
         assert_f32_close(np64(out[r][rows][:, cols]), ref, f"shard {r}")
 
 
-def test_gpt3_ffn_n8_full(ctx):
+@pytest.mark.parametrize("flags,batched", [(0, False), (0x8, True), (0x18, True)])
+def test_gpt3_ffn_n8_full(ctx, flags, batched):
     """GPT-3 FFN, 8-way: looped AllGather into W1 shards with GELU, looped
-    ReduceScatter out of W2 shards, fused bias+dropout+residual; sampled."""
+    ReduceScatter out of W2 shards, fused bias+dropout+residual; sampled.
+    Run in the copy-stream form with one epilogue per rank, and in the
+    benchmark's configurations: fused permute (one-way and two-way ring) with
+    the batched epilogue."""
     import collective_overlap_amd as cce
+    print(f"[gpu] gpt3_ffn_n8 full flags={flags} batched={batched}", flush=True)
     n = 8
     X = [W.normal((1024, 12288), 1.0, s, device=DEV) for s in range(n)]
     W1 = [W.weight_store(12288, 6144, 0.02, 10 + r, device=DEV) for r in range(n)]
@@ -154,11 +159,16 @@ def test_gpt3_ffn_n8_full(ctx):
     H = [torch.empty((8192, 6144), device=DEV, dtype=BF) for _ in range(n)]
     acc = [torch.empty((1024, 12288), device=DEV) for _ in range(n)]
     out = [torch.empty((1024, 12288), device=DEV, dtype=BF) for _ in range(n)]
-    cce.cce_looped_allgather_einsum(ctx, "lhs_rows", X, W1, H, flags=cce.CCE_FLAG_GELU)
-    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", H, W2, acc)
-    for r in range(n):
-        cce.cce_fused_reduce_epilogue(ctx, [acc[r]], b, R[r], out[r], 0.1, 0, 0,
-                                      mask_row0=r * 1024, mask_col0=0, mask_ld=12288)
+    cce.cce_looped_allgather_einsum(ctx, "lhs_rows", X, W1, H, flags=flags | cce.CCE_FLAG_GELU)
+    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", H, W2, acc, flags=flags)
+    if batched:
+        cce.cce_fused_reduce_epilogue_batched(ctx, [[a] for a in acc], b, R, out, 0.1, 0, 0,
+                                              mask_row0=[r * 1024 for r in range(n)],
+                                              mask_col0=0, mask_ld=12288)
+    else:
+        for r in range(n):
+            cce.cce_fused_reduce_epilogue(ctx, [acc[r]], b, R[r], out[r], 0.1, 0, 0,
+                                          mask_row0=r * 1024, mask_col0=0, mask_ld=12288)
     sync()
     # layer 1: H_r rows (global tokens) x sampled FFN columns
     grow = _rows(8, 8192, 7)
