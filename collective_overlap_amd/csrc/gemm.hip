@@ -107,26 +107,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Exact (erf) GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).  erf comes from
+// the rational approximation of Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7):
+//   erfc(a) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),
+//   t = 1 / (1 + p a), a >= 0,
+// and 1 + erf(u) is formed as 2 - erfc(|u|) for u >= 0 and erfc(|u|) for
+// u < 0, so the negative tail has no cancellation.  About a dozen VALU
+// operations against several dozen for the library erff; the epilogue runs
+// while the matrix cores idle, so its length shows in the kernel time.
 __device__ __forceinline__ float gelu_exact(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  const float u = x * 0.70710678118654752f;
+  const float a = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f +
+                                                                          t * 1.061405429f))));
+  const float q = poly * __expf(-(a * a));
+  return 0.5f * x * (u >= 0.0f ? 2.0f - q : q);
 }
 
-// Epilogue for 4 consecutive columns [n, n+4) of row m.
+// Accumulator input of 4 consecutive columns [n, n+4) of row m (zeros past
+// the edges; store_quad skips those).
+__device__ __forceinline__ f32x4 load_cin_quad(const KArgs& a, const float* cinbase, int m, int n) {
+  f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (m >= a.M || n >= a.N) return r;
+  const float* cin = cinbase + static_cast<int64_t>(m) * a.ldcin + n;
+  if (n + 3 < a.N) {
+    r = *reinterpret_cast<const f32x4*>(cin);
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.N) r[e] = cin[e];
+  }
+  return r;
+}
+
+// Epilogue for 4 consecutive columns [n, n+4) of row m; cinv is the
+// accumulator input (EPI_ACCUM) loaded by load_cin_quad.
 template <typename TOut, int EPI, bool GELU>
-__device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, const float* cinbase, int m,
-                                           int n, f32x4 v) {
+__device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, int m, int n, f32x4 v,
+                                           f32x4 cinv) {
   if (m >= a.M || n >= a.N) return;
   const bool full = (n + 3 < a.N);
-  if (EPI == EPI_ACCUM) {
-    const float* cin = cinbase + static_cast<int64_t>(m) * a.ldcin + n;
-    if (full) {
-      f32x4 r = *reinterpret_cast<const f32x4*>(cin);
-      v = r + v;
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (n + e < a.N) v[e] = cin[e] + v[e];
-    }
-  }
+  if (EPI == EPI_ACCUM) v = cinv + v;
   if (GELU) {
     for (int e = 0; e < 4; ++e) v[e] = gelu_exact(v[e]);
   }
@@ -181,7 +204,8 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS, typename TOut, int EPI, bool GELU>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
+  constexpr int NW = WM * WN;                // waves
   constexpr int ROWB = BK * 2;               // bytes per LDS row
   constexpr int CPR = BK / 8;                // 16-byte chunks per row
   constexpr int KK = BK / 16;                // k16 steps per k tile
@@ -189,10 +213,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int RPI = 1024 / ROWB;           // rows per 1 KB load instruction
-  constexpr int A_DMA = BM / (4 * RPI);      // load instructions per wave per stage
-  constexpr int B_DMA = BN / (4 * RPI);
+  constexpr int A_DMA = BM / (NW * RPI);     // load instructions per wave per stage
+  constexpr int B_DMA = BN / (NW * RPI);
   constexpr int N_DMA = A_DMA + B_DMA;
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(KK % 2 == 0 && NS >= 2 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
   static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
@@ -228,12 +252,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   uint32_t a_off[A_DMA], b_off[B_DMA];
 #pragma unroll
   for (int p = 0; p < A_DMA; ++p) {
-    const int r = RPI * (4 * p + wave) + dl_row;
+    const int r = RPI * (NW * p + wave) + dl_row;
     a_off[p] = (m0 + r < a.M) ? (r * a.lda + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
 #pragma unroll
   for (int p = 0; p < B_DMA; ++p) {
-    const int r = RPI * (4 * p + wave) + dl_row;
+    const int r = RPI * (NW * p + wave) + dl_row;
     b_off[p] = (n0 + r < a.N) ? (r * a.ldb + dl_chunk * 8) * 2u : uint32_t(kOob);
   }
   // Rows past M / N start at kOob; chunks past K add kOob.  Operands are
@@ -244,9 +268,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     const uint32_t kadd = k0 * 2u + ((k0 + dl_chunk * 8) < a.K ? 0u : uint32_t(kOob));
     char* s = smem + buf * STAGE + wave * 1024;
 #pragma unroll
-    for (int p = 0; p < A_DMA; ++p) dma16(ra, s + p * 4096, a_off[p] + kadd);
+    for (int p = 0; p < A_DMA; ++p) dma16(ra, s + p * NW * 1024, a_off[p] + kadd);
 #pragma unroll
-    for (int p = 0; p < B_DMA; ++p) dma16(rb, s + BM * ROWB + p * 4096, b_off[p] + kadd);
+    for (int p = 0; p < B_DMA; ++p) dma16(rb, s + BM * ROWB + p * NW * 1024, b_off[p] + kadd);
   };
 
   auto kadd_of = [&](int k0) {
@@ -255,8 +279,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   // Load instruction d of the wave's N_DMA (A first, then B).
   auto dma_one = [&](int buf, uint32_t kadd, int d) {
     char* s = smem + buf * STAGE + wave * 1024;
-    if (d < A_DMA) dma16(ra, s + d * 4096, a_off[d] + kadd);
-    else dma16(rb, s + BM * ROWB + (d - A_DMA) * 4096, b_off[d - A_DMA] + kadd);
+    if (d < A_DMA) dma16(ra, s + d * NW * 1024, a_off[d] + kadd);
+    else dma16(rb, s + BM * ROWB + (d - A_DMA) * NW * 1024, b_off[d - A_DMA] + kadd);
   };
 
   // Fragment addressing: row r = base + 32 i + (lane & 31) with base a
@@ -309,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
     const int row0 = fwd_a ? m0 : n0;
     const int rows = fwd_a ? BM : BN;
     const int lim = fwd_a ? a.M : a.N;
-    constexpr int RP = 256 / CPR;                // rows per pass
+    constexpr int RP = 64 * NW / CPR;            // rows per pass
     const int c = tid % CPR, r0 = tid / CPR;
     const int k = kt * BK + c * 8;
     if (k >= a.K) return;
@@ -348,6 +372,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   // case.
   constexpr int NMF = FM * FN;
   constexpr int C = (N_DMA + 1) / 2;         // loads per half
+  // fragment reads: one per RS MFMAs, spread over the step
+  constexpr int RS = NMF >= 2 * (FM + FN) ? 2 : 1;
   const int KT = (a.K + BK - 1) / BK;
   if (KT > 0) {
 #pragma unroll
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
         mfma_one(kk & 1, q);
-        if (q < FM + FN) fread_one(cur, kk + 1, (kk + 1) & 1, q);
+        if (q % RS == 0 && q / RS < FM + FN) fread_one(cur, kk + 1, (kk + 1) & 1, q / RS);
 #pragma unroll
         for (int d = C; d < N_DMA; ++d)
           if (kk == 0 && (d - C) * NMF / C == q) dma_one(prv, kadd1, d);
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
         mfma_one((KK - 1) & 1, q);
-        if (q < FM + FN) fread_one(nxt, 0, 0, q);
+        if (q % RS == 0 && q / RS < FM + FN) fread_one(nxt, 0, 0, q / RS);
 #pragma unroll
         for (int d = 0; d < C; ++d)
           if (d * NMF / C == q) dma_one(cur, kadd, d);
@@ -407,24 +433,35 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(KArgs a) {
   wait_vmcnt<0>();
 
   // Epilogue: block (i, j) holds C^T; lane owns row m, columns n..n+3 per quad.
+  // Blocks go one at a time (register pressure); in the accumulate mode the
+  // accumulator input of block b+1 is loaded before block b is finished, so
+  // its memory latency overlaps block b's stores instead of stalling them.
   void* cbase = a.p.c[g];
   const float* cin = a.p.cin[g];
+  constexpr int NB = FM * FN;
+  auto quad_m = [&](int b) { return m0 + wm * WTM + (b / FN) * 32 + (lane & 31); };
+  auto quad_n = [&](int b, int q) { return n0 + wn * WTN + (b % FN) * 32 + 8 * q + 4 * (lane >> 5); };
+  f32x4 cb[2][4];
+  if (EPI == EPI_ACCUM) {
 #pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int m = m0 + wm * WTM + j * 32 + (lane & 31);
+    for (int q = 0; q < 4; ++q) cb[0][q] = load_cin_quad(a, cin, quad_m(0), quad_n(0, q));
+  }
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+  for (int b = 0; b < NB; ++b) {
+    const int i = b % FN, j = b / FN;
+    if (EPI == EPI_ACCUM && b + 1 < NB) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * (lane >> 5);
-        f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                   acc[i][j][4 * q + 3]};
-        store_quad<TOut, EPI, GELU>(a, cbase, cin, m, n, v);
-      }
-      // One block at a time: keeps the accumulate-mode loads from being
-      // hoisted all at once (register pressure).
-      __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < 4; ++q)
+        cb[(b + 1) & 1][q] = load_cin_quad(a, cin, quad_m(b + 1), quad_n(b + 1, q));
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                 acc[i][j][4 * q + 3]};
+      store_quad<TOut, EPI, GELU>(a, cbase, quad_m(b), quad_n(b, q), v,
+                                  EPI == EPI_ACCUM ? cb[b & 1][q] : f32x4{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -478,7 +515,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
   for (int q = 0; q < 4; ++q) {
     const int n = n0 + wn * 32 + 8 * q + 4 * (lane >> 5);
     f32x4 v = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    store_quad<TOut, EPI, GELU>(a, a.p.c[g], a.p.cin[g], m, n, v);
+    const f32x4 cinv = EPI == EPI_ACCUM ? load_cin_quad(a, a.p.cin[g], m, n) : f32x4{};
+    store_quad<TOut, EPI, GELU>(a, a.p.c[g], m, n, v, cinv);
   }
 }
 
