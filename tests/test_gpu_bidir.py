@@ -127,3 +127,22 @@ def test_bidir_rejects_case2(ctx):
                                         flags=cce.CCE_FLAG_BIDIRECTIONAL)
     assert e.value.status == 2
     assert all(torch.count_nonzero(o) == 0 for o in out)
+
+
+def test_bidir_32_ranks_integer_probe(ctx):
+    """The largest two-way ring (64 groups per launch), bit-exact."""
+    import collective_overlap_amd as cce
+    n = 32
+    for flags in _forms(cce):
+        looped, local, oshape, ol, oc = _ag_inputs("lhs_rows", n, (24, 64, 40), torch.bfloat16, True, 2)
+        out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+        cce.cce_looped_allgather_einsum(ctx, "lhs_rows", looped, local, out, flags=flags)
+        a, b, rshape, oa, ob = _rs_inputs("slice_rhs_cols", n, (8, 64, 24), torch.bfloat16, True, 3)
+        rout = [torch.empty(rshape, device=DEV) for _ in range(n)]
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_rhs_cols", a, b, rout, flags=flags)
+        sync()
+        ref, _, _ = ring.simulate_allgather_einsum_bidir("lhs_rows", ol, oc)
+        rref, _, _ = ring.simulate_einsum_reducescatter_bidir("slice_rhs_cols", oa, ob)
+        for r in range(n):
+            assert np.array_equal(np64(out[r]), ref[r]), f"flags {flags} allgather rank {r}"
+            assert np.array_equal(np64(rout[r]), rref[r]), f"flags {flags} reducescatter rank {r}"

@@ -314,3 +314,42 @@ def test_reducescatter_fused_permute_matches(ctx, mode, dims, n):
     for r in range(n):
         assert torch.equal(outs[0][r], outs[1][r]), f"rank {r}"
         assert_f32_close(np64(outs[1][r]), ref[r], f"rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# Largest rank counts and empty extents
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", [0, 0x1, 0x8])
+def test_max_ranks_integer_probe(ctx, flags):
+    """CCE_MAX_RANKS = 64 ranks (one launch of 64 groups), bit-exact."""
+    import collective_overlap_amd as cce
+    n = 64
+    looped, local, oshape, ol, oc = _ag_inputs("rhs_cols", n, (40, 64, 16), torch.bfloat16, True, 4)
+    out = [torch.empty(oshape, device=DEV) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", looped, local, out, flags=flags)
+    a, b, rshape, oa, ob = _rs_inputs("slice_lhs_rows", n, (8, 64, 24), torch.bfloat16, True, 8)
+    rout = [torch.empty(rshape, device=DEV) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", a, b, rout, flags=flags)
+    sync()
+    ref = oe.allgather_einsum("rhs_cols", ol, oc)
+    rref = oe.einsum_reducescatter("slice_lhs_rows", oa, ob)
+    for r in range(n):
+        assert np.array_equal(np64(out[r]), ref[r]), f"allgather rank {r}"
+        assert np.array_equal(np64(rout[r]), rref[r]), f"reducescatter rank {r}"
+
+
+def test_empty_extents_are_noops(ctx):
+    """Zero rows or columns: the call succeeds and touches nothing."""
+    import collective_overlap_amd as cce
+    n = 3
+    looped = [torch.zeros((0, 64), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    local = [torch.zeros((32, 64), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    out = [torch.zeros((32, 0), device=DEV) for _ in range(n)]
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", looped, local, out)
+    a = [torch.zeros((0, 64), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    b = [torch.zeros((16, 64), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    rout = [torch.zeros((0, 16), device=DEV) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", a, b, rout)
+    parts = [torch.zeros((0, 16), device=DEV)]
+    cce.cce_fused_reduce_epilogue(ctx, parts, None, None, torch.zeros((0, 16), device=DEV), 0.1)
+    sync()

@@ -31,7 +31,8 @@ def _rows(n, total, seed):
     return np.sort(g.choice(total, size=min(n, total), replace=False))
 
 
-def test_ag_fp32_n2_full(ctx):
+@pytest.mark.parametrize("flags", [0, 0x8, 0x18])   # copy stream; fused; fused two-way
+def test_ag_fp32_n2_full(ctx, flags):
     """N=2 fp32 AllGather-Einsum case 1 and the 2-partial epilogue, compared
     in full."""
     import collective_overlap_amd as cce
@@ -41,7 +42,7 @@ def test_ag_fp32_n2_full(ctx):
     # weight shards W_k [256, 512] stored as [512, 256]
     Wt = [W.uniform((512, 256), 10 + r, device=DEV) for r in range(n)]
     Y = [torch.empty((64, 1024), device=DEV) for _ in range(n)]
-    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", Wt, X, Y)
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", Wt, X, Y, flags=flags)
     P = [W.uniform(w.shapes["P"], 20 + k, device=DEV) for k in range(n)]
     b = W.uniform(w.shapes["bias"], 30, device=DEV)
     R = W.uniform(w.shapes["R"], 31, device=DEV)
@@ -57,9 +58,11 @@ def test_ag_fp32_n2_full(ctx):
     assert_f32_close(np64(out), eref, "epilogue", tol=1e-6)
 
 
-def test_attn_outproj_n8_full(ctx):
+@pytest.mark.parametrize("allreduce", [False, True])
+def test_attn_outproj_n8_full(ctx, allreduce):
     """8 local partial GEMMs [8192,1024] x [1024,8192] and the 8-partial fused
-    epilogue at full size; sampled rows of each."""
+    epilogue at full size (one output, or the FusedAllReduce's 8 replicas);
+    sampled rows of each."""
     import collective_overlap_amd as cce
     n = 8
     IN = [W.normal((8192, 1024), 1.0, k, device=DEV) for k in range(n)]
@@ -70,8 +73,15 @@ def test_attn_outproj_n8_full(ctx):
     R = W.normal((8192, 8192), 1.0, 21, device=DEV)
     out = torch.empty((8192, 8192), device=DEV, dtype=BF)
     mask = torch.empty((8192, 8192), device=DEV, dtype=torch.uint8)
-    cce.cce_fused_reduce_epilogue(ctx, P, b, R, out, 0.1, 0, 0, mask_out=mask)
+    if allreduce:
+        reps = [out] + [torch.empty_like(out) for _ in range(n - 1)]
+        cce.cce_fused_allreduce_epilogue(ctx, P, b, R, reps, 0.1, 0, 0, mask_out=mask)
+    else:
+        cce.cce_fused_reduce_epilogue(ctx, P, b, R, out, 0.1, 0, 0, mask_out=mask)
     sync()
+    if allreduce:
+        for q in (1, 7):
+            assert torch.equal(reps[q].view(torch.int16), out.view(torch.int16)), f"replica {q}"
     rows = _rows(48, 8192, 1)
     cols = _rows(512, 8192, 2)
     for q in (0, 3, 7):
@@ -93,7 +103,8 @@ def test_attn_outproj_n8_full(ctx):
         assert_bf16_close(np64(out[r:r + 1]), ref, f"epilogue row {r}")
 
 
-def test_mlp2_n4_full(ctx):
+@pytest.mark.parametrize("flags", [0, 0x8, 0x18])   # copy stream; fused; fused two-way
+def test_mlp2_n4_full(ctx, flags):
     """2-layer MLP, 4-way: layer 1 looped AllGather (W1 shards [4096,4096])
     with GELU, layer 2 looped AllGather (W2 shards [16384,1024]).  For the
     sampled rows the oracle derives H from X itself (rounded to bf16, H's
@@ -105,8 +116,8 @@ def test_mlp2_n4_full(ctx):
     W2 = [W.weight_store(16384, 1024, 0.02, 20 + s, device=DEV) for s in range(n)]
     H = [torch.empty((2048, 16384), device=DEV, dtype=BF) for _ in range(n)]
     Y = [torch.empty((2048, 4096), device=DEV, dtype=BF) for _ in range(n)]
-    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W1, X, H, flags=cce.CCE_FLAG_GELU)
-    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W2, H, Y)
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W1, X, H, flags=flags | cce.CCE_FLAG_GELU)
+    cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W2, H, Y, flags=flags)
     sync()
     rows = _rows(6, 2048, 3)
     cols = _rows(384, 4096, 4)
@@ -121,7 +132,8 @@ def test_mlp2_n4_full(ctx):
         assert_bf16_close(np64(Y[r][rows][:, cols]), y_ref, f"Y rank {r}")
 
 
-def test_rs_n8_full(ctx):
+@pytest.mark.parametrize("flags", [0, 0x8, 0x18])   # copy stream; fused; fused two-way
+def test_rs_n8_full(ctx, flags):
     """Einsum-ReduceScatter, 8 ranks, X [16384,2048] x W [2048,4096], fp32
     accumulator shards [2048,4096]; sampled rows x columns of every shard."""
     import collective_overlap_amd as cce
@@ -129,7 +141,7 @@ def test_rs_n8_full(ctx):
     X = [W.normal((16384, 2048), 1.0, r, device=DEV) for r in range(n)]
     Wt = [W.weight_store(2048, 4096, 0.02, 10 + r, device=DEV) for r in range(n)]
     out = [torch.empty((2048, 4096), device=DEV) for _ in range(n)]
-    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", X, Wt, out)
+    cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", X, Wt, out, flags=flags)
     sync()
     rows = _rows(16, 2048, 5)
     cols = _rows(512, 4096, 6)
