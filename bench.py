@@ -15,7 +15,8 @@ the data itself: the AllGather forwards the shard it stages through LDS, the
 ReduceScatter's accumulate epilogue stores into the next rank's
 accumulator); --permute stream times the form with async copies on a second
 stream instead.  Both, and the same kernels serialised on one stream, are
-reported.
+reported.  The ring is two-way by default (two partial einsums per
+iteration, one per direction); --transfer one-way times the one-way ring.
 
 Prints one JSON line: whole-step bf16 TFLOP/s (value), the dominant kernel's
 roofline, the epilogue's HBM rate, the looped-vs-serial comparison with the
@@ -346,12 +347,12 @@ def gemm_roofline(recs, dtype, steps):
     return roof, per
 
 
-def measured_traffic(workload, permute):
+def measured_traffic(workload, permute, transfer):
     """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE
     counter runs (profiles/traffic_<workload>.json), scaled by the factors a
     plain copy of known size gave.  None when no such run exists for this
-    workload and permute form, or when the GEMM source has changed since the
-    counters were taken."""
+    workload, permute form and ring direction, or when the GEMM source has
+    changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
@@ -360,7 +361,8 @@ def measured_traffic(workload, permute):
         t = json.load(f)
     with open(os.path.join(ROOT, t["kernel_source"]), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if sha != t["kernel_source_sha256"] or t.get("permute") != permute:
+    if (sha != t["kernel_source_sha256"] or t.get("permute") != permute
+            or t.get("transfer", "one-way") != transfer):
         return None
     return t["gemm_bytes_per_launch"]["mean"]
 
@@ -376,9 +378,9 @@ def main(argv=None):
     ap.add_argument("--permute", choices=("fused", "stream"), default="fused",
                     help="fused: each partial GEMM sends the data itself; stream: async "
                          "copies on a second stream ordered by events")
-    ap.add_argument("--bidir", action="store_true",
-                    help="bidirectional ring: two partial einsums per iteration, one per "
-                         "direction, ceil(n/2) iterations")
+    ap.add_argument("--transfer", choices=("bidir", "one-way"), default="bidir",
+                    help="bidir (default): two-way ring, two partial einsums per iteration, "
+                         "ceil(n/2) iterations; one-way: the ring of the loop's pairs only")
     ap.add_argument("--allreduce", action="store_true",
                     help="attn_outproj_n8: FusedAllReduce epilogue, the result on every rank")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
@@ -419,7 +421,7 @@ def main(argv=None):
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     log("inputs ready; warmup")
-    bid = cce.CCE_FLAG_BIDIRECTIONAL if a.bidir else 0
+    bid = cce.CCE_FLAG_BIDIRECTIONAL if a.transfer == "bidir" else 0
     main_flags = (cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0) | bid
     for _ in range(a.warmup):
         step.run(ctx, main_flags)
@@ -429,7 +431,7 @@ def main(argv=None):
     value = step.flops * a.steps / wall / 1e12
     roof, per_shape = gemm_roofline(recs, step.dtype, a.steps)
     if roof is not None:
-        roof["traffic"] = measured_traffic(a.workload, a.permute)
+        roof["traffic"] = measured_traffic(a.workload, a.permute, a.transfer)
         if roof["traffic"] is not None:
             roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 counters)"
 
@@ -506,7 +508,8 @@ def main(argv=None):
         "data": "synthetic (seeded torch generators; no dataset)",
         "config": dict(step.config(), permute=a.permute,
                        **({"epilogue": "fused_allreduce"} if a.allreduce else {}),
-                       transfer="bidirectional" if a.bidir else "one-way"),
+                       **({"transfer": "bidirectional" if bid else "one-way"}
+                          if a.workload != "attn_outproj_n8" else {})),
         "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),
         "roofline": roof,
         "cpu_baseline": cpu,
