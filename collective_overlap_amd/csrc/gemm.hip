@@ -31,6 +31,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "cce_internal.hpp"
 
@@ -384,8 +385,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int q = 0; q < FM + FN; ++q) fread_one(0, 0, 0, q);
   }
+  // Epilogue geometry: block b = (i, j) = (b % FN, b / FN) holds C^T; the
+  // lane owns row quad_m(b) and columns quad_n(b, q) .. +3 for q = 0..3.
+  void* cbase = a.p.c[g];
+  const float* cin = a.p.cin[g];
+  constexpr int NB = FM * FN;
+  auto quad_m = [&](int b) { return m0 + wm * WTM + (b / FN) * 32 + (lane & 31); };
+  auto quad_n = [&](int b, int q) { return n0 + wn * WTN + (b % FN) * 32 + 8 * q + 4 * (lane >> 5); };
+  // Accumulate mode: the accumulator input of the first NPRE blocks is loaded
+  // into registers during the last k tiles -- PER_IT blocks in each of two
+  // iterations, one load per MFMA slot of the step after the barrier -- so
+  // that its HBM traffic overlaps MFMAs instead of stalling the epilogue.
+  constexpr bool PREF = (EPI == EPI_ACCUM);
+  constexpr int PER_IT = PREF ? NB / 8 : 0;   // blocks per prefetch iteration
+  constexpr int NPRE = 2 * PER_IT;
+  f32x4 cpre[NPRE > 0 ? NPRE : 1][4];
+  // this lane's first accumulator input: row quad_m(0), column quad_n(0, 0)
+  const float* cin_w = PREF ? cin + static_cast<int64_t>(quad_m(0)) * a.ldcin + quad_n(0, 0) : cin;
+
   int cur = 0;                  // buffer of tile kt
-  for (int kt = 0; kt < KT; ++kt) {
+  // One k tile.  PH = 1, 2: also load the accumulator input of prefetch
+  // group PH-1.
+  auto iteration = [&](int kt, auto ph) {
+    constexpr int PH = decltype(ph)::value;
     const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
     const int prv = (cur == 0) ? NS - 1 : cur - 1;   // buffer of tile kt+NS-1
     // Second half of tile kt+NS-1's loads.  At kt = 0 this repeats loads of
@@ -421,35 +443,54 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int d = 0; d < C; ++d)
           if (d * NMF / C == q) dma_one(cur, kadd, d);
+        if constexpr (PH > 0) {
+          if (q < 4 * PER_IT) {
+            // whole tiles only (peel is false at the matrix edges)
+            const int bb = (PH - 1) * PER_IT + q / 4, qq = q % 4;
+            cpre[bb][qq] = *reinterpret_cast<const f32x4*>(
+                cin_w + (bb / FN) * 32 * a.ldcin + (bb % FN) * 32 + 8 * qq);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Forward tile kt+1 (fused permute) after this step's work is issued.
     if (kt + 1 < KT) forward(nxt, kt + 1);
     cur = nxt;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  const bool peel = NPRE > 0 && KT >= 3 && 4 * PER_IT <= NMF && m0 + BM <= a.M && n0 + BN <= a.N;
+  const int KT_main = peel ? KT - 3 : KT;
+  for (int kt = 0; kt < KT_main; ++kt) iteration(kt, P0{});
+  if constexpr (PREF) {
+    if (peel) {
+      iteration(KT - 3, std::integral_constant<int, 1>{});
+      iteration(KT - 2, std::integral_constant<int, 2>{});
+      iteration(KT - 1, P0{});
+    } else {
+#pragma unroll
+      for (int bb = 0; bb < NPRE; ++bb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) cpre[bb][qq] = load_cin_quad(a, cin, quad_m(bb), quad_n(bb, qq));
+    }
   }
   // The last iterations issued loads past K (they land as zeros); drain them
   // before the workgroup's LDS can be handed to another workgroup.
   wait_vmcnt<0>();
 
-  // Epilogue: block (i, j) holds C^T; lane owns row m, columns n..n+3 per quad.
-  // Blocks go one at a time (register pressure); in the accumulate mode the
-  // accumulator input of block b+1 is loaded before block b is finished, so
-  // its memory latency overlaps block b's stores instead of stalling them.
-  void* cbase = a.p.c[g];
-  const float* cin = a.p.cin[g];
-  constexpr int NB = FM * FN;
-  auto quad_m = [&](int b) { return m0 + wm * WTM + (b / FN) * 32 + (lane & 31); };
-  auto quad_n = [&](int b, int q) { return n0 + wn * WTN + (b % FN) * 32 + 8 * q + 4 * (lane >> 5); };
+  // Epilogue, one block at a time (register pressure).  Accumulate mode:
+  // blocks below NPRE take the prefetched input; for the others the input of
+  // block b+1 is loaded before block b is finished, so its latency overlaps
+  // block b's stores.
   f32x4 cb[2][4];
-  if (EPI == EPI_ACCUM) {
+  if (PREF && NPRE < NB) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cb[0][q] = load_cin_quad(a, cin, quad_m(0), quad_n(0, q));
+    for (int q = 0; q < 4; ++q) cb[NPRE & 1][q] = load_cin_quad(a, cin, quad_m(NPRE), quad_n(NPRE, q));
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int i = b % FN, j = b / FN;
-    if (EPI == EPI_ACCUM && b + 1 < NB) {
+    if (PREF && b + 1 > NPRE && b + 1 < NB) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         cb[(b + 1) & 1][q] = load_cin_quad(a, cin, quad_m(b + 1), quad_n(b + 1, q));
@@ -458,8 +499,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
     for (int q = 0; q < 4; ++q) {
       f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                  acc[i][j][4 * q + 3]};
-      store_quad<TOut, EPI, GELU>(a, cbase, quad_m(b), quad_n(b, q), v,
-                                  EPI == EPI_ACCUM ? cb[b & 1][q] : f32x4{});
+      f32x4 cv = f32x4{};
+      if (PREF) cv = (b < NPRE) ? cpre[b < NPRE ? b : 0][q] : cb[b & 1][q];
+      store_quad<TOut, EPI, GELU>(a, cbase, quad_m(b), quad_n(b, q), v, cv);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
