@@ -59,6 +59,10 @@ constexpr int kOob = 0x40000000;
 #endif
 constexpr int kBK = CCE_GEMM_BK;
 constexpr int kNS = CCE_GEMM_NS;
+#ifndef CCE_GEMM_STAGED_STORE
+#define CCE_GEMM_STAGED_STORE 1
+#endif
+constexpr bool kStagedStore = CCE_GEMM_STAGED_STORE;
 // added to steer a load past num_records
 constexpr int64_t kMaxRsrcBytes = kOob - 256;
 
@@ -403,6 +407,48 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // this lane's first accumulator input: row quad_m(0), column quad_n(0, 0)
   const float* cin_w = PREF ? cin + static_cast<int64_t>(quad_m(0)) * a.ldcin + quad_n(0, 0) : cin;
 
+  // bf16 store mode: the result passes through LDS on its way out.  The
+  // accumulators (block (i, j) of a wave holds C^T, the lane 4 consecutive
+  // columns of one row per register quad) are written to LDS row-major and
+  // read back in 16-byte chunks along the rows, so that a wave's store
+  // instruction writes whole rows (1 KB of consecutive bytes) instead of 32
+  // rows x 16 bytes in 8-byte pieces, a pattern that ran at about a third of
+  // the HBM write bandwidth.  Chunk c of staged row r is kept at chunk
+  // c ^ (r & ESW) so that both the 32-row writes and the row reads spread
+  // over the banks.  A tile that does not fit the LDS goes in EP passes of
+  // EJP 32-row blocks per wave.  fp32 results store from the registers: 16
+  // bytes per lane already reach the write bandwidth, and the accumulate
+  // mode is bound by the HBM traffic of its input and output, to which a
+  // round trip through LDS only adds.
+  constexpr bool STAGED = (EPI == EPI_STORE) && sizeof(TOut) == 2 && kStagedStore;
+  constexpr int ESZ = static_cast<int>(sizeof(TOut));
+  constexpr int ERB = BN * ESZ;                  // staged row bytes
+  constexpr int ECR = ERB / 16;                  // chunks per staged row
+  constexpr int EPC = 16 / ESZ;                  // elements per chunk
+  constexpr int EP = (BM * ERB + NS * STAGE - 1) / (NS * STAGE);
+  constexpr int EJP = FM / EP;
+  constexpr int EPR = BM / EP;                   // staged rows per pass
+  constexpr int ERI = 64 * NW / ECR;             // rows per read instruction
+  constexpr int EIT = EPR / ERI;                 // read instructions per pass
+  constexpr int ESW = ECR < 32 ? ECR - 1 : 31;
+  static_assert(!STAGED || (FM % EP == 0 && EPR * ERB <= NS * STAGE && 64 * NW % ECR == 0 &&
+                            32 % ERI == 0 && EPR % ERI == 0),
+                "staged epilogue shape");
+  const bool whole = m0 + BM <= a.M && n0 + BN <= a.N;
+  // 16-byte result rows: chunks inside the matrix are stored as vectors,
+  // the rest element by element.
+  const bool vec = (reinterpret_cast<uintptr_t>(cbase) & 15) == 0 &&
+                   (static_cast<int64_t>(a.ldc) * ESZ) % 16 == 0;
+  // Tile row of read instruction `it` of pass p for thread row 0: staged row
+  // lr = ERI it + tid / ECR belongs to wave row lr / (32 EJP), block
+  // p EJP + (lr / 32) % EJP, row lr % 32 (ERI divides 32, so `it` alone
+  // fixes the block).
+  auto erow = [&](int p, int it) {
+    const int lr = ERI * it;
+    return (lr / (32 * EJP)) * WTM + 32 * (p * EJP + (lr / 32) % EJP) + lr % 32;
+  };
+  const int e_r = tid / ECR, e_c = tid % ECR;
+
   int cur = 0;                  // buffer of tile kt
   // One k tile.  PH = 1, 2: also load the accumulator input of prefetch
   // group PH-1.
@@ -477,6 +523,59 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // The last iterations issued loads past K (they land as zeros); drain them
   // before the workgroup's LDS can be handed to another workgroup.
   wait_vmcnt<0>();
+
+  if constexpr (STAGED) {
+    // every wave's last fragment reads are done before LDS is overwritten
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < EP; ++p) {
+      if (p > 0) __syncthreads();   // the previous pass's reads are done
+#pragma unroll
+      for (int jj = 0; jj < EJP; ++jj) {
+        const int j = p * EJP + jj;
+        const int lr = wm * 32 * EJP + jj * 32 + (lane & 31);
+        char* srow = smem + lr * ERB;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                       acc[i][j][4 * q + 3]};
+            const int byte = (wn * WTN + 32 * i + 8 * q + 4 * (lane >> 5)) * ESZ;
+            char* d = srow + (((byte >> 4) ^ (lr & ESW)) << 4) + (byte & 15);
+            if (GELU) {
+              for (int e = 0; e < 4; ++e) v[e] = gelu_exact(v[e]);
+            }
+            if constexpr (ESZ == 4) {
+              *reinterpret_cast<f32x4*>(d) = v;
+            } else {
+              bf16x4 h;
+              for (int e = 0; e < 4; ++e) h[e] = static_cast<__bf16>(v[e]);
+              *reinterpret_cast<bf16x4*>(d) = h;
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < EIT; ++it) {
+        const int lr = ERI * it + e_r;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + lr * ERB + ((e_c ^ (lr & ESW)) << 4));
+        const int m = m0 + erow(p, it) + e_r;
+        const int n = n0 + EPC * e_c;
+        if (!whole && (m >= a.M || n >= a.N)) continue;
+        TOut* dst = reinterpret_cast<TOut*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
+        if (vec && (whole || n + EPC <= a.N)) {
+          *reinterpret_cast<u32x4*>(dst) = raw;
+        } else {
+          const TOut* src = reinterpret_cast<const TOut*>(&raw);
+          for (int e = 0; e < EPC; ++e)
+            if (n + e < a.N) dst[e] = src[e];
+        }
+      }
+    }
+    return;
+  }
 
   // Epilogue, one block at a time (register pressure).  Accumulate mode:
   // blocks below NPRE take the prefetched input; for the others the input of
