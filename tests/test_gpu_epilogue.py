@@ -189,3 +189,66 @@ def test_fused_allreduce(ctx, case):
             assert_f32_close(np64(outs[r]), ref[r], f"rank {r}", tol=1e-6)
         else:
             assert_bf16_close(np64(outs[r]), ref[r], f"rank {r}")
+
+
+VECTOR = [
+    # rows, cols, n, part, out, p, bias, residual, row0, col0, mask_ld
+    (64, 512, 1, "f32", "bf16", 0.1, True, True, 0, 0, None),
+    (33, 264, 2, "f32", "f32", 0.3, True, False, 0, 0, None),
+    (40, 1024, 8, "bf16", "bf16", 0.1, True, True, 0, 0, None),     # general kernel both ways
+    (17, 96, 2, "bf16", "f32", 1.0, False, True, 0, 0, None),
+    (17, 96, 2, "bf16", "bf16", 0.0, True, True, 0, 0, None),
+    (9, 2056, 1, "bf16", "bf16", 0.5, True, True, 7, 4, 3000),
+    (65600, 8, 1, "f32", "f32", 0.1, True, True, 0, 0, None),   # more rows than one grid row each
+]
+
+
+@pytest.mark.parametrize("case", VECTOR)
+def test_vector_kernel_equals_general_kernel(ctx, case):
+    """Calls without a mask output take the vector kernel (one or two
+    partials, whole 8-column vectors, aligned mask index, at most 65535 rows);
+    asking for the mask forces the general kernel.  Both give the same bits,
+    and the oracle's values."""
+    import collective_overlap_amd as cce
+    rows, cols, n, pt, ot, p, has_b, has_r, r0, c0, mld = case
+    print(f"[gpu] vector epilogue {case}", flush=True)
+    pdt = torch.float32 if pt == "f32" else torch.bfloat16
+    odt = torch.float32 if ot == "f32" else torch.bfloat16
+    parts = [_mk((rows, cols), 400 + k, pdt) for k in range(n)]
+    bias = W.normal((cols,), 0.02, 90, device=DEV, dtype=odt) if has_b else None
+    res = _mk((rows, cols), 91, odt) if has_r else None
+    fast = torch.full((rows, cols), float("nan"), device=DEV, dtype=odt)
+    gen = torch.full((rows, cols), float("nan"), device=DEV, dtype=odt)
+    mask = torch.empty((rows, cols), device=DEV, dtype=torch.uint8)
+    cce.cce_fused_reduce_epilogue(ctx, parts, bias, res, fast, p, 3, 1, r0, c0, mld)
+    cce.cce_fused_reduce_epilogue(ctx, parts, bias, res, gen, p, 3, 1, r0, c0, mld, mask_out=mask)
+    sync()
+    it = torch.int16 if odt == torch.bfloat16 else torch.int32
+    assert torch.equal(fast.view(it), gen.view(it))
+    ref, keep = oep.fused_reduce_epilogue([np64(x) for x in parts],
+                                          np64(bias) if has_b else None,
+                                          np64(res) if has_r else None, p, 3, 1, r0, c0,
+                                          mld if mld else c0 + cols)
+    assert np.array_equal(mask.cpu().numpy().astype(bool), keep)
+    if ot == "f32":
+        assert_f32_close(np64(fast), ref, "vector epilogue", tol=1e-6)
+    else:
+        assert_bf16_close(np64(fast), ref, "vector epilogue")
+
+
+def test_vector_kernel_replicas(ctx):
+    """FusedAllReduce without a mask output (vector kernel, every replica
+    stored) against the same call with one (general kernel)."""
+    import collective_overlap_amd as cce
+    n, rows, cols = 2, 96, 1024
+    parts = [_mk((rows, cols), 500 + r, torch.bfloat16) for r in range(n)]
+    bias = W.normal((cols,), 0.02, 90, device=DEV, dtype=torch.bfloat16)
+    res = _mk((rows, cols), 91, torch.bfloat16)
+    fast = [torch.full((rows, cols), float("nan"), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    gen = [torch.full((rows, cols), float("nan"), device=DEV, dtype=torch.bfloat16) for _ in range(n)]
+    mask = torch.empty((rows, cols), device=DEV, dtype=torch.uint8)
+    cce.cce_fused_allreduce_epilogue(ctx, parts, bias, res, fast, 0.1, 4, 2)
+    cce.cce_fused_allreduce_epilogue(ctx, parts, bias, res, gen, 0.1, 4, 2, mask_out=mask)
+    sync()
+    for r in range(n):
+        assert torch.equal(fast[r].view(torch.int16), gen[r].view(torch.int16)), f"replica {r}"
