@@ -83,17 +83,29 @@ class Gpt3Ffn:
                 "ffn": self.F, "w1_shard": [self.Hd, self.fs], "w2_shard": [self.fs, self.Hd],
                 "p_drop": self.p, "acc_dtype": "f32", "global_batch": self.T}
 
+    # False: the ReduceScatter stores its fp32 result, and a second call
+    # applies the epilogue (bench.py --separate-epilogue)
+    fuse_epilogue = True
+
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
         cce.cce_looped_allgather_einsum(ctx, "lhs_rows", self.X, self.W1, self.H, self.ws_ag,
                                         flags=flags | cce.CCE_FLAG_GELU)
+        rows0 = [r * self.ts for r in range(self.n)]
+        if self.fuse_epilogue:
+            # The ReduceScatter hands its accumulators straight to the fused
+            # bias + dropout + residual epilogue (one launch over the ranks).
+            cce.cce_looped_einsum_reducescatter_epilogue(
+                ctx, "slice_lhs_rows", self.H, self.W2, self.b, self.R, self.out, self.p, 0, 0,
+                mask_row0=rows0, mask_col0=0, mask_ld=self.Hd, workspace=self.ws_rs, flags=flags)
+            return
         cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", self.H, self.W2, self.acc,
                                             self.ws_rs, flags=flags)
         # One launch for the 8 ranks' shards (each rank's slice of the
         # reduced tensor gets bias, dropout and residual).
         cce.cce_fused_reduce_epilogue_batched(
             ctx, [[a] for a in self.acc], self.b, self.R, self.out, self.p, 0, 0,
-            mask_row0=[r * self.ts for r in range(self.n)], mask_col0=0, mask_ld=self.Hd)
+            mask_row0=rows0, mask_col0=0, mask_ld=self.Hd)
 
     def oracle_sample(self, t=8):
         """The oracle end to end on t tokens of every shard; returns
@@ -383,6 +395,10 @@ def main(argv=None):
                          "ceil(n/2) iterations; one-way: the ring of the loop's pairs only")
     ap.add_argument("--allreduce", action="store_true",
                     help="attn_outproj_n8: FusedAllReduce epilogue, the result on every rank")
+    ap.add_argument("--separate-epilogue", action="store_true",
+                    help="gpt3_ffn_n8: the ReduceScatter stores its fp32 result and a second "
+                         "call applies the epilogue (default: one call, the accumulators go "
+                         "straight into the epilogue)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -418,6 +434,10 @@ def main(argv=None):
         if not hasattr(step, "use_allreduce"):
             raise SystemExit("--allreduce applies to attn_outproj_n8 only")
         step.use_allreduce()
+    if a.separate_epilogue:
+        if not hasattr(step, "fuse_epilogue"):
+            raise SystemExit("--separate-epilogue applies to gpt3_ffn_n8 only")
+        step.fuse_epilogue = False
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     log("inputs ready; warmup")
@@ -508,6 +528,8 @@ def main(argv=None):
         "data": "synthetic (seeded torch generators; no dataset)",
         "config": dict(step.config(), permute=a.permute,
                        **({"epilogue": "fused_allreduce"} if a.allreduce else {}),
+                       **({"epilogue": "in the ReduceScatter" if step.fuse_epilogue
+                           else "separate call"} if hasattr(step, "fuse_epilogue") else {}),
                        **({"transfer": "bidirectional" if bid else "one-way"}
                           if a.workload != "attn_outproj_n8" else {})),
         "frac_of_mfma_peak": round(value / PEAK_TFLOPS[step.dtype], 4),

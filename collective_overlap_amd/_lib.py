@@ -66,6 +66,11 @@ PROTOTYPES = {
     "cce_looped_einsum_reducescatter_workspace": (_I, [_I, _I, _I, cce_mat, ctypes.POINTER(_SZ)]),
     "cce_looped_einsum_reducescatter": (_I, [_P, _I, _I, _I, _I, _I, _PP, cce_mat, _PP, cce_mat,
                                              _PP, cce_mat, _P, _SZ, _U32, _P]),
+    "cce_looped_einsum_reducescatter_epilogue": (_I, [_P, _I, _I, _I, _I, _PP, cce_mat, _PP,
+                                                      cce_mat, _P, _PP, _I64, ctypes.c_double,
+                                                      _U64, _U64, ctypes.POINTER(ctypes.c_int64),
+                                                      _I64, _I64, _PP, cce_mat, _P, _SZ, _U32,
+                                                      _P]),
     "cce_grouped_gemm": (_I, [_P, _I, _I, _I, _PP, cce_mat, _PP, cce_mat, _PP, cce_mat, _U32, _P]),
     "cce_fused_reduce_epilogue": (_I, [_P, _I, _I, _PP, cce_mat, _P, _I, _P, _I, _I64,
                                        ctypes.c_double, _U64, _U64, _I64, _I64, _I64, _P, _I,

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -470,6 +471,20 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
   return CCE_OK;
 }
 
+// The fused reduce epilogue applied to a ReduceScatter's fp32 result
+// (cce_looped_einsum_reducescatter_epilogue).
+struct RsEpi {
+  const void* bias = nullptr;
+  const void* const* res = nullptr;   // [n] or NULL
+  int64_t ld_res = 0;
+  bool dropout = false, drop_all = false;
+  uint32_t threshold = 0;
+  float scale = 1.0f;
+  uint64_t seed = 0, offset = 0;
+  const int64_t* mrow0 = nullptr;     // [n]
+  int64_t mcol0 = 0, mld = 0;
+};
+
 struct RsCall {
   RsGeom g;
   cce_dtype in_t, out_t;
@@ -481,6 +496,7 @@ struct RsCall {
   cce_mat oshape;
   char* ws;
   hipMemcpyKind copy_kind;
+  const RsEpi* epi = nullptr;
 };
 
 PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
@@ -506,9 +522,63 @@ PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
   return {nullptr, 0};
 }
 
+// One batched launch of the fused epilogue over every rank's half h of the
+// output: src[r] holds rank r's fp32 partial(s) (one in the one-way form, the
+// cw and ccw accumulators in the two-way form), which are summed first.
+cce_status rs_epilogue(cce_ctx* ctx, const RsCall& c, int h, int n_part,
+                       const std::vector<std::array<PtrLd, 2>>& src, hipStream_t s) {
+  const RsEpi& x = *c.epi;
+  const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
+  const int64_t ext = (h == 0) ? c.g.h0 : c.g.h1;
+  const int64_t base = h * c.g.h0;            // first row (or column) of the half
+  const size_t eo = esize(c.out_t);
+  EpilogueLaunch E;
+  E.n = n_part;
+  E.batch = c.g.n;
+  E.part_t = CCE_F32;
+  E.rows = rows_mode ? ext : c.g.other;
+  E.cols = rows_mode ? c.g.other : ext;
+  if (E.rows == 0 || E.cols == 0) return CCE_OK;
+  E.ld_part = c.g.acc_ld;
+  E.bias = x.bias ? static_cast<const char*>(x.bias) + (rows_mode ? 0 : base * eo) : nullptr;
+  E.bias_t = c.out_t;
+  E.res_t = c.out_t;
+  E.ld_res = x.ld_res;
+  E.out_t = c.out_t;
+  E.ld_out = c.oshape.ld;
+  E.threshold = x.threshold;
+  E.drop_all = x.drop_all;
+  E.dropout = x.dropout;
+  E.scale = x.scale;
+  E.seed = x.seed;
+  E.offset = x.offset;
+  E.mcol0 = x.mcol0 + (rows_mode ? 0 : base);
+  E.mld = x.mld;
+  for (int r = 0; r < c.g.n; ++r) {
+    for (int k = 0; k < n_part; ++k) E.parts[r * n_part + k] = src[r][k].p;
+    E.res[r] = x.res ? static_cast<const char*>(x.res[r]) +
+                           (rows_mode ? base * x.ld_res * static_cast<int64_t>(eo) : base * eo)
+                     : nullptr;
+    E.out[r] = rs_resolve(c, BufRef{B_OUT, 0, static_cast<uint8_t>(h), static_cast<int16_t>(r)}).p;
+    E.mask[r] = nullptr;
+    E.mrow0[r] = x.mrow0[r] + (rows_mode ? base : 0);
+  }
+  const double bytes = static_cast<double>(E.batch) * E.rows * E.cols *
+                           (4.0 * n_part + (x.res ? eo : 0) + eo) +
+                       (x.bias ? static_cast<double>(E.cols) * eo : 0.0);
+  int slot;
+  CCE_TRY(prof_begin(ctx, s, 2, -1, 0.0, bytes, &slot));
+  CCE_TRY(launch_fused_epilogue(E, s));
+  return prof_end(ctx, s, slot);
+}
+
 cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream_t compute) {
   const size_t ein = esize(c.in_t);
   const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
+  // one-way form with the fused epilogue: where each rank's result half ends
+  std::vector<std::array<PtrLd, 2>> final_acc[2] = {std::vector<std::array<PtrLd, 2>>(c.g.n),
+                                                    std::vector<std::array<PtrLd, 2>>(c.g.n)};
+  bool has_final[2] = {false, false};
   for (const Op& o : plan.ops) {
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
     if (o.kind == OP_RECORD || o.kind == OP_WAIT) {
@@ -516,6 +586,14 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       continue;
     }
     const int64_t ext = (o.half == 0) ? c.g.h0 : c.g.h1;   // extent along the sliced dim
+    if (o.kind == OP_SUM && c.epi) {
+      // Two-way form with the fused epilogue: the cw and ccw accumulators go
+      // straight into it and are summed before the bias (never stored).
+      std::vector<std::array<PtrLd, 2>> src(c.g.n);
+      for (const Item& it : o.items) src[it.c.rank] = {rs_resolve(c, it.a), rs_resolve(c, it.cin)};
+      CCE_TRY(rs_epilogue(ctx, c, o.half, 2, src, compute));
+      continue;
+    }
     if (o.kind == OP_SUM) {
       // Align-and-sum of the bidirectional form: out = cw + ccw, one batched
       // epilogue launch (two fp32 partials per rank, no bias, no dropout).
@@ -578,8 +656,18 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
     for (const Item& it : o.items) {
       const int r = gi++;
       const int64_t t = it.shard;
-      const PtrLd A = rs_resolve(c, it.a), B = rs_resolve(c, it.b), D = rs_resolve(c, it.c);
+      const PtrLd A = rs_resolve(c, it.a), B = rs_resolve(c, it.b);
+      PtrLd D = rs_resolve(c, it.c);
       L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
+      if (c.epi && it.c.kind == B_OUT) {
+        // One-way form with the fused epilogue: the last partial accumulates
+        // in place into the received accumulator (every element is read
+        // before it is written, by the same lane), which the epilogue reads.
+        D = rs_resolve(c, it.cin);
+        L.out_t = CCE_F32;
+        final_acc[o.half][it.c.rank] = {D, D};
+        has_final[o.half] = true;
+      }
       const int64_t off = t * c.g.shard + o.half * c.g.h0;     // start along the sliced dim
       if (rows_mode) {
         L.p.a[r] = A.p + off * A.ld * ein;
@@ -607,6 +695,8 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       CCE_TRY(prof_end(ctx, compute, slot));
     }
   }
+  for (int h = 0; h < 2; ++h)
+    if (has_final[h]) CCE_TRY(rs_epilogue(ctx, c, h, 1, final_acc[h], compute));
   return CCE_OK;
 }
 
@@ -808,14 +898,23 @@ cce_status cce_looped_einsum_reducescatter_workspace(int n_ranks, cce_rs_mode mo
   return CCE_OK;
 }
 
-cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,
-                                           cce_dtype in_t, cce_dtype acc_t, cce_dtype out_t,
-                                           const void* const* a, cce_mat a_shape,
-                                           const void* const* b, cce_mat b_shape,
-                                           void* const* out, cce_mat out_shard, void* workspace,
-                                           size_t workspace_bytes, uint32_t flags,
-                                           cce_stream stream) {
-  clear_error();
+// The epilogue's arguments as the caller gives them.
+struct RsEpiArgs {
+  const void* bias;
+  const void* const* res;
+  int64_t ld_res;
+  double p_drop;
+  uint64_t seed, offset;
+  const int64_t* mrow0;
+  int64_t mcol0, mld;
+};
+
+static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype in_t,
+                          cce_dtype acc_t, cce_dtype out_t, const void* const* a,
+                          cce_mat a_shape, const void* const* b, cce_mat b_shape,
+                          void* const* out, cce_mat out_shard, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, cce_stream stream,
+                          const RsEpiArgs* ea) {
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
                 CCE_FLAG_BIDIRECTIONAL))
@@ -846,6 +945,35 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
                 os = span_bytes(out_shard, eout);
   if (as > kMaxOperandBytes || bs > kMaxOperandBytes)
     return fail(CCE_EUNSUPPORTED, "a GEMM operand exceeds 1 GiB");
+  RsEpi epi;
+  if (ea) {
+    // The epilogue reads the result from the workspace's accumulators.
+    if (n_ranks < 2)
+      return fail(CCE_EUNSUPPORTED, "the fused epilogue needs n_ranks >= 2 (with one rank, use "
+                                    "cce_grouped_gemm and cce_fused_reduce_epilogue)");
+    if (std::isnan(ea->p_drop)) return fail(CCE_EINVAL, "p_drop is NaN");
+    if (!ea->mrow0) return fail(CCE_EINVAL, "mask_row0 is NULL");
+    if (ea->mcol0 < 0 || ea->mld < ea->mcol0 + out_shard.cols)
+      return fail(CCE_EINVAL, "mask index base must satisfy 0 <= col0, col0 + cols <= mask_ld");
+    for (int r = 0; r < n_ranks; ++r)
+      if (ea->mrow0[r] < 0) return fail(CCE_EINVAL, "mask row base must be >= 0");
+    if (ea->res) CCE_TRY(check_mat("residual", cce_mat{out_shard.rows, out_shard.cols, ea->ld_res}));
+    epi.bias = ea->bias;
+    epi.res = ea->res;
+    epi.ld_res = ea->ld_res;
+    epi.seed = ea->seed;
+    epi.offset = ea->offset;
+    epi.mrow0 = ea->mrow0;
+    epi.mcol0 = ea->mcol0;
+    epi.mld = ea->mld;
+    if (ea->p_drop >= 1.0) {
+      epi.drop_all = true;
+    } else if (ea->p_drop > 0.0) {
+      epi.dropout = true;
+      epi.threshold = static_cast<uint32_t>(std::floor(ea->p_drop * 4294967296.0));
+      epi.scale = static_cast<float>(1.0 / (1.0 - ea->p_drop));
+    }
+  }
   std::vector<Range> ranges;
   for (int r = 0; r < n_ranks; ++r) {
     const std::string rs = std::to_string(r);
@@ -855,6 +983,16 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
     ranges.push_back(range_of(a[r], as, "a[" + rs + "]", false));
     ranges.push_back(range_of(b[r], bs, "b[" + rs + "]", false));
     ranges.push_back(range_of(out[r], os, "out[" + rs + "]", true));
+    if (ea && ea->res) {
+      const int64_t rsz = span_bytes(cce_mat{out_shard.rows, out_shard.cols, ea->ld_res}, eout);
+      CCE_TRY(check_ptr(("residual[" + rs + "]").c_str(), ea->res[r], rsz));
+      ranges.push_back(range_of(ea->res[r], rsz, "residual[" + rs + "]", false));
+    }
+  }
+  if (ea && ea->bias) {
+    const int64_t bsz = out_shard.cols * static_cast<int64_t>(eout);
+    CCE_TRY(check_ptr("bias", ea->bias, bsz));
+    ranges.push_back(range_of(ea->bias, bsz, "bias", false));
   }
   if (g.total > 0) {
     if (!workspace || workspace_bytes < static_cast<size_t>(g.total))
@@ -872,7 +1010,33 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
   CCE_TRY(ensure_events(ctx, plan.n_events));
   RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
            copy_kind(flags)};
+  c.epi = ea ? &epi : nullptr;
   return rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
+}
+
+cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,
+                                           cce_dtype in_t, cce_dtype acc_t, cce_dtype out_t,
+                                           const void* const* a, cce_mat a_shape,
+                                           const void* const* b, cce_mat b_shape,
+                                           void* const* out, cce_mat out_shard, void* workspace,
+                                           size_t workspace_bytes, uint32_t flags,
+                                           cce_stream stream) {
+  clear_error();
+  return rs_impl(ctx, n_ranks, mode, in_t, acc_t, out_t, a, a_shape, b, b_shape, out, out_shard,
+                 workspace, workspace_bytes, flags, stream, nullptr);
+}
+
+cce_status cce_looped_einsum_reducescatter_epilogue(
+    cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype in_t, cce_dtype out_t,
+    const void* const* a, cce_mat a_shape, const void* const* b, cce_mat b_shape,
+    const void* bias, const void* const* residuals, int64_t ld_res, double p_drop,
+    uint64_t seed, uint64_t offset, const int64_t* mask_row0, int64_t mask_col0,
+    int64_t mask_ld, void* const* out, cce_mat out_shard, void* workspace,
+    size_t workspace_bytes, uint32_t flags, cce_stream stream) {
+  clear_error();
+  const RsEpiArgs ea{bias, residuals, ld_res, p_drop, seed, offset, mask_row0, mask_col0, mask_ld};
+  return rs_impl(ctx, n_ranks, mode, in_t, CCE_F32, out_t, a, a_shape, b, b_shape, out, out_shard,
+                 workspace, workspace_bytes, flags, stream, &ea);
 }
 
 cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtype out_t,

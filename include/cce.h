@@ -256,6 +256,40 @@ cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mod
                                            uint32_t flags, cce_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Looped Einsum-ReduceScatter with the fused reduce epilogue
+ * ([OV] Sections 4, 5.1, 5.4.1 and 5.4.2; [CC] Figure 3 program).
+ *
+ *   out[r] = residual[r] + keep * (S_r + bias) * c,   c = 1 / (1 - p_drop)
+ *
+ * where S_r is the fp32 result that cce_looped_einsum_reducescatter gives
+ * for rank r with the same a, b, mode and flags.  The result is, bit for
+ * bit, that call with out_t = CCE_F32 followed by
+ * cce_fused_reduce_epilogue_batched over the ranks (one partial each, the
+ * same bias, residuals, dropout and mask arguments), without storing S_r in
+ * the caller's memory:
+ *   - with CCE_FLAG_BIDIRECTIONAL the two chains' accumulators go straight
+ *     into the epilogue, which sums them (cw + ccw, the align-and-sum's
+ *     order) before the bias: the sum is never stored;
+ *   - in the one-way form the last iteration leaves S_r in the workspace and
+ *     one batched epilogue launch reads it from there.
+ * Arguments: as cce_looped_einsum_reducescatter (acc_t is CCE_F32), plus
+ * the epilogue's: bias [out cols] of out_t or NULL; residuals NULL or n_ranks
+ * pointers to [out rows, out cols] arrays of out_t with ld_res; dropout,
+ * seed, offset and the keep mask as cce_fused_reduce_epilogue, with
+ * mask_row0[r] the global row of rank r's first output row.  out[r] of
+ * out_t (CCE_F32 or CCE_BF16) with out_shard.ld.  The workspace is the one
+ * cce_looped_einsum_reducescatter_workspace returns.  flags: those of
+ * cce_looped_einsum_reducescatter.  No mask output.
+ * ---------------------------------------------------------------------- */
+cce_status cce_looped_einsum_reducescatter_epilogue(
+    cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype in_t, cce_dtype out_t,
+    const void* const* a, cce_mat a_shape, const void* const* b, cce_mat b_shape,
+    const void* bias, const void* const* residuals, int64_t ld_res, double p_drop,
+    uint64_t seed, uint64_t offset, const int64_t* mask_row0, int64_t mask_col0,
+    int64_t mask_ld, void* const* out, cce_mat out_shard, void* workspace,
+    size_t workspace_bytes, uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
  * Grouped local GEMM: c[g] = a[g] * b[g]^T for g < n_groups, one launch.
  * This is the per-rank MatMul of two tensors sliced on the contraction dim,
  * producing one local partial per rank ([CC] Figure 3 program, the MatMul

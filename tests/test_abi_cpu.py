@@ -235,6 +235,9 @@ def test_null_context_rejected_before_any_work(cce):
     assert cce.cce_fused_reduce_epilogue_batched(None, 2, 1, 0, arr, m, None, 0, None, 0, 8,
                                                  0.1, 0, 0, rows0, 0, 8, arr, 0, 8, None, 0,
                                                  None) == 1
+    assert cce.cce_looped_einsum_reducescatter_epilogue(None, 2, 0, 1, 1, arr, cce_mat(16, 8, 8),
+                                                        arr, m, None, None, 8, 0.1, 0, 0, rows0,
+                                                        0, 8, arr, m, None, 0, 0, None) == 1
 
 
 # ---------------------------------------------------------------------------
