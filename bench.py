@@ -107,6 +107,21 @@ class Gpt3Ffn:
             ctx, [[a] for a in self.acc], self.b, self.R, self.out, self.p, 0, 0,
             mask_row0=rows0, mask_col0=0, mask_ld=self.Hd)
 
+    def monolithic(self):
+        """The same two layers unlooped, on pre-gathered operands: one grouped
+        GEMM per layer (H_r = GELU(X_all W1_r), P_r = H_r W2_r in fp32, the
+        full per-rank partial that a plain ReduceScatter would then reduce).
+        Returns a callable running both; no permutes, no epilogue."""
+        import torch
+        import collective_overlap_amd as cce
+        x_all = torch.cat(self.X)                       # [T, Hd], gathered
+        parts = [torch.empty((self.T, self.Hd), device=x_all.device) for _ in range(self.n)]
+
+        def run(ctx):
+            cce.cce_grouped_gemm(ctx, [x_all] * self.n, self.W1, self.H, gelu=True)
+            cce.cce_grouped_gemm(ctx, self.H, self.W2, parts)
+        return run
+
     def oracle_sample(self, t=8):
         """The oracle end to end on t tokens of every shard; returns
         (seconds, flops, description, rel error vs the device outputs)."""
@@ -466,6 +481,26 @@ def main(argv=None):
                     "bytes_per_launch": tb / len(epi)}
     gemm_ms = sum(r["ms"] for r in recs if r["kind"] == "gemm") / a.steps
 
+    mono = None
+    if hasattr(step, "monolithic") and not a.no_serial:
+        # The decomposition's cost: the same FLOPs as one grouped GEMM per
+        # layer on pre-gathered operands, against the looped step.
+        log("timed region: the same layers unlooped (monolithic grouped GEMMs)")
+        run_mono = step.monolithic()
+        for _ in range(max(1, a.warmup // 2)):
+            run_mono(ctx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            run_mono(ctx)
+        torch.cuda.synchronize()
+        mono_ms = (time.perf_counter() - t0) / a.steps * 1e3
+        mono = {"ms": round(mono_ms, 4), "TFLOP/s": round(step.flops / (mono_ms * 1e-3) / 1e12, 2),
+                "looped_step_over_monolithic": round(ms_per_step / mono_ms, 4),
+                "looped_gemms_over_monolithic": round(gemm_ms / mono_ms, 4)}
+        del run_mono
+        torch.cuda.empty_cache()
+
     overlap = None
     has_permute = a.workload not in ("attn_outproj_n8",)
     if not a.no_serial and has_permute:
@@ -537,6 +572,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "epilogue": epi_info,
         "overlap": overlap,
+        "monolithic": mono,
         "gemm_ms_per_step": round(gemm_ms, 3),
         "gemm_shapes": list(per_shape.values()),
         "parity": parity,
