@@ -227,6 +227,18 @@ class Mlp2:
                                         flags=flags | cce.CCE_FLAG_GELU)
         cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W2, self.H, self.Y, flags=flags)
 
+    def monolithic(self):
+        """Both layers unlooped: each rank multiplies by the gathered weights
+        (the shards concatenated), one grouped GEMM per layer."""
+        import torch
+        import collective_overlap_amd as cce
+        w1, w2 = torch.cat(self.W1), torch.cat(self.W2)     # [Hh, F], [F, Hh]
+
+        def run(ctx):
+            cce.cce_grouped_gemm(ctx, self.X, [w1] * self.n, self.H, gelu=True)
+            cce.cce_grouped_gemm(ctx, self.H, [w2] * self.n, self.Y)
+        return run
+
     def oracle_sample(self, t=8):
         import numpy as np
         from oracle import einsum as oe, numerics
@@ -268,6 +280,17 @@ class RsN8:
         import collective_overlap_amd as cce
         cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", self.X, self.Wt, self.out,
                                             flags=flags)
+
+    def monolithic(self):
+        """Every rank's full fp32 partial X_r W_r (what a plain ReduceScatter
+        would then reduce), one grouped GEMM."""
+        import torch
+        import collective_overlap_amd as cce
+        parts = [torch.empty((self.T, self.N), device=self.X[0].device) for _ in range(self.n)]
+
+        def run(ctx):
+            cce.cce_grouped_gemm(ctx, self.X, self.Wt, parts)
+        return run
 
     def oracle_sample(self, t=16):
         import numpy as np
