@@ -153,15 +153,19 @@ def test_rs_n8_full(ctx, flags):
         assert_f32_close(np64(out[r][rows][:, cols]), ref, f"shard {r}")
 
 
-@pytest.mark.parametrize("flags,batched", [(0, False), (0x8, True), (0x18, True)])
-def test_gpt3_ffn_n8_full(ctx, flags, batched):
+@pytest.mark.parametrize("flags,batched,in_rs", [(0, False, False), (0x8, True, False),
+                                                 (0x18, True, False), (0x18, True, True),
+                                                 (0x8, True, True)])
+def test_gpt3_ffn_n8_full(ctx, flags, batched, in_rs):
     """GPT-3 FFN, 8-way: looped AllGather into W1 shards with GELU, looped
     ReduceScatter out of W2 shards, fused bias+dropout+residual; sampled.
-    Run in the copy-stream form with one epilogue per rank, and in the
-    benchmark's configurations: fused permute (one-way and two-way ring) with
-    the batched epilogue."""
+    Run in the copy-stream form with one epilogue per rank, in the fused
+    permute (one-way and two-way ring) with the batched epilogue, and with the
+    epilogue inside the ReduceScatter (the benchmark's configuration: fused
+    permute, two-way ring), whose output must equal the two-call path's bit
+    for bit."""
     import collective_overlap_amd as cce
-    print(f"[gpu] gpt3_ffn_n8 full flags={flags} batched={batched}", flush=True)
+    print(f"[gpu] gpt3_ffn_n8 full flags={flags} batched={batched} in_rs={in_rs}", flush=True)
     n = 8
     X = [W.normal((1024, 12288), 1.0, s, device=DEV) for s in range(n)]
     W1 = [W.weight_store(12288, 6144, 0.02, 10 + r, device=DEV) for r in range(n)]
@@ -181,6 +185,14 @@ def test_gpt3_ffn_n8_full(ctx, flags, batched):
         for r in range(n):
             cce.cce_fused_reduce_epilogue(ctx, [acc[r]], b, R[r], out[r], 0.1, 0, 0,
                                           mask_row0=r * 1024, mask_col0=0, mask_ld=12288)
+    if in_rs:
+        fused = [torch.empty((1024, 12288), device=DEV, dtype=BF) for _ in range(n)]
+        cce.cce_looped_einsum_reducescatter_epilogue(
+            ctx, "slice_lhs_rows", H, W2, b, R, fused, 0.1, 0, 0,
+            mask_row0=[r * 1024 for r in range(n)], mask_col0=0, mask_ld=12288, flags=flags)
+        sync()
+        for r in range(n):
+            assert torch.equal(fused[r].view(torch.int16), out[r].view(torch.int16)), f"rank {r}"
     sync()
     # layer 1: H_r rows (global tokens) x sampled FFN columns
     grow = _rows(8, 8192, 7)
