@@ -33,6 +33,9 @@ def allgather_einsum(mode: str, looped: list[np.ndarray],
       rhs_cols : Y_r = A_r @ concat_cols(B_0..B_{N-1})      (case 1)
       lhs_cols : Y_r = concat_cols(A_0..A_{N-1}) @ B_r      (case 2)
       rhs_rows : Y_r = A_r @ concat_rows(B_0..B_{N-1})      (case 2)
+      lhs_batch: Y_r = concat_batch(A_0..A_{N-1}) @ B_r     (case 3)
+                 A_s [b_s, m, k], B_r [N b_s, k, n]: one matmul per batch
+                 element, Y_r [N b_s, m, n]
     """
     if mode == "lhs_rows":
         full = allgather(looped, axis=0)
@@ -46,6 +49,9 @@ def allgather_einsum(mode: str, looped: list[np.ndarray],
     if mode == "rhs_rows":
         full = allgather(looped, axis=0)
         return [a @ full for a in local]
+    if mode == "lhs_batch":
+        full = allgather(looped, axis=0)            # [N b_s, m, k]
+        return [np.matmul(full, b) for b in local]
     raise ValueError(mode)
 
 

@@ -85,6 +85,8 @@ def allreduce(fulls: list[np.ndarray]) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 AG_MODES = ("lhs_rows", "rhs_cols", "lhs_cols", "rhs_rows")
+# case 3: batched operands (3-D arrays), the looped factor split on the batch dim
+AG_BATCH_MODES = ("lhs_batch",)
 RS_MODES = ("slice_lhs_rows", "slice_rhs_cols")
 
 
@@ -99,6 +101,10 @@ def _ag_partial(mode: str, held: np.ndarray, local: np.ndarray, shard_id: int):
       case 2 ([OV] 5.1): the looped factor is split on the contracting dim;
         the local factor is DynamicSliced along its contracting dim with the
         size of the looped shard, at the looped shard's ID.
+      case 3 ([OV] 5.1): the looped factor is split on the batch dim; the
+        local factor is DynamicSliced along its batch dim, at the looped
+        shard's ID, with the looped shard's batch extent (the reading of the
+        slice size), and the product is one matmul per batch element.
     """
     if mode == "rhs_cols":          # held = B_s [K, n_s], local = A_r [M, K]
         return local @ held
@@ -110,12 +116,19 @@ def _ag_partial(mode: str, held: np.ndarray, local: np.ndarray, shard_id: int):
     if mode == "rhs_rows":          # held = B_s [k_s, N], local = A_r [M, K]
         ks = held.shape[0]
         return local[:, shard_id * ks:(shard_id + 1) * ks] @ held
+    if mode == "lhs_batch":         # held = A_s [b_s, m, K], local = B_r [N b_s, K, N]
+        bs = held.shape[0]
+        return np.matmul(held, local[shard_id * bs:(shard_id + 1) * bs])
     raise ValueError(mode)
 
 
 def _ag_update(mode: str, out: np.ndarray, part: np.ndarray, shard_id: int):
-    """Update of [OV] 5.1: DynamicUpdateSlice for case 1, Addition for case 2."""
-    if mode == "rhs_cols":
+    """Update of [OV] 5.1: DynamicUpdateSlice for cases 1 and 3 (along the
+    batch dim for case 3), Addition for case 2."""
+    if mode == "lhs_batch":
+        bs = part.shape[0]
+        out[shard_id * bs:(shard_id + 1) * bs] = part
+    elif mode == "rhs_cols":
         w = part.shape[1]
         out[:, shard_id * w:(shard_id + 1) * w] = part
     elif mode == "lhs_rows":
@@ -135,6 +148,8 @@ def _ag_out_shape(mode: str, n: int, shard: np.ndarray, local: np.ndarray):
         return (shard.shape[0], local.shape[1])
     if mode == "rhs_rows":
         return (local.shape[0], shard.shape[1])
+    if mode == "lhs_batch":
+        return (n * shard.shape[0], shard.shape[1], local.shape[2])
     raise ValueError(mode)
 
 
@@ -155,7 +170,7 @@ def simulate_allgather_einsum(mode: str, looped: list[np.ndarray],
       transfers[i]    -- list of (src, dst, shard_id) moved in iteration i.
     """
     n = len(looped)
-    assert mode in AG_MODES and len(local) == n
+    assert mode in AG_MODES + AG_BATCH_MODES and len(local) == n
     held = [(looped[r], r) for r in range(n)]       # aligned at loop start
     outs = [np.zeros(_ag_out_shape(mode, n, looped[0], local[r]))
             for r in range(n)]
@@ -284,7 +299,7 @@ def simulate_allgather_einsum_bidir(mode: str, looped: list[np.ndarray],
                          phase "prologue" or the iteration index.
     """
     n = len(looped)
-    assert mode in AG_MODES and len(local) == n
+    assert mode in AG_MODES + AG_BATCH_MODES and len(local) == n
     k_cw, k_ccw = bidir_lengths(n)
     cw_pairs, ccw_pairs = ring_pairs(n), reversed_ring_pairs(n)
     own = [(looped[r], r) for r in range(n)]

@@ -158,3 +158,75 @@ def test_allgather_einsum_backward_matches_autograd(mode, n):
     for s in range(n):
         assert np.allclose(d_looped[s], tl[s].grad.numpy(), rtol=1e-12, atol=1e-12)
         assert np.allclose(d_local[s], tc[s].grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Case 3 ([OV] 5.1): the looped LHS split on the batch dim
+# ---------------------------------------------------------------------------
+def _batch_shards(n, rng, bs=2, m=2, k=3, c=4, integer=False):
+    draw = (lambda shape: rng.integers(-4, 5, size=shape).astype(np.float64)) if integer \
+        else rng.standard_normal
+    looped = [draw((bs, m, k)) for _ in range(n)]          # A_s [b_s, m, k]
+    local = [draw((n * bs, k, c)) for _ in range(n)]       # B_r [N b_s, k, n]
+    return looped, local
+
+
+def test_allgather_batch_vs_triple_loop():
+    rng = np.random.default_rng(21)
+    n, bs = 3, 2
+    looped, local = _batch_shards(n, rng, bs)
+    got = einsum.allgather_einsum("lhs_batch", looped, local)
+    for r in range(n):
+        assert got[r].shape == (n * bs, 2, 4)
+        for s in range(n):
+            for e in range(bs):
+                ref = _loop_matmul(looped[s][e], local[r][s * bs + e])
+                np.testing.assert_allclose(got[r][s * bs + e], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_n1_allgather_batch_is_batched_matmul():
+    rng = np.random.default_rng(22)
+    looped, local = _batch_shards(1, rng, bs=3)
+    got = einsum.allgather_einsum("lhs_batch", looped, local)[0]
+    for e in range(3):
+        np.testing.assert_allclose(got[e], _loop_matmul(looped[0][e], local[0][e]),
+                                   rtol=1e-13, atol=1e-13)
+
+
+def test_allgather_batch_reduces_to_case1_with_one_rhs():
+    """When every batch slice of B_r is the same matrix, case 3 is case 1
+    (looped LHS split on rows) applied to the shards' stacked rows."""
+    rng = np.random.default_rng(23)
+    n, bs, m, k, c = 4, 2, 3, 5, 6
+    looped = [rng.standard_normal((bs, m, k)) for _ in range(n)]
+    b0 = [rng.standard_normal((k, c)) for _ in range(n)]
+    local = [np.broadcast_to(b, (n * bs, k, c)).copy() for b in b0]
+    got = einsum.allgather_einsum("lhs_batch", looped, local)
+    want = einsum.allgather_einsum("lhs_rows", [x.reshape(bs * m, k) for x in looped], b0)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g.reshape(n * bs * m, c), w, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_batch_loop_agrees_with_definition(n):
+    rng = np.random.default_rng(200 + n)
+    looped, local = _batch_shards(n, rng)
+    ref = einsum.allgather_einsum("lhs_batch", looped, local)
+    outs, sched, _ = ring.simulate_allgather_einsum("lhs_batch", looped, local)
+    for o, r in zip(outs, ref):
+        np.testing.assert_allclose(o, r, rtol=1e-12, atol=1e-12)
+    assert sched == [[(r + i) % n for r in range(n)] for i in range(n)]   # case 1's schedule
+    outs2, _, _ = ring.simulate_allgather_einsum_bidir("lhs_batch", looped, local)
+    for o, r in zip(outs2, ref):
+        np.testing.assert_allclose(o, r, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 5])
+def test_batch_loop_bit_equal_on_integer_probes(n):
+    rng = np.random.default_rng(300 + n)
+    looped, local = _batch_shards(n, rng, integer=True)
+    ref = einsum.allgather_einsum("lhs_batch", looped, local)
+    for sim in (ring.simulate_allgather_einsum, ring.simulate_allgather_einsum_bidir):
+        outs = sim("lhs_batch", looped, local)[0]
+        for o, r in zip(outs, ref):
+            assert np.array_equal(o, r)
