@@ -21,7 +21,7 @@ CCE_FLAG_COPY_DMA = 0x4
 CCE_FLAG_FUSED_PERMUTE = 0x8
 CCE_FLAG_BIDIRECTIONAL = 0x10
 
-AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3}
+AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3, "lhs_batch": 4}
 RS_MODES = {"slice_lhs_rows": 0, "slice_rhs_cols": 1}
 
 

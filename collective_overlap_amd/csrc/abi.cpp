@@ -183,8 +183,9 @@ struct AgGeom {
   int mode = 0;
   bool case2 = false;
   bool case2_ws = false;
-  int64_t M = 0, N = 0, K = 0;          // per-iteration GEMM
-  int64_t recv_bytes = 0;               // one receive buffer (packed)
+  int64_t M = 0, N = 0, K = 0;          // per-iteration GEMM (one batch element for case 3)
+  int64_t bs = 1;                       // case 3: batch elements per shard
+  int64_t recv_bytes = 0;               // one receive buffer (the looped shard, its ld included)
   int64_t acc_ld = 0, acc_bytes = 0;    // case-2 fp32 accumulator
   int64_t ccw_off = 0;                  // counter-clockwise receive buffers (bidirectional)
   int64_t total = 0;                    // enough for every flag combination
@@ -194,7 +195,7 @@ cce_status ag_geometry(int n, int mode, cce_dtype in_t, cce_dtype out_t, const c
                        const cce_mat* local, const cce_mat& out, AgGeom& g) {
   if (n < 1 || n > CCE_MAX_RANKS)
     return fail(n < 1 ? CCE_EINVAL : CCE_EUNSUPPORTED, "n_ranks out of range: " + std::to_string(n));
-  if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
+  if (mode < 0 || mode > 4) return fail(CCE_EINVAL, "bad AllGather mode");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   CCE_TRY(check_mat("looped_shard", looped));
   CCE_TRY(check_mat("out_shape", out));
@@ -229,9 +230,29 @@ cce_status ag_geometry(int n, int mode, cce_dtype in_t, cce_dtype out_t, const c
       if (local && (local->rows != out.rows || local->cols != nn * looped.cols))
         return fail(CCE_EINVAL, "local must be [out rows, n * looped cols] " + mat_str(*local));
       break;
+    case CCE_AG_LHS_BATCH:
+      // b_s batch elements per shard, stacked row-wise; b_s comes from the
+      // local operand (n * b_s stacked [N, K] factors), so the workspace
+      // query, which has no local shape, sizes the receive buffers only.
+      g.K = looped.cols; g.N = out.cols; g.M = looped.rows;
+      if (out.rows != nn * looped.rows) return fail(CCE_EINVAL, "out rows must be n * looped rows");
+      if (local) {
+        if (local->cols != looped.cols)
+          return fail(CCE_EINVAL, "local must have the looped shard's K " + mat_str(*local));
+        if (out.cols == 0 || local->rows == 0 || local->rows % (nn * out.cols) != 0)
+          return fail(CCE_EINVAL, "local rows must be n * b_s * out cols " + mat_str(*local));
+        g.bs = local->rows / (nn * out.cols);
+        if (looped.rows % g.bs != 0)
+          return fail(CCE_EINVAL, "looped rows must be b_s * m (b_s = " + std::to_string(g.bs) + ")");
+        g.M = looped.rows / g.bs;
+      }
+      break;
   }
   if (g.K % 8 != 0) return fail(CCE_EUNSUPPORTED, "contraction length must be a multiple of 8");
-  g.recv_bytes = (n > 1) ? align256(looped.rows * looped.cols * static_cast<int64_t>(esize(in_t))) : 0;
+  // Receive buffers keep the caller's ld: one launch can hold a caller's
+  // shard and a received one (iteration 0 of the two-way form), and a launch
+  // has a single ld per operand.
+  g.recv_bytes = (n > 1) ? align256(looped.rows * looped.ld * static_cast<int64_t>(esize(in_t))) : 0;
   if (g.case2_ws) {
     g.acc_ld = round8(out.cols);
     g.acc_bytes = align256(out.rows * g.acc_ld * 4);
@@ -369,12 +390,12 @@ PtrLd ag_resolve(const AgCall& c, const BufRef& b) {
     case B_LOCAL: return {const_cast<char*>(static_cast<const char*>(c.local[r])), c.local_shape.ld};
     case B_OUT: return {static_cast<char*>(c.out[r]), c.oshape.ld};
     case B_RECV:
-      return {c.ws + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes, c.lshape.cols};
+      return {c.ws + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes, c.lshape.ld};
     case B_CASE2:
       return {c.ws + 2LL * c.g.n * c.g.recv_bytes + r * c.g.acc_bytes, c.g.acc_ld};
     case B_RECV_CCW:
       return {c.ws + c.g.ccw_off + (static_cast<int64_t>(b.parity) * c.g.n + r) * c.g.recv_bytes,
-              c.lshape.cols};
+              c.lshape.ld};
   }
   return {nullptr, 0};
 }
@@ -396,7 +417,10 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
         const PtrLd src = ag_resolve(c, it.a), dst = ag_resolve(c, it.c);
         if (c.lshape.rows == 0 || w == 0) continue;
         if (src.ld == dst.ld) {
-          HIP_TRY(hipMemcpyAsync(dst.p, src.p, c.lshape.rows * src.ld * ein, c.copy_kind, s));
+          // the shard's exact span: no read of the caller's memory past its
+          // last row
+          const int64_t span = ((c.lshape.rows - 1) * src.ld + c.lshape.cols) * ein;
+          HIP_TRY(hipMemcpyAsync(dst.p, src.p, span, c.copy_kind, s));
         } else {
           HIP_TRY(hipMemcpy2DAsync(dst.p, dst.ld * ein, src.p, src.ld * ein, w, c.lshape.rows,
                                    c.copy_kind, s));
@@ -407,7 +431,9 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
     }
     // GEMM
     GemmLaunch L;
-    L.groups = static_cast<int>(o.items.size());   // one group per item (rank, direction)
+    // one group per item (rank, direction); case 3: one per batch element
+    const int per = (c.g.mode == CCE_AG_LHS_BATCH) ? static_cast<int>(c.g.bs) : 1;
+    L.groups = static_cast<int>(o.items.size()) * per;
     L.M = c.g.M;
     L.N = c.g.N;
     L.K = c.g.K;
@@ -417,50 +443,65 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
     L.gelu = c.gelu && (!c.g.case2 || last);
     int gi = 0;
     for (const Item& it : o.items) {
-      const int r = gi++;
       const int64_t s_id = it.shard;
       const PtrLd held = ag_resolve(c, it.a);
       const PtrLd loc = ag_resolve(c, it.b);
       const PtrLd dst = ag_resolve(c, it.c);
       L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
       L.ldc = dst.ld;
-      char* cptr = dst.p;
       const int64_t eo = esize(L.out_t);
-      switch (c.g.mode) {
-        case CCE_AG_LHS_ROWS:
-          L.p.a[r] = held.p; L.lda = held.ld;
-          L.p.b[r] = loc.p; L.ldb = loc.ld;
-          cptr += s_id * c.g.M * dst.ld * eo;
-          break;
-        case CCE_AG_RHS_COLS:
-          L.p.a[r] = loc.p; L.lda = loc.ld;
-          L.p.b[r] = held.p; L.ldb = held.ld;
-          cptr += s_id * c.g.N * eo;
-          break;
-        case CCE_AG_LHS_COLS:
-          L.p.a[r] = held.p; L.lda = held.ld;
-          L.p.b[r] = loc.p + s_id * c.g.K * ein; L.ldb = loc.ld;
-          break;
-        case CCE_AG_RHS_ROWS:
-          L.p.a[r] = loc.p + s_id * c.g.K * ein; L.lda = loc.ld;
-          L.p.b[r] = held.p; L.ldb = held.ld;
-          break;
-      }
-      L.p.c[r] = cptr;
-      if (it.has_fwd) {
-        const PtrLd f = ag_resolve(c, it.fwd);
-        L.fwd = (c.g.mode == CCE_AG_LHS_ROWS || c.g.mode == CCE_AG_LHS_COLS) ? FWD_A : FWD_B;
-        L.p.fwd[r] = f.p;
-        L.ldfwd = f.ld;
-      } else {
-        L.p.fwd[r] = nullptr;
-      }
-      if (it.has_cin) {
-        const PtrLd cin = ag_resolve(c, it.cin);
-        L.p.cin[r] = reinterpret_cast<const float*>(cin.p);
-        L.ldcin = cin.ld;
-      } else {
-        L.p.cin[r] = nullptr;
+      const PtrLd f = it.has_fwd ? ag_resolve(c, it.fwd) : PtrLd{nullptr, 0};
+      for (int e = 0; e < per; ++e) {
+        const int r = gi++;
+        char* cptr = dst.p;
+        switch (c.g.mode) {
+          case CCE_AG_LHS_ROWS:
+            L.p.a[r] = held.p; L.lda = held.ld;
+            L.p.b[r] = loc.p; L.ldb = loc.ld;
+            cptr += s_id * c.g.M * dst.ld * eo;
+            break;
+          case CCE_AG_RHS_COLS:
+            L.p.a[r] = loc.p; L.lda = loc.ld;
+            L.p.b[r] = held.p; L.ldb = held.ld;
+            cptr += s_id * c.g.N * eo;
+            break;
+          case CCE_AG_LHS_COLS:
+            L.p.a[r] = held.p; L.lda = held.ld;
+            L.p.b[r] = loc.p + s_id * c.g.K * ein; L.ldb = loc.ld;
+            break;
+          case CCE_AG_RHS_ROWS:
+            L.p.a[r] = loc.p + s_id * c.g.K * ein; L.lda = loc.ld;
+            L.p.b[r] = held.p; L.ldb = held.ld;
+            break;
+          case CCE_AG_LHS_BATCH: {
+            // element e of shard s: its rows of the held shard, the local
+            // operand's element s*b_s + e, the output's element s*b_s + e
+            const int64_t j = s_id * per + e;
+            L.p.a[r] = held.p + e * c.g.M * held.ld * ein; L.lda = held.ld;
+            L.p.b[r] = loc.p + j * c.g.N * loc.ld * ein; L.ldb = loc.ld;
+            cptr += j * c.g.M * dst.ld * eo;
+            break;
+          }
+        }
+        L.p.c[r] = cptr;
+        if (it.has_fwd) {
+          L.fwd = (c.g.mode == CCE_AG_LHS_ROWS || c.g.mode == CCE_AG_LHS_COLS ||
+                   c.g.mode == CCE_AG_LHS_BATCH)
+                      ? FWD_A
+                      : FWD_B;
+          // case 3: element e of the shard lands at its rows of the next buffer
+          L.p.fwd[r] = f.p + (c.g.mode == CCE_AG_LHS_BATCH ? e * c.g.M * f.ld * ein : 0);
+          L.ldfwd = f.ld;
+        } else {
+          L.p.fwd[r] = nullptr;
+        }
+        if (it.has_cin) {
+          const PtrLd cin = ag_resolve(c, it.cin);
+          L.p.cin[r] = reinterpret_cast<const float*>(cin.p);
+          L.ldcin = cin.ld;
+        } else {
+          L.p.cin[r] = nullptr;
+        }
       }
     }
     int slot;
@@ -853,6 +894,8 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
     return fail(CCE_EUNSUPPORTED, "the bidirectional form takes the case-1 modes only");
   if (bidir && 2 * n_ranks > CCE_MAX_RANKS)
     return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
+  if (static_cast<int64_t>(bidir ? 2 : 1) * n_ranks * g.bs > CCE_MAX_RANKS)
+    return fail(CCE_EUNSUPPORTED, "case 3: n * b_s GEMM groups (2 * n * b_s two-way) exceed CCE_MAX_RANKS");
   const size_t ein = esize(in_t), eout = esize(out_t);
   const int64_t ls = span_bytes(looped_shard, ein), cs = span_bytes(local_shape, ein),
                 os = span_bytes(out_shape, eout);
@@ -1301,7 +1344,7 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
     return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   Plan p;
   if (kind == 0) {
-    if (mode < 0 || mode > 3) return fail(CCE_EINVAL, "bad AllGather mode");
+    if (mode < 0 || mode > 4) return fail(CCE_EINVAL, "bad AllGather mode");
     const bool case2 = (mode == CCE_AG_LHS_COLS || mode == CCE_AG_RHS_ROWS);
     if (bidir && case2)
       return fail(CCE_EUNSUPPORTED, "the bidirectional form takes the case-1 modes only");

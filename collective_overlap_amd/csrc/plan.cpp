@@ -560,10 +560,11 @@ std::string describe_plan(const Plan& p) {
         std::snprintf(line, sizeof line, "%s it=%d h=%d epi=%d final=%d", kname, o.iter, o.half,
                       o.epi, o.final_store ? 1 : 0);
         out += line;
-        // AllGather case 1 writes the slice of its shard: name it, so that
+        // AllGather cases 1 and 3 write the slice of their shard: name it, so that
         // two items writing different slices of one output do not collide.
         const bool slice_out = p.kind == 0 && o.kind == OP_GEMM &&
-                               (p.mode == CCE_AG_LHS_ROWS || p.mode == CCE_AG_RHS_COLS);
+                               (p.mode == CCE_AG_LHS_ROWS || p.mode == CCE_AG_RHS_COLS ||
+                                p.mode == CCE_AG_LHS_BATCH);
         std::string rd, wr, sh, xs;
         for (const Item& it : o.items) {
           std::string ir = bufname(it.a), iw = bufname(it.c);

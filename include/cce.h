@@ -100,8 +100,8 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
                                   second buffer with a prologue transfer; the
                                   ReduceScatter ends with an epilogue transfer
                                   and an align-and-sum of the two
-                                  accumulators.  AllGather case 1 modes and
-                                  both ReduceScatter modes; n_ranks <= 32.
+                                  accumulators.  AllGather case 1 and 3 modes
+                                  and both ReduceScatter modes; n_ranks <= 32.
                                   Combines with SERIAL, GELU, COPY_DMA and
                                   FUSED_PERMUTE. */
 
@@ -162,15 +162,15 @@ cce_status cce_ctx_read_profile(cce_ctx* ctx, int max_records, cce_prof_record* 
 cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
 
 /* ------------------------------------------------------------------------
- * Looped AllGather-Einsum ([OV] Sections 4 and 5.1, cases 1 and 2).
+ * Looped AllGather-Einsum ([OV] Sections 4 and 5.1, cases 1, 2 and 3).
  *
  * looped[r] is rank r's own shard (shard ID r) of the operand the AllGather
  * would rebuild; local[r] is rank r's operand that never moves; out[r]
  * receives rank r's full result.  In iteration i rank r computes the partial
  * einsum on shard s = (r + i) mod n while that shard travels on to rank
- * r - 1; the update is a store into the result slice of shard s (case 1,
- * DynamicUpdateSlice) or an addition (case 2).  Shapes (storage orientation,
- * see the header comment):
+ * r - 1; the update is a store into the result slice of shard s (cases 1
+ * and 3, DynamicUpdateSlice) or an addition (case 2).  Shapes (storage
+ * orientation, see the header comment):
  *
  *   CCE_AG_LHS_ROWS  case 1, looped left factor split on rows M:
  *                    looped [m_s, K], local B^T [N, K], out [n*m_s, N];
@@ -184,12 +184,25 @@ cce_status cce_shard_schedule(int n_ranks, int kind, int32_t* table);
  *   CCE_AG_RHS_ROWS  case 2, looped right factor split on K:
  *                    looped B^T [N, k_s], local A [M, n*k_s], out [M, N];
  *                    out += (A columns [s*k_s, (s+1)*k_s)) * shard^T.
+ *   CCE_AG_LHS_BATCH case 3, looped left factor split on a batch dim: b_s
+ *                    batch elements per shard, each stacked row-wise:
+ *                    looped [b_s*m, K] (element e = rows [e*m, (e+1)*m)),
+ *                    local B^T [n*b_s*N, K] (element j's B^T = rows
+ *                    [j*N, (j+1)*N)), out [n*b_s*m, N] (element j = rows
+ *                    [j*m, (j+1)*m)); b_s = local rows / (n * out cols).
+ *                    Element e of shard s multiplies the local operand's
+ *                    element s*b_s + e (a DynamicSlice along its batch dim,
+ *                    of the shard's batch extent) and fills out element
+ *                    s*b_s + e.  One GEMM group per batch element: n*b_s
+ *                    (2*n*b_s with CCE_FLAG_BIDIRECTIONAL) must not exceed
+ *                    CCE_MAX_RANKS.
  *
  * in_t: CCE_BF16 (fp32 accumulation) or CCE_F32 (both inputs the same type).
  * out_t: CCE_BF16 or CCE_F32 (round to nearest even on the final store).
  * Case 2 accumulates across iterations in fp32 (in `out` itself when out_t is
  * CCE_F32, else in the workspace).  flags: CCE_FLAG_SERIAL, CCE_FLAG_GELU,
- * CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_BIDIRECTIONAL (case 1).
+ * CCE_FLAG_COPY_DMA, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_BIDIRECTIONAL (cases 1
+ * and 3).
  * workspace: device memory of at least the size the query returns (two
  * receive buffers per rank and direction, plus the fp32 accumulators of
  * case 2 with a bf16 output; the size covers every flag combination); its
@@ -199,7 +212,8 @@ typedef enum cce_ag_mode {
   CCE_AG_LHS_ROWS = 0,
   CCE_AG_RHS_COLS = 1,
   CCE_AG_LHS_COLS = 2,
-  CCE_AG_RHS_ROWS = 3
+  CCE_AG_RHS_ROWS = 3,
+  CCE_AG_LHS_BATCH = 4
 } cce_ag_mode;
 
 cce_status cce_looped_allgather_einsum_workspace(int n_ranks, cce_ag_mode mode, cce_dtype in_t,

@@ -67,7 +67,7 @@ def _shards(op):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("out_t", [0, 1])
 @pytest.mark.parametrize("flags", [0, 1])
 def test_allgather_plan_race_free(n, mode, out_t, flags):
@@ -247,7 +247,7 @@ FUSED = 0x8
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0), (1, 1)])
+@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (0, 2), (0, 3), (0, 4), (1, 0), (1, 1)])
 def test_fused_plans_race_free_and_copy_free(n, kind, mode):
     text = _plan(kind, n, mode, 1, FUSED)
     assert plan_check.check(text) == []
@@ -316,7 +316,7 @@ def test_bidir_shard_schedule_is_the_oracles(n):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 16, 32])
-@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("kind,mode", [(0, 0), (0, 1), (0, 4), (1, 0), (1, 1)])
 @pytest.mark.parametrize("extra", [0, 1, 8])
 def test_bidir_plans_race_free(n, kind, mode, extra):
     text = _plan(kind, n, mode, 1, BIDIR | extra)
