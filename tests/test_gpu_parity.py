@@ -317,6 +317,57 @@ def test_reducescatter_fused_permute_matches(ctx, mode, dims, n):
 
 
 # ---------------------------------------------------------------------------
+# Accumulate launches at the large tile shapes: whole tiles with more k tiles
+# than accumulator blocks take the accumulator input during the last k tiles,
+# edge tiles in the epilogue.  Integer probes make every order exact.
+# ---------------------------------------------------------------------------
+FOLD_CASES = [
+    # mode, n, shard extent s, other extent c, K, flags.
+    # copy stream: half-shard launches of 500 rows, 256x128 tiles, ragged
+    # rows, a K tail (18 k tiles)
+    ("slice_lhs_rows", 4, 1000, 4096, 1100, 0),
+    # fused permute: 256x256 tiles, exactly one more k tile than blocks (17)
+    ("slice_lhs_rows", 4, 1024, 4096, 1088, 0x8),
+    # two-way ring, fused permute: 256x256 tiles, ragged rows
+    ("slice_lhs_rows", 2, 1000, 4096, 1280, 0x18),
+    # fused permute, one way: 256x128 tiles, ragged rows
+    ("slice_lhs_rows", 2, 1000, 4096, 1280, 0x8),
+    # column shards: 256x256 tiles, ragged rows, a K tail
+    ("slice_rhs_cols", 4, 4096, 1000, 1100, 0x8),
+]
+
+
+@pytest.mark.parametrize("mode,n,s,c,K,flags", FOLD_CASES)
+def test_reducescatter_large_tiles_integer_probe(ctx, mode, n, s, c, K, flags):
+    import collective_overlap_amd as cce
+    print(f"[gpu] reducescatter large tiles {mode} n={n} s={s} c={c} K={K} flags={flags:#x}",
+          flush=True)
+    a, b, oshape, _, _ = _rs_inputs(mode, n, (s, K, c), torch.bfloat16, True, seed=11)
+    out = [torch.full(oshape, float("nan"), device=DEV) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out, flags=flags)
+    sync()
+    # sampled rows, tile edges and the ragged last tile included
+    m_ext = s if mode == "slice_lhs_rows" else c
+    rows = np.unique(np.concatenate([_rows_sample(24, m_ext, 3),
+                                     [0, 255, 256, 767, 768, m_ext - 1]]))
+    rows = rows[rows < m_ext]
+    if mode == "slice_lhs_rows":
+        oa = [np.concatenate([np64(x[t * s + rows]) for t in range(n)]) for x in a]
+        ob = [np64(y).T for y in b]
+    else:
+        oa = [np64(x[rows]) for x in a]
+        ob = [np64(y).T for y in b]
+    ref = oe.einsum_reducescatter(mode, oa, ob)
+    for r in range(n):
+        assert np.array_equal(np64(out[r][rows]), ref[r]), f"rank {r}"
+
+
+def _rows_sample(k, total, seed):
+    g = np.random.default_rng(seed)
+    return np.sort(g.choice(total, size=min(k, total), replace=False))
+
+
+# ---------------------------------------------------------------------------
 # Largest rank counts and empty extents
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("flags", [0, 0x1, 0x8])
