@@ -325,7 +325,7 @@ FOLD_CASES = [
     # mode, n, shard extent s, other extent c, K, flags.
     # copy stream: half-shard launches of 500 rows, 256x128 tiles, ragged
     # rows, a K tail (18 k tiles)
-    ("slice_lhs_rows", 4, 1000, 4096, 1100, 0),
+    ("slice_lhs_rows", 4, 1000, 4096, 1096, 0),
     # fused permute: 256x256 tiles, exactly one more k tile than blocks (17)
     ("slice_lhs_rows", 4, 1024, 4096, 1088, 0x8),
     # two-way ring, fused permute: 256x256 tiles, ragged rows
@@ -333,7 +333,7 @@ FOLD_CASES = [
     # fused permute, one way: 256x128 tiles, ragged rows
     ("slice_lhs_rows", 2, 1000, 4096, 1280, 0x8),
     # column shards: 256x256 tiles, ragged rows, a K tail
-    ("slice_rhs_cols", 4, 4096, 1000, 1100, 0x8),
+    ("slice_rhs_cols", 4, 4096, 1000, 1096, 0x8),
 ]
 
 
