@@ -77,6 +77,41 @@ def test_grouped_gemm_integer_probe_bit_exact(ctx, dt):
         assert np.array_equal(np64(c[g]), ref)
 
 
+# bf16 results of launches with more tiles than CUs: each workgroup walks
+# several tiles and stores part of a tile's results while it computes the
+# next.  Ragged rows (edge tiles store at once), k-tile counts below and
+# above the spread of those stores, and a padded output row stride.
+PERSISTENT_CASES = [
+    # G, M, N, K, output ld (None: N)
+    (2, 4000, 4096, 200, None),       # 512 tiles of 256x256, ragged rows, 4 k tiles
+    (1, 8192, 8192, 64, None),        # 1024 tiles, one k tile
+    (3, 1024, 4096, 1000, 4104),      # 192 tiles of 256x256 -> 256x128 tiles, padded ld
+    (4, 2048, 2048, 1032, None),      # 256 tiles: one per workgroup, 17 k tiles
+]
+
+
+@pytest.mark.parametrize("G,M,N,K,ld", PERSISTENT_CASES)
+def test_grouped_gemm_many_tiles_bf16_integer_probe(ctx, G, M, N, K, ld):
+    import collective_overlap_amd as cce
+    print(f"[gpu] grouped_gemm many tiles G={G} M={M} N={N} K={K} ld={ld}", flush=True)
+    a = [_t((M, K), 60 + g, torch.bfloat16, True) for g in range(G)]
+    b = [_t((N, K), 70 + g, torch.bfloat16, True) for g in range(G)]
+    if ld is None:
+        bigs = [torch.full((M, N), float("nan"), device=DEV, dtype=torch.bfloat16) for _ in range(G)]
+        c = bigs
+    else:
+        bigs = [torch.zeros((M, ld), device=DEV, dtype=torch.bfloat16) for _ in range(G)]
+        c = [x[:, :N] for x in bigs]
+    cce.cce_grouped_gemm(ctx, a, b, c)
+    sync()
+    for g in range(G):
+        # exact integers in fp32, rounded once to bf16
+        ref = numerics.bf16_round(np64(a[g]) @ np64(b[g]).T)
+        assert np.array_equal(np64(c[g]), ref), f"group {g}"
+        if ld is not None:
+            assert torch.count_nonzero(bigs[g][:, N:]) == 0     # padding untouched
+
+
 def test_grouped_gemm_gelu_and_strided(ctx):
     import collective_overlap_amd as cce
     M, N, K = 384, 261, 200
