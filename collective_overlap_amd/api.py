@@ -162,11 +162,27 @@ def cce_looped_allgather_einsum_workspace(n_ranks, mode, in_dtype, out_dtype, lo
     return nb.value
 
 
-def _workspace(nbytes, device, workspace):
+def _torch_stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _workspace(nbytes, device, workspace, stream=None):
+    """The caller's workspace, or a temporary one.  A temporary one is freed
+    when the call returns, while the work that uses it may still be queued on
+    `stream` (the copy stream joins back into it).  When that is not the
+    current stream, the caching allocator is told, so that it does not hand
+    the memory out again before `stream` has finished with it."""
     if nbytes == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        s = _torch_stream(stream, device)
+        if s != torch.cuda.current_stream(device):
+            workspace.record_stream(s)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -180,7 +196,7 @@ def cce_looped_allgather_einsum(ctx: Context, mode, looped, local, out, workspac
     need = cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t,
                                                  (lm.rows, lm.cols, lm.ld),
                                                  (om.rows, om.cols, om.ld))
-    ws, wsb = _workspace(need, out[0].device, workspace)
+    ws, wsb = _workspace(need, out[0].device, workspace, stream)
     check(lib().cce_looped_allgather_einsum(
         ctx.handle, n, mode, in_t, out_t,
         ptr_array([t.data_ptr() for t in looped]), lm,
@@ -209,7 +225,7 @@ def cce_looped_einsum_reducescatter(ctx: Context, mode, a, b, out, workspace=Non
     am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
     in_t, out_t = _dtype(a[0].dtype), _dtype(out[0].dtype)
     need = cce_looped_einsum_reducescatter_workspace(n, mode, (om.rows, om.cols, om.ld))
-    ws, wsb = _workspace(need, out[0].device, workspace)
+    ws, wsb = _workspace(need, out[0].device, workspace, stream)
     check(lib().cce_looped_einsum_reducescatter(
         ctx.handle, n, mode, in_t, CCE_F32, out_t,
         ptr_array([t.data_ptr() for t in a]), am,
@@ -237,7 +253,7 @@ def cce_looped_einsum_reducescatter_epilogue(ctx: Context, mode, a, b, bias, res
         mask_ld = mask_col0 + om.cols
     rows0 = list(mask_row0) if mask_row0 is not None else [0] * n
     need = cce_looped_einsum_reducescatter_workspace(n, mode, (om.rows, om.cols, om.ld))
-    ws, wsb = _workspace(need, out[0].device, workspace)
+    ws, wsb = _workspace(need, out[0].device, workspace, stream)
     check(lib().cce_looped_einsum_reducescatter_epilogue(
         ctx.handle, n, mode, _dtype(a[0].dtype), _dtype(out[0].dtype),
         ptr_array([t.data_ptr() for t in a]), am,
