@@ -85,6 +85,7 @@ PROTOTYPES = {
     "cce_overlap_beneficial": (_I, [ctypes.c_double] * 4),
     "cce_overlap_choose": (_I, [ctypes.c_double] * 5),
     "cce_describe_plan": (_I, [_I, _I, _I, _I, _U32, ctypes.c_char_p, _SZ, ctypes.POINTER(_SZ)]),
+    "cce_debug_fail_op": (_I, [_I]),
 }
 
 

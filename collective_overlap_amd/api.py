@@ -28,7 +28,7 @@ __all__ = [
     "cce_looped_einsum_reducescatter_workspace", "cce_looped_einsum_reducescatter_epilogue",
     "cce_grouped_gemm",
     "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched",
-    "cce_fused_allreduce_epilogue", "cce_describe_plan",
+    "cce_fused_allreduce_epilogue", "cce_describe_plan", "cce_debug_fail_op",
     "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
     "CCE_FLAG_BIDIRECTIONAL",
@@ -146,6 +146,12 @@ def cce_describe_plan(kind: int, n_ranks: int, mode: int, out_dtype=CCE_BF16, fl
     check(lib().cce_describe_plan(kind, n_ranks, mode, _dtype(out_dtype), flags, buf, need.value,
                                   ctypes.byref(need)), "cce_describe_plan")
     return buf.value.decode()
+
+
+def cce_debug_fail_op(index: int) -> None:
+    """Error-path test hook: plan operation `index` (1-based) of the next
+    looped call on this thread fails as a HIP error would; 0 disarms."""
+    check(lib().cce_debug_fail_op(int(index)), "cce_debug_fail_op")
 
 
 def cce_looped_allgather_einsum_workspace(n_ranks, mode, in_dtype, out_dtype, looped_shape,

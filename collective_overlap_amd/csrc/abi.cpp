@@ -43,6 +43,18 @@ namespace cce {
 namespace {
 thread_local std::string g_err;
 
+// Error-path test hook (cce_debug_fail_op): plan operation g_fail_at of a
+// looped call on this thread fails as a HIP error would.  Fires once.
+thread_local int g_fail_at = 0;
+thread_local int g_ops_seen = 0;
+
+bool fail_due() {
+  if (g_fail_at <= 0) return false;
+  if (++g_ops_seen != g_fail_at) return false;
+  g_fail_at = 0;
+  return true;
+}
+
 // GEMM operands are addressed through 32-bit buffer offsets (see gemm.hip).
 constexpr int64_t kMaxOperandBytes = (int64_t{1} << 30) - 256;
 
@@ -400,9 +412,24 @@ PtrLd ag_resolve(const AgCall& c, const BufRef& b) {
   return {nullptr, 0};
 }
 
+// A plan that fails part-way may leave work on the copy stream that the
+// caller's stream would no longer wait for.  Join the copy stream back
+// (best effort: the first error is the one reported), so that the caller's
+// later work, freeing the workspace included, stays ordered after it.
+cce_status joined(cce_ctx* ctx, hipStream_t compute, cce_status st) {
+  if (st == CCE_OK || ctx->events.empty()) return st;
+  const std::string err = g_err;
+  if (hipEventRecord(ctx->events[0], ctx->copy) == hipSuccess)
+    (void)hipStreamWaitEvent(compute, ctx->events[0], 0);
+  g_err = err;
+  return st;
+}
+
 cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream_t compute) {
   const size_t ein = esize(c.in_t);
+  g_ops_seen = 0;
   for (const Op& o : plan.ops) {
+    if (fail_due()) return fail(CCE_EHIP, "injected failure at plan op " + std::to_string(g_ops_seen));
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
     if (o.kind == OP_RECORD || o.kind == OP_WAIT) {
       CCE_TRY(run_events(ctx, o, s));
@@ -620,7 +647,9 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
   std::vector<std::array<PtrLd, 2>> final_acc[2] = {std::vector<std::array<PtrLd, 2>>(c.g.n),
                                                     std::vector<std::array<PtrLd, 2>>(c.g.n)};
   bool has_final[2] = {false, false};
+  g_ops_seen = 0;
   for (const Op& o : plan.ops) {
+    if (fail_due()) return fail(CCE_EHIP, "injected failure at plan op " + std::to_string(g_ops_seen));
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
     if (o.kind == OP_RECORD || o.kind == OP_WAIT) {
       CCE_TRY(run_events(ctx, o, s));
@@ -762,6 +791,13 @@ const char* cce_status_string(cce_status s) {
 const char* cce_last_error(void) { return g_err.c_str(); }
 
 const char* cce_version(void) { return "0.1.0"; }
+
+cce_status cce_debug_fail_op(int index) {
+  if (index < 0) return fail(CCE_EINVAL, "cce_debug_fail_op: index must be >= 0");
+  g_fail_at = index;
+  g_ops_seen = 0;
+  return CCE_OK;
+}
 
 cce_status cce_ctx_create(int device, cce_ctx** out) {
   clear_error();
@@ -925,10 +961,10 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
   const Plan plan = bidir ? build_allgather_plan_bidir(n_ranks, mode, serial, fused)
                           : build_allgather_plan(n_ranks, mode, g.case2_ws, serial, fused);
-  CCE_TRY(ensure_events(ctx, plan.n_events));
+  CCE_TRY(ensure_events(ctx, std::max(plan.n_events, 1)));
   AgCall c{g, in_t, out_t, looped, looped_shard, local, local_shape, out, out_shape,
            static_cast<char*>(workspace), (flags & CCE_FLAG_GELU) != 0, copy_kind(flags)};
-  return ag_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
+  return joined(ctx, static_cast<hipStream_t>(stream), ag_execute(ctx, c, plan, static_cast<hipStream_t>(stream)));
 }
 
 cce_status cce_looped_einsum_reducescatter_workspace(int n_ranks, cce_rs_mode mode, cce_dtype acc_t,
@@ -1050,11 +1086,11 @@ static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
   const Plan plan = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, g.h1 > 0, serial, fused)
                           : build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
-  CCE_TRY(ensure_events(ctx, plan.n_events));
+  CCE_TRY(ensure_events(ctx, std::max(plan.n_events, 1)));
   RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
            copy_kind(flags)};
   c.epi = ea ? &epi : nullptr;
-  return rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream));
+  return joined(ctx, static_cast<hipStream_t>(stream), rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream)));
 }
 
 cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,

@@ -436,6 +436,20 @@ int cce_overlap_choose(double comp, double comm0, double shard_bytes0, double co
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t,
                              uint32_t flags, char* buf, size_t buf_len, size_t* needed);
 
+/* ------------------------------------------------------------------------
+ * Error-path test hook.  Arms a failure: plan operation `index` (1-based, in
+ * the order cce_describe_plan lists them: a GEMM or epilogue launch, a copy,
+ * an event record or wait) of the next looped call on this thread is not
+ * enqueued; the call returns CCE_EHIP as if that HIP call had failed, with
+ * cce_last_error naming the operation.  The operations before it stay
+ * enqueued, and the call joins the copy stream back into `stream` before it
+ * returns, so the caller's later work stays ordered after them.  The hook
+ * fires once; index 0 disarms it, an index past the plan's length never
+ * fires.  Returns CCE_EINVAL for a negative index.  For tests of the error
+ * path and of the state a failed call leaves behind.
+ * ---------------------------------------------------------------------- */
+cce_status cce_debug_fail_op(int index);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,18 @@ def test_status_strings(cce):
     assert cce.cce_version().decode().count(".") == 2
 
 
+def test_debug_fail_op_validates(cce):
+    """The error-path hook arms and disarms without a device; a negative
+    index is rejected."""
+    from collective_overlap_amd import cce_debug_fail_op
+    from collective_overlap_amd._lib import CceError
+    cce_debug_fail_op(3)
+    cce_debug_fail_op(0)
+    with pytest.raises(CceError) as e:
+        cce_debug_fail_op(-1)
+    assert e.value.status == 1
+
+
 @pytest.mark.parametrize("n", list(range(1, 17)) + [31, 64])
 def test_shard_schedule_is_the_oracles(n):
     from collective_overlap_amd import cce_shard_schedule

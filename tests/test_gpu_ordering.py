@@ -9,7 +9,9 @@ result.  These tests delay the caller's stream with a bounded spin kernel
 (torch.cuda._sleep) so that a missing fork would let the copies read inputs
 that are not written yet, and they poison the workspace with all-ones bytes
 (NaN in fp32 and bf16).  Inputs are integer probes, so every correct result
-is exact and equal to the oracle's."""
+is exact and equal to the oracle's.  A call made to fail part-way (the
+error-path hook) must return CCE_EHIP, leave nothing running that the
+caller's stream does not wait for, and leave the context usable."""
 
 import numpy as np
 import pytest
@@ -157,3 +159,40 @@ def test_temporary_workspace_outlives_the_call(ctx, kind, delay):
     sync()
     for r in range(n):
         assert np.array_equal(np64(out[r]), ref[r]), f"rank {r}"
+
+
+@pytest.mark.parametrize("kind", ["ag", "rs"])
+@pytest.mark.parametrize("flags", FORMS)
+def test_failed_call_joins_and_leaves_the_context_usable(ctx, kind, flags):
+    """Every plan operation in turn is made to fail.  The call reports
+    CCE_EHIP naming the operation; the caller's stream, synchronised, has
+    nothing left pending; the workspace can be released; the next call on
+    the same context gives the exact result."""
+    import collective_overlap_amd as cce
+    from collective_overlap_amd._lib import CceError
+    print(f"[gpu] error path: {kind} flags={flags:#x}", flush=True)
+    n = 3
+    x, y, out, ref = (_ag_case if kind == "ag" else _rs_case)(n)
+    failures = 0
+    try:
+        for k in range(1, 200):
+            cce.cce_debug_fail_op(k)
+            failed = False
+            try:
+                _call(cce, ctx, kind, x, y, out, flags)
+            except CceError as e:
+                assert e.status == 4, str(e)
+                assert "injected failure" in str(e)
+                failed = True
+            torch.cuda.current_stream().synchronize()
+            if not failed:
+                break
+            failures += 1
+            good = [torch.full_like(o, float("nan")) for o in out]
+            _call(cce, ctx, kind, x, y, good, flags)
+            sync()
+            for r in range(n):
+                assert np.array_equal(np64(good[r]), ref[r]), f"after failure at op {k}, rank {r}"
+    finally:
+        cce.cce_debug_fail_op(0)
+    assert failures >= 2
