@@ -77,6 +77,40 @@ def test_grouped_gemm_integer_probe_bit_exact(ctx, dt):
         assert np.array_equal(np64(c[g]), ref)
 
 
+def test_gelu_device_values_within_the_erf_bound(ctx):
+    """The store epilogue's GELU, element by element, against the exact
+    fp64 definition.  The GEMM passes every bf16 value x in [-2^4, 2^4)
+    through exactly (A[:, 0] = x, B^T[:, 0] = 1, all else 0), so the fp32
+    output is GELU evaluated at x.  The device forms erf with the rational
+    approximation of Abramowitz and Stegun 7.1.26 (|error| <= 1.5e-7) in
+    fp32; allowing 6e-7 more for the fp32 evaluation of that formula, the
+    error of 1 + erf is below 7.5e-7, hence the bound 0.5 |x| 7.5e-7 plus
+    two fp32 ulps of the result."""
+    import collective_overlap_amd as cce
+    sign = np.array([1.0, -1.0])[:, None, None]
+    exps = np.arange(-20, 4)[None, :, None].astype(np.float64)
+    mant = (1.0 + np.arange(128) / 128.0)[None, None, :]
+    x = np.concatenate([(sign * mant * 2.0 ** exps).ravel(), [0.0]])
+    M, K, N = x.size, 8, 8
+    a = torch.zeros((M, K), dtype=torch.bfloat16)
+    a[:, 0] = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(a[:, 0].double().numpy(), x)        # exact in bf16
+    b = torch.zeros((N, K), dtype=torch.bfloat16)
+    b[:, 0] = 1.0
+    c = torch.full((M, N), float("nan"), device=DEV)
+    cce.cce_grouped_gemm(ctx, [a.to(DEV)], [b.to(DEV)], [c], gelu=True)
+    sync()
+    got = np64(c)
+    ref = numerics.gelu(x)[:, None]
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    bound = 0.5 * np.abs(x)[:, None] * 7.5e-7 + 2 * ulp
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), (f"x={x[worst[0]]!r} got={got[worst]!r} ref={ref[worst[0], 0]!r} "
+                                  f"err={err[worst]:.3e} bound={bound[worst]:.3e}")
+    assert got[-1, 0] == 0.0                                   # GELU(0) = 0
+
+
 # bf16 results of launches with more tiles than CUs: each workgroup walks
 # several tiles and stores part of a tile's results while it computes the
 # next.  Ragged rows (edge tiles store at once), k-tile counts below and
