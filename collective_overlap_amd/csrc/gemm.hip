@@ -407,20 +407,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // this lane's first accumulator input: row quad_m(0), column quad_n(0, 0)
   const float* cin_w = PREF ? cin + static_cast<int64_t>(quad_m(0)) * a.ldcin + quad_n(0, 0) : cin;
 
-  // bf16 store mode: the result passes through LDS on its way out.  The
+  // Store mode: the result passes through LDS on its way out.  The
   // accumulators (block (i, j) of a wave holds C^T, the lane 4 consecutive
   // columns of one row per register quad) are written to LDS row-major and
   // read back in 16-byte chunks along the rows, so that a wave's store
   // instruction writes whole rows (1 KB of consecutive bytes) instead of 32
-  // rows x 16 bytes in 8-byte pieces, a pattern that ran at about a third of
-  // the HBM write bandwidth.  Chunk c of staged row r is kept at chunk
-  // c ^ (r & ESW) so that both the 32-row writes and the row reads spread
-  // over the banks.  A tile that does not fit the LDS goes in EP passes of
-  // EJP 32-row blocks per wave.  fp32 results store from the registers: 16
-  // bytes per lane already reach the write bandwidth, and the accumulate
-  // mode is bound by the HBM traffic of its input and output, to which a
-  // round trip through LDS only adds.
-  constexpr bool STAGED = (EPI == EPI_STORE) && sizeof(TOut) == 2 && kStagedStore;
+  // rows x 16 bytes, in 8-byte pieces for bf16, a pattern that ran at about
+  // a third of the HBM write bandwidth (for fp32 it stalls the address
+  // path, and staging was 1% faster on the ReduceScatter).  Chunk c of
+  // staged row r is kept at chunk c ^ (r & ESW) so that both the 32-row
+  // writes and the row reads spread over the banks.  A tile that does not
+  // fit the LDS (fp32) goes in EP passes of EJP 32-row blocks per wave.  The
+  // accumulate mode stores from the registers: staging it gave up the
+  // register prefetch of its input and was 15% slower on the ReduceScatter.
+  constexpr bool STAGED = (EPI == EPI_STORE) && kStagedStore;
   constexpr int ESZ = static_cast<int>(sizeof(TOut));
   constexpr int ERB = BN * ESZ;                  // staged row bytes
   constexpr int ECR = ERB / 16;                  // chunks per staged row
