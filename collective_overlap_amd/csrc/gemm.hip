@@ -396,11 +396,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   constexpr int NB = FM * FN;
   auto quad_m = [&](int b) { return m0 + wm * WTM + (b / FN) * 32 + (lane & 31); };
   auto quad_n = [&](int b, int q) { return n0 + wn * WTN + (b % FN) * 32 + 8 * q + 4 * (lane >> 5); };
-  // Accumulate mode: the accumulator input of the first NPRE blocks is loaded
-  // into registers during the last k tiles -- PER_IT blocks in each of two
-  // iterations, one load per MFMA slot of the step after the barrier -- so
-  // that its HBM traffic overlaps MFMAs instead of stalling the epilogue.
-  constexpr bool PREF = (EPI == EPI_ACCUM);
+  // Accumulate mode with fp32 results and no GELU: staged through LDS like
+  // the store mode (below).  Otherwise the accumulator input of the first
+  // NPRE blocks is loaded into registers during the last k tiles -- PER_IT
+  // blocks in each of two iterations, one load per MFMA slot of the step
+  // after the barrier -- so that its HBM traffic overlaps MFMAs instead of
+  // stalling the epilogue.
+  constexpr bool ACS = (EPI == EPI_ACCUM) && !GELU && sizeof(TOut) == 4 && kStagedStore;
+  constexpr bool PREF = (EPI == EPI_ACCUM) && !ACS;
   constexpr int PER_IT = PREF ? NB / 8 : 0;   // blocks per prefetch iteration
   constexpr int NPRE = 2 * PER_IT;
   f32x4 cpre[NPRE > 0 ? NPRE : 1][4];
@@ -418,9 +421,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // staged row r is kept at chunk c ^ (r & ESW) so that both the 32-row
   // writes and the row reads spread over the banks.  A tile that does not
   // fit the LDS (fp32) goes in EP passes of EJP 32-row blocks per wave.  The
-  // accumulate mode stores from the registers: staging it gave up the
-  // register prefetch of its input and was 15% slower on the ReduceScatter.
-  constexpr bool STAGED = (EPI == EPI_STORE) && kStagedStore;
+  // accumulate mode with fp32 results is staged the same way, and reads its
+  // input in the same 16-byte chunks along the rows, every chunk of a pass
+  // issued before the pass is written to LDS; for whole tiles the first
+  // pass's chunks are loaded during the last-but-one k tile (together
+  // 1.3-1.7% on the ReduceScatter over loading the input block by block in
+  // the registers' layout).  With GELU or bf16 results it keeps the
+  // register path.
+  constexpr bool STAGED = ((EPI == EPI_STORE) && kStagedStore) || ACS;
   constexpr int ESZ = static_cast<int>(sizeof(TOut));
   constexpr int ERB = BN * ESZ;                  // staged row bytes
   constexpr int ECR = ERB / 16;                  // chunks per staged row
@@ -450,6 +458,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   const int e_r = tid / ECR, e_c = tid % ECR;
 
   int cur = 0;                  // buffer of tile kt
+  f32x4 cinv[ACS ? EIT : 1];    // accumulate mode, staged: input chunks of a pass
   // One k tile.  PH = 1, 2: also load the accumulator input of prefetch
   // group PH-1.
   auto iteration = [&](int kt, auto ph) {
@@ -489,7 +498,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int d = 0; d < C; ++d)
           if (d * NMF / C == q) dma_one(cur, kadd, d);
-        if constexpr (PH > 0) {
+        if constexpr (ACS && PH == 3) {
+          // pass 0's input chunks, a k tile ahead of the epilogue
+#pragma unroll
+          for (int it = 0; it < EIT; ++it)
+            if (it * NMF / EIT == q)
+              cinv[it] = *reinterpret_cast<const f32x4*>(
+                  cin + static_cast<int64_t>(m0 + erow(0, it) + e_r) * a.ldcin + n0 + EPC * e_c);
+        }
+        if constexpr (PREF && PH > 0) {
           if (q < 4 * PER_IT) {
             // whole tiles only (peel is false at the matrix edges)
             const int bb = (PH - 1) * PER_IT + q / 4, qq = q % 4;
@@ -506,8 +523,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   };
   using P0 = std::integral_constant<int, 0>;
   const bool peel = NPRE > 0 && KT >= 3 && 4 * PER_IT <= NMF && m0 + BM <= a.M && n0 + BN <= a.N;
-  const int KT_main = peel ? KT - 3 : KT;
+  const bool pf = ACS && KT >= 2 && m0 + BM <= a.M && n0 + BN <= a.N &&
+                  (reinterpret_cast<uintptr_t>(cin) & 15) == 0 && a.ldcin % 4 == 0;
+  const int KT_main = peel ? KT - 3 : (pf ? KT - 2 : KT);
   for (int kt = 0; kt < KT_main; ++kt) iteration(kt, P0{});
+  if constexpr (ACS) {
+    if (pf) {
+      iteration(KT - 2, std::integral_constant<int, 3>{});
+      iteration(KT - 1, P0{});
+    }
+  }
   if constexpr (PREF) {
     if (peel) {
       iteration(KT - 3, std::integral_constant<int, 1>{});
@@ -530,6 +555,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int p = 0; p < EP; ++p) {
       if (p > 0) __syncthreads();   // the previous pass's reads are done
+      if constexpr (ACS) {
+        // this pass's input chunks, in flight while the pass is staged
+        if (p > 0 || !pf) {
+#pragma unroll
+          for (int it = 0; it < EIT; ++it)
+            cinv[it] = load_cin_quad(a, cin, m0 + erow(p, it) + e_r, n0 + EPC * e_c);
+        }
+      }
 #pragma unroll
       for (int jj = 0; jj < EJP; ++jj) {
         const int j = p * EJP + jj;
@@ -565,6 +598,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         const int n = n0 + EPC * e_c;
         if (!whole && (m >= a.M || n >= a.N)) continue;
         TOut* dst = reinterpret_cast<TOut*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
+        if constexpr (ACS) {
+          // C = Cin + part, the register epilogue's addition
+          const f32x4 v = cinv[it] + __builtin_bit_cast(f32x4, raw);
+          if (vec && (whole || n + EPC <= a.N)) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+            for (int e = 0; e < EPC; ++e)
+              if (n + e < a.N) reinterpret_cast<float*>(dst)[e] = v[e];
+          }
+          continue;
+        }
         if (vec && (whole || n + EPC <= a.N)) {
           *reinterpret_cast<u32x4*>(dst) = raw;
         } else {
