@@ -345,7 +345,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
     for (int r = r0; r < rows; r += RP) {
       if (row0 + r >= lim) break;
       const u32x4 v = *reinterpret_cast<const u32x4*>(s + r * ROWB + ((c ^ swz<CPR>(r)) << 4));
-      *reinterpret_cast<u32x4*>(fdst + static_cast<int64_t>(row0 + r) * a.ldfwd + k) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(fdst + static_cast<int64_t>(row0 + r) * a.ldfwd + k));
     }
   };
 
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
           // C = Cin + part, the register epilogue's addition
           const f32x4 v = cinv[it] + __builtin_bit_cast(f32x4, raw);
           if (vec && (whole || n + EPC <= a.N)) {
-            *reinterpret_cast<f32x4*>(dst) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
           } else {
             for (int e = 0; e < EPC; ++e)
               if (n + e < a.N) reinterpret_cast<float*>(dst)[e] = v[e];
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
           continue;
         }
         if (vec && (whole || n + EPC <= a.N)) {
-          *reinterpret_cast<u32x4*>(dst) = raw;
+          __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(dst));
         } else {
           const TOut* src = reinterpret_cast<const TOut*>(&raw);
           for (int e = 0; e < EPC; ++e)
