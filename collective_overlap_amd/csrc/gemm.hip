@@ -133,13 +133,14 @@ __device__ __forceinline__ float gelu_exact(float x) {
 }
 
 // Accumulator input of 4 consecutive columns [n, n+4) of row m (zeros past
-// the edges; store_quad skips those).
+// the edges; store_quad skips those).  The input is read once, so the load
+// is nontemporal and leaves the L2 to the operand tiles.
 __device__ __forceinline__ f32x4 load_cin_quad(const KArgs& a, const float* cinbase, int m, int n) {
   f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
   if (m >= a.M || n >= a.N) return r;
   const float* cin = cinbase + static_cast<int64_t>(m) * a.ldcin + n;
   if (n + 3 < a.N) {
-    r = *reinterpret_cast<const f32x4*>(cin);
+    r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(cin));
   } else {
     for (int e = 0; e < 4; ++e)
       if (n + e < a.N) r[e] = cin[e];
@@ -161,7 +162,7 @@ __device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, int m, i
   if constexpr (sizeof(TOut) == 4) {
     float* c = reinterpret_cast<float*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
     if (full) {
-      *reinterpret_cast<f32x4*>(c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(c));
     } else {
       for (int e = 0; e < 4; ++e)
         if (n + e < a.N) c[e] = v[e];
@@ -171,7 +172,7 @@ __device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, int m, i
     bf16x4 h;
     for (int e = 0; e < 4; ++e) h[e] = static_cast<__bf16>(v[e]);
     if (full) {
-      *reinterpret_cast<bf16x4*>(c) = h;
+      __builtin_nontemporal_store(h, reinterpret_cast<bf16x4*>(c));
     } else {
       for (int e = 0; e < 4; ++e)
         if (n + e < a.N) c[e] = h[e];
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // rank's receive buffer while it sits in LDS.  k tile kt of a row block is
   // written by the one workgroup of that block whose other tile index equals
   // kt modulo the number of such workgroups, which spreads the stores evenly.
+  // The next launch reads it: nontemporal stores.
   const bool fwd_a = a.fwd == FWD_A, fwd_b = a.fwd == FWD_B;
   __bf16* fdst = reinterpret_cast<__bf16*>(a.p.fwd[g]);
   auto forward = [&](int buf, int kt) {
@@ -503,15 +505,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
           for (int it = 0; it < EIT; ++it)
             if (it * NMF / EIT == q)
-              cinv[it] = *reinterpret_cast<const f32x4*>(
-                  cin + static_cast<int64_t>(m0 + erow(0, it) + e_r) * a.ldcin + n0 + EPC * e_c);
+              cinv[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+                  cin + static_cast<int64_t>(m0 + erow(0, it) + e_r) * a.ldcin + n0 + EPC * e_c));
         }
         if constexpr (PREF && PH > 0) {
           if (q < 4 * PER_IT) {
             // whole tiles only (peel is false at the matrix edges)
             const int bb = (PH - 1) * PER_IT + q / 4, qq = q % 4;
-            cpre[bb][qq] = *reinterpret_cast<const f32x4*>(
-                cin_w + (bb / FN) * 32 * a.ldcin + (bb % FN) * 32 + 8 * qq);
+            cpre[bb][qq] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+                cin_w + (bb / FN) * 32 * a.ldcin + (bb % FN) * 32 + 8 * qq));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -599,7 +601,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         if (!whole && (m >= a.M || n >= a.N)) continue;
         TOut* dst = reinterpret_cast<TOut*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
         if constexpr (ACS) {
-          // C = Cin + part, the register epilogue's addition
+          // C = Cin + part, the register epilogue's addition.  Results are
+          // read once, by a later launch: nontemporal stores, here and below.
           const f32x4 v = cinv[it] + __builtin_bit_cast(f32x4, raw);
           if (vec && (whole || n + EPC <= a.N)) {
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
