@@ -20,6 +20,7 @@ CCE_FLAG_GELU = 0x2
 CCE_FLAG_COPY_DMA = 0x4
 CCE_FLAG_FUSED_PERMUTE = 0x8
 CCE_FLAG_BIDIRECTIONAL = 0x10
+CCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3, "lhs_batch": 4}
 RS_MODES = {"slice_lhs_rows": 0, "slice_rhs_cols": 1}
@@ -71,6 +72,12 @@ PROTOTYPES = {
                                                       _U64, _U64, ctypes.POINTER(ctypes.c_int64),
                                                       _I64, _I64, _PP, cce_mat, _P, _SZ, _U32,
                                                       _P]),
+    "cce_looped_einsum_reducescatter_epilogue_noalloc": (_I, [_P, _I, _I, _I, _I, _PP, cce_mat,
+                                                              _PP, cce_mat, _P, _PP, _I64,
+                                                              ctypes.c_double, _U64, _U64,
+                                                              ctypes.POINTER(ctypes.c_int64),
+                                                              _I64, _I64, _PP, cce_mat, _U32,
+                                                              _P]),
     "cce_grouped_gemm": (_I, [_P, _I, _I, _I, _PP, cce_mat, _PP, cce_mat, _PP, cce_mat, _U32, _P]),
     "cce_fused_reduce_epilogue": (_I, [_P, _I, _I, _PP, cce_mat, _P, _I, _P, _I, _I64,
                                        ctypes.c_double, _U64, _U64, _I64, _I64, _I64, _P, _I,

@@ -26,7 +26,7 @@ __all__ = [
     "Context", "cce_shard_schedule", "cce_looped_allgather_einsum",
     "cce_looped_allgather_einsum_workspace", "cce_looped_einsum_reducescatter",
     "cce_looped_einsum_reducescatter_workspace", "cce_looped_einsum_reducescatter_epilogue",
-    "cce_grouped_gemm",
+    "cce_looped_einsum_reducescatter_epilogue_noalloc", "cce_grouped_gemm",
     "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched",
     "cce_fused_allreduce_epilogue", "cce_describe_plan", "cce_debug_fail_op",
     "cce_version",
@@ -271,6 +271,35 @@ def cce_looped_einsum_reducescatter_epilogue(ctx: Context, mode, a, b, bias, res
         int(mask_ld), ptr_array([t.data_ptr() for t in out]), om,
         ws.data_ptr() if ws is not None else None, wsb, flags,
         _stream(stream, out[0].device)), "cce_looped_einsum_reducescatter_epilogue")
+    return out
+
+
+def cce_looped_einsum_reducescatter_epilogue_noalloc(ctx: Context, mode, a, b, bias, residuals,
+                                                     out, p_drop: float, seed: int = 0,
+                                                     offset: int = 0, mask_row0=None,
+                                                     mask_col0: int = 0, mask_ld: int | None = None,
+                                                     flags: int = 0, stream=None):
+    """cce_looped_einsum_reducescatter_epilogue without a workspace: the
+    library's static device scratch (CCE_NOALLOC_SCRATCH_BYTES per GPU) takes
+    its place, and nothing is allocated.  Calls that overlap on one GPU race
+    on that scratch."""
+    n = len(a)
+    mode = RS_MODES[mode] if isinstance(mode, str) else mode
+    am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
+    rm = _same(residuals, "residual") if residuals is not None else None
+    if mask_ld is None:
+        mask_ld = mask_col0 + om.cols
+    rows0 = list(mask_row0) if mask_row0 is not None else [0] * n
+    check(lib().cce_looped_einsum_reducescatter_epilogue_noalloc(
+        ctx.handle, n, mode, _dtype(a[0].dtype), _dtype(out[0].dtype),
+        ptr_array([t.data_ptr() for t in a]), am,
+        ptr_array([t.data_ptr() for t in b]), bm,
+        bias.data_ptr() if bias is not None else None,
+        ptr_array([t.data_ptr() for t in residuals]) if residuals is not None else None,
+        rm.ld if rm is not None else om.cols,
+        float(p_drop), int(seed), int(offset), (ctypes.c_int64 * n)(*rows0), int(mask_col0),
+        int(mask_ld), ptr_array([t.data_ptr() for t in out]), om, flags,
+        _stream(stream, out[0].device)), "cce_looped_einsum_reducescatter_epilogue_noalloc")
     return out
 
 

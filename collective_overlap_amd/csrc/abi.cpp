@@ -16,6 +16,7 @@
 #include <array>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -150,6 +151,50 @@ cce_status ensure_events(cce_ctx* ctx, int n) {
     HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     ctx->events.push_back(e);
   }
+  return CCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free entry point
+// (cce_looped_einsum_reducescatter_epilogue_noalloc): its workspace is this
+// file-scope device array instead of caller memory.  Every GPU the library
+// runs on holds its own copy, at its own address, until the process ends.
+// The array's name is a host-side stand-in, never a device address: host
+// code uses only the address hipGetSymbolAddress returns, looked up once per
+// device (at cce_ctx_create, with that device current) and kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[CCE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+hipError_t g_scratch_err[kMaxScratchDevices] = {};
+
+// Once per device, with `device` current.
+void scratch_setup(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] != nullptr) return;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && p != nullptr) {
+    g_scratch_ptr[device] = p;
+    g_scratch_err[device] = hipSuccess;
+  } else {
+    g_scratch_err[device] = (e == hipSuccess) ? hipErrorInvalidSymbol : e;
+  }
+}
+
+cce_status scratch_of(int device, void** out) {
+  if (device < 0 || device >= kMaxScratchDevices)
+    return fail(CCE_EUNSUPPORTED, "the static scratch covers devices 0.." +
+                                      std::to_string(kMaxScratchDevices - 1));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr)
+    return fail(CCE_EHIP, std::string("hipGetSymbolAddress(scratch) failed on device ") +
+                              std::to_string(device) + ": " +
+                              hipGetErrorString(g_scratch_err[device]));
+  *out = g_scratch_ptr[device];
   return CCE_OK;
 }
 
@@ -807,6 +852,7 @@ cce_status cce_ctx_create(int device, cce_ctx** out) {
   HIP_TRY(hipGetDeviceCount(&count));
   if (device < 0 || device >= count) return fail(CCE_EINVAL, "bad device " + std::to_string(device));
   DeviceGuard guard(device);
+  scratch_setup(device);
   cce_ctx* c = new cce_ctx();
   c->device = device;
   hipError_t e = hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking);
@@ -1116,6 +1162,29 @@ cce_status cce_looped_einsum_reducescatter_epilogue(
   const RsEpiArgs ea{bias, residuals, ld_res, p_drop, seed, offset, mask_row0, mask_col0, mask_ld};
   return rs_impl(ctx, n_ranks, mode, in_t, CCE_F32, out_t, a, a_shape, b, b_shape, out, out_shard,
                  workspace, workspace_bytes, flags, stream, &ea);
+}
+
+cce_status cce_looped_einsum_reducescatter_epilogue_noalloc(
+    cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype in_t, cce_dtype out_t,
+    const void* const* a, cce_mat a_shape, const void* const* b, cce_mat b_shape,
+    const void* bias, const void* const* residuals, int64_t ld_res, double p_drop,
+    uint64_t seed, uint64_t offset, const int64_t* mask_row0, int64_t mask_col0,
+    int64_t mask_ld, void* const* out, cce_mat out_shard, uint32_t flags, cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  // The workspace this call needs, checked against the static maximum before
+  // anything else touches the arguments' memory.
+  RsGeom g;
+  CCE_TRY(rs_geometry(n_ranks, mode, CCE_F32, out_shard, g));
+  if (static_cast<uint64_t>(g.total) > CCE_NOALLOC_SCRATCH_BYTES)
+    return fail(CCE_EUNSUPPORTED, "needs " + std::to_string(g.total) +
+                                      " bytes of workspace; the static scratch holds " +
+                                      std::to_string(CCE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (g.total > 0) CCE_TRY(scratch_of(ctx->device, &ws));
+  const RsEpiArgs ea{bias, residuals, ld_res, p_drop, seed, offset, mask_row0, mask_col0, mask_ld};
+  return rs_impl(ctx, n_ranks, mode, in_t, CCE_F32, out_t, a, a_shape, b, b_shape, out, out_shard,
+                 ws, ws ? static_cast<size_t>(CCE_NOALLOC_SCRATCH_BYTES) : 0, flags, stream, &ea);
 }
 
 cce_status cce_grouped_gemm(cce_ctx* ctx, int n_groups, cce_dtype in_t, cce_dtype out_t,

@@ -304,6 +304,34 @@ cce_status cce_looped_einsum_reducescatter_epilogue(
     size_t workspace_bytes, uint32_t flags, cce_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Allocation-free variant of cce_looped_einsum_reducescatter_epilogue, for
+ * callers that cannot allocate device memory or hand over a workspace: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * allocation.  Arguments, results and errors are those of
+ * cce_looped_einsum_reducescatter_epilogue without the workspace (same
+ * kernels, bit-identical outputs); the caller still passes inputs and
+ * outputs.  The workspace is a static device array of
+ * CCE_NOALLOC_SCRATCH_BYTES inside the library: each GPU holds its own copy
+ * from the library's first context on that device until the process ends.
+ * A call whose workspace (the size cce_looped_einsum_reducescatter_workspace
+ * returns) exceeds it returns CCE_EUNSUPPORTED before anything is enqueued.
+ * The call allocates no device memory (no hipMalloc, hipFree or allocating
+ * library routine); the context's event pool grows on its first looped call,
+ * as for every entry point.  The array keeps the last call's contents and
+ * every call on a GPU shares it: calls on one stream are ordered, but calls
+ * that overlap on one GPU (other streams, other contexts or threads) race on
+ * it.  Devices 0..63.
+ * ---------------------------------------------------------------------- */
+#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+cce_status cce_looped_einsum_reducescatter_epilogue_noalloc(
+    cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype in_t, cce_dtype out_t,
+    const void* const* a, cce_mat a_shape, const void* const* b, cce_mat b_shape,
+    const void* bias, const void* const* residuals, int64_t ld_res, double p_drop,
+    uint64_t seed, uint64_t offset, const int64_t* mask_row0, int64_t mask_col0,
+    int64_t mask_ld, void* const* out, cce_mat out_shard, uint32_t flags, cce_stream stream);
+
+/* ------------------------------------------------------------------------
  * Grouped local GEMM: c[g] = a[g] * b[g]^T for g < n_groups, one launch.
  * This is the per-rank MatMul of two tensors sliced on the contraction dim,
  * producing one local partial per rank ([CC] Figure 3 program, the MatMul
