@@ -91,8 +91,10 @@ class Gpt3Ffn:
 
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
+        # (the fine-grained flag concerns the ReduceScatter's chunk consumer)
         cce.cce_looped_allgather_einsum(ctx, "lhs_rows", self.X, self.W1, self.H, self.ws_ag,
-                                        flags=flags | cce.CCE_FLAG_GELU)
+                                        flags=(flags & ~cce.CCE_FLAG_FINE_GRAINED) |
+                                        cce.CCE_FLAG_GELU)
         rows0 = [r * self.ts for r in range(self.n)]
         if self.fuse_epilogue:
             # The ReduceScatter hands its accumulators straight to the fused
@@ -227,6 +229,7 @@ class Mlp2:
 
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
+        flags &= ~cce.CCE_FLAG_FINE_GRAINED      # (a ReduceScatter flag)
         cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W1, self.X, self.H,
                                         flags=flags | cce.CCE_FLAG_GELU)
         cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W2, self.H, self.Y, flags=flags)
@@ -336,7 +339,8 @@ class AgFp32N2:
 
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
-        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.Wt, self.X, self.Y, flags=flags)
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.Wt, self.X, self.Y,
+                                        flags=flags & ~cce.CCE_FLAG_FINE_GRAINED)
         cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, 0.1, 0, 0)
 
     def oracle_sample(self, t=64):
@@ -442,6 +446,9 @@ def main(argv=None):
                     help="gpt3_ffn_n8: the ReduceScatter stores its fp32 result and a second "
                          "call applies the epilogue (default: one call, the accumulators go "
                          "straight into the epilogue)")
+    ap.add_argument("--fine-grained", action="store_true",
+                    help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
+                         "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -486,6 +493,8 @@ def main(argv=None):
     log("inputs ready; warmup")
     bid = cce.CCE_FLAG_BIDIRECTIONAL if a.transfer == "bidir" else 0
     main_flags = (cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0) | bid
+    if a.fine_grained:
+        main_flags |= cce.CCE_FLAG_FINE_GRAINED
     for _ in range(a.warmup):
         step.run(ctx, main_flags)
     log(f"timed region (permute {a.permute})")
@@ -603,6 +612,7 @@ def main(argv=None):
         "dtype": step.dtype,
         "data": "synthetic (seeded torch generators; no dataset)",
         "config": dict(step.config(), permute=a.permute,
+                       **({"chunk_consumer": "in the last launch"} if a.fine_grained else {}),
                        **({"epilogue": "fused_allreduce"} if a.allreduce else {}),
                        **({"epilogue": "in the ReduceScatter" if step.fuse_epilogue
                            else "separate call"} if hasattr(step, "fuse_epilogue") else {}),

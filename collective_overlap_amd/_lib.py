@@ -20,6 +20,7 @@ CCE_FLAG_GELU = 0x2
 CCE_FLAG_COPY_DMA = 0x4
 CCE_FLAG_FUSED_PERMUTE = 0x8
 CCE_FLAG_BIDIRECTIONAL = 0x10
+CCE_FLAG_FINE_GRAINED = 0x20
 CCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3, "lhs_batch": 4}
@@ -59,6 +60,8 @@ PROTOTYPES = {
     "cce_ctx_destroy": (_I, [_P]),
     "cce_ctx_set_profiling": (_I, [_P, _I]),
     "cce_ctx_read_profile": (_I, [_P, _I, ctypes.POINTER(cce_prof_record), ctypes.POINTER(_I)]),
+    "cce_ctx_check_signals": (_I, [_P, _P]),
+    "cce_debug_signal_giveup": (_I, [_I]),
     "cce_shard_schedule": (_I, [_I, _I, ctypes.POINTER(ctypes.c_int32)]),
     "cce_looped_allgather_einsum_workspace": (_I, [_I, _I, _I, _I, cce_mat, cce_mat,
                                                    ctypes.POINTER(_SZ)]),

@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_BIDIRECTIONAL, CCE_FLAG_COPY_DMA,
-                   CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
+                   CCE_FLAG_FINE_GRAINED, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
                    CCE_FLAG_SERIAL,
                    AG_MODES, RS_MODES,
                    cce_mat, check, lib, ptr_array)
@@ -29,9 +29,9 @@ __all__ = [
     "cce_looped_einsum_reducescatter_epilogue_noalloc", "cce_grouped_gemm",
     "cce_fused_reduce_epilogue", "cce_fused_reduce_epilogue_batched",
     "cce_fused_allreduce_epilogue", "cce_describe_plan", "cce_debug_fail_op",
-    "cce_version",
+    "cce_debug_signal_giveup", "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
-    "CCE_FLAG_BIDIRECTIONAL",
+    "CCE_FLAG_BIDIRECTIONAL", "CCE_FLAG_FINE_GRAINED",
     "AG_MODES", "RS_MODES",
 ]
 
@@ -106,6 +106,13 @@ class Context:
         return [dict(kind=kinds.get(r.kind, str(r.kind)), iter=r.iter, ms=r.ms, flops=r.flops,
                      bytes=r.bytes) for r in recs[:n.value]]
 
+    def check_signals(self, stream=None):
+        """Wait for `stream` (default: the current one), then raise CceError
+        (CCE_EHIP) if a fine-grained chunk consumer gave up waiting since the
+        last check; clears the count."""
+        check(lib().cce_ctx_check_signals(self._h, _stream(stream, self.device)),
+              "cce_ctx_check_signals")
+
     def close(self):
         if self._h:
             lib().cce_ctx_destroy(self._h)
@@ -152,6 +159,13 @@ def cce_debug_fail_op(index: int) -> None:
     """Error-path test hook: plan operation `index` (1-based) of the next
     looped call on this thread fails as a HIP error would; 0 disarms."""
     check(lib().cce_debug_fail_op(int(index)), "cce_debug_fail_op")
+
+
+def cce_debug_signal_giveup(polls: int) -> None:
+    """Test hook of the fine-grained overlap: in the next CCE_FLAG_FINE_GRAINED
+    call on this thread the first producers withhold their ready words and
+    every waiting consumer gives up after at most `polls` polls; 0 disarms."""
+    check(lib().cce_debug_signal_giveup(int(polls)), "cce_debug_signal_giveup")
 
 
 def cce_looped_allgather_einsum_workspace(n_ranks, mode, in_dtype, out_dtype, looped_shape,

@@ -51,6 +51,10 @@ COMMON = [
     # Packed fp32 VALU ops stay off: hipcc -O3 would otherwise form them from
     # plain float code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Loops marked for full unrolling stay fully unrolled up to this size: the
+    # GEMM epilogue's passes index the accumulator registers by the pass
+    # number, and a pass left rolled would move them to scratch memory.
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

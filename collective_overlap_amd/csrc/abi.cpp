@@ -32,6 +32,7 @@ struct cce_prof_slot {
 struct cce_ctx {
   int device = 0;
   hipStream_t copy = nullptr;
+  unsigned* err = nullptr;               // device word: chunk consumers that gave up (fine-grained overlap)
   std::vector<hipEvent_t> events;        // ordering events (no timing)
   bool profiling = false;
   std::vector<hipEvent_t> timing_pool;   // timing events, reused
@@ -48,6 +49,11 @@ thread_local std::string g_err;
 // looped call on this thread fails as a HIP error would.  Fires once.
 thread_local int g_fail_at = 0;
 thread_local int g_ops_seen = 0;
+
+// Test hook of the fine-grained overlap's bounded wait (cce_debug_signal_giveup):
+// the next fine-grained call's first producers do not publish and its
+// consumers poll at most this many times.  Fires once.
+thread_local int g_giveup_polls = 0;
 
 bool fail_due() {
   if (g_fail_at <= 0) return false;
@@ -333,6 +339,9 @@ struct RsGeom {
   int H = 2;                      // accumulator chains (halves) per shard
   int64_t acc_ld = 0, half_bytes = 0;
   int64_t region = 0;             // one set of accumulators (cw); the ccw set follows
+  int64_t sig_off = 0;            // chunk signal words (CCE_FLAG_FINE_GRAINED) follow both sets
+  int64_t sig_tiles = 0;          // chunks per output: (64 x 64)-tiles of a shard
+  int64_t sig_words = 0;          // 2 per chunk, n outputs
   int64_t total = 0;              // enough for every flag combination
 };
 
@@ -376,6 +385,13 @@ cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsG
   // The bidirectional form needs a second (counter-clockwise) set; with one
   // rank there are no accumulators at all.
   g.total = (n > 1) ? 2 * g.region : 0;
+  // Two words per output chunk for the fine-grained overlap, counted for the
+  // smallest GEMM tile (64 x 64, the fp32 kernel's), whatever tile the
+  // launch takes.
+  g.sig_off = g.total;
+  g.sig_tiles = ((g.shard + 63) / 64) * ((g.other + 63) / 64);
+  g.sig_words = (n > 1) ? 2LL * n * g.sig_tiles : 0;
+  g.total += align256(4 * g.sig_words);
   if (fused) {
     g.h0 = g.shard;
     g.h1 = 0;
@@ -610,6 +626,7 @@ struct RsCall {
   char* ws;
   hipMemcpyKind copy_kind;
   const RsEpi* epi = nullptr;
+  unsigned* err = nullptr;        // the context's give-up counter (fine-grained overlap)
 };
 
 PtrLd rs_resolve(const RsCall& c, const BufRef& b) {
@@ -685,6 +702,58 @@ cce_status rs_epilogue(cce_ctx* ctx, const RsCall& c, int h, int n_part,
   return prof_end(ctx, s, slot);
 }
 
+// The chunk consumer's arguments of an EPI_FINAL launch of half h (fine-
+// grained overlap): the per-launch part; the per-output part is filled item
+// by item (rs_final_item).  Without the fused epilogue the consumer is the
+// align-and-sum of the two ring directions: no bias, mask or residual.
+void rs_final_launch(const RsCall& c, int h, FinalArgs& f) {
+  const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
+  const int64_t base = h * c.g.h0;   // first row (or column) of the half
+  const size_t eo = esize(c.out_t);
+  f.ld_out = c.oshape.ld;
+  f.sig = reinterpret_cast<unsigned*>(c.ws + c.g.sig_off);
+  f.sig_tiles = c.g.sig_tiles;
+  f.err = c.err;
+  f.cap = kSignalPollCap;
+  f.nopub = 0;
+  if (g_giveup_polls > 0) {
+    f.cap = static_cast<unsigned>(g_giveup_polls);
+    f.nopub = 1;
+  }
+  if (!c.epi) return;
+  const RsEpi& x = *c.epi;
+  f.bias = x.bias ? static_cast<const char*>(x.bias) + (rows_mode ? 0 : base * eo) : nullptr;
+  f.ld_res = x.ld_res;
+  f.mode = x.drop_all ? 2 : (x.dropout ? 1 : 0);
+  f.threshold = x.threshold;
+  f.scale = x.scale;
+  f.key0 = static_cast<uint32_t>(x.seed);
+  f.key1 = static_cast<uint32_t>(x.seed >> 32);
+  f.off0 = static_cast<uint32_t>(x.offset);
+  f.off1 = static_cast<uint32_t>(x.offset >> 32);
+  f.mcol0 = x.mcol0 + (rows_mode ? 0 : base);
+  f.mld = x.mld;
+  f.aligned = (f.mld % 4 == 0) && (f.mcol0 % 4 == 0);
+}
+
+void rs_final_item(const RsCall& c, int h, const Item& it, FinalArgs& f) {
+  const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
+  const int64_t base = h * c.g.h0;
+  const size_t eo = esize(c.out_t);
+  const int s = it.c.rank;
+  f.out[s] = rs_resolve(c, it.c).p;
+  f.other[s] = (it.has_other && it.pair < 0) ? reinterpret_cast<const float*>(rs_resolve(c, it.other).p)
+                                             : nullptr;
+  f.res[s] = nullptr;
+  f.mrow0[s] = 0;
+  if (!c.epi) return;
+  const RsEpi& x = *c.epi;
+  f.res[s] = x.res ? static_cast<const char*>(x.res[s]) +
+                         (rows_mode ? base * x.ld_res * static_cast<int64_t>(eo) : base * eo)
+                   : nullptr;
+  f.mrow0[s] = x.mrow0[s] + (rows_mode ? base : 0);
+}
+
 cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream_t compute) {
   const size_t ein = esize(c.in_t);
   const bool rows_mode = (c.g.mode == CCE_RS_SLICE_LHS_ROWS);
@@ -693,6 +762,13 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
                                                     std::vector<std::array<PtrLd, 2>>(c.g.n)};
   bool has_final[2] = {false, false};
   g_ops_seen = 0;
+  // Fine-grained overlap: the chunk signal words start at zero (a kernel,
+  // not a memset: the call may be captured in a graph).
+  bool fine = false;
+  for (const Op& o : plan.ops) fine = fine || (o.kind == OP_GEMM && o.epi == EPI_FINAL);
+  if (fine)
+    CCE_TRY(launch_zero_words(reinterpret_cast<unsigned*>(c.ws + c.g.sig_off), c.g.sig_words,
+                              compute));
   for (const Op& o : plan.ops) {
     if (fail_due()) return fail(CCE_EHIP, "injected failure at plan op " + std::to_string(g_ops_seen));
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
@@ -767,6 +843,8 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       L.M = c.g.other;
       L.N = ext;
     }
+    const bool final_op = (o.epi == EPI_FINAL);
+    if (final_op) rs_final_launch(c, o.half, L.fin);
     int gi = 0;
     for (const Item& it : o.items) {
       const int r = gi++;
@@ -774,7 +852,15 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       const PtrLd A = rs_resolve(c, it.a), B = rs_resolve(c, it.b);
       PtrLd D = rs_resolve(c, it.c);
       L.out_t = (it.c.kind == B_OUT) ? c.out_t : CCE_F32;
-      if (c.epi && it.c.kind == B_OUT) {
+      if (final_op) {
+        // The chunk consumer writes the output; a paired item stores its
+        // partial at its own accumulator when it claims a chunk first.
+        rs_final_item(c, o.half, it, L.fin);
+        L.fin.oid[r] = static_cast<int8_t>(it.c.rank);
+        L.fin.partner[r] = static_cast<int8_t>(it.pair);
+        D = it.pair >= 0 ? rs_resolve(c, it.meet) : PtrLd{nullptr, c.g.acc_ld};
+        D.ld = c.g.acc_ld;
+      } else if (c.epi && it.c.kind == B_OUT) {
         // One-way form with the fused epilogue: the last partial accumulates
         // in place into the received accumulator (every element is read
         // before it is written, by the same lane), which the epilogue reads.
@@ -860,7 +946,35 @@ cce_status cce_ctx_create(int device, cce_ctx** out) {
     delete c;
     return fail(CCE_EHIP, std::string("hipStreamCreateWithFlags: ") + hipGetErrorString(e));
   }
+  // The fine-grained overlap's give-up counter (cce_ctx_check_signals).
+  e = hipMalloc(reinterpret_cast<void**>(&c->err), 256);
+  if (e == hipSuccess) e = hipMemset(c->err, 0, 256);
+  if (e != hipSuccess) {
+    if (c->err) hipFree(c->err);
+    hipStreamDestroy(c->copy);
+    delete c;
+    return fail(CCE_EHIP, std::string("context error word: ") + hipGetErrorString(e));
+  }
   *out = c;
+  return CCE_OK;
+}
+
+cce_status cce_ctx_check_signals(cce_ctx* ctx, cce_stream stream) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  DeviceGuard guard(ctx->device);
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  unsigned v = 0;
+  HIP_TRY(hipMemcpy(&v, ctx->err, sizeof v, hipMemcpyDeviceToHost));
+  if (v == 0) return CCE_OK;
+  HIP_TRY(hipMemset(ctx->err, 0, sizeof v));
+  return fail(CCE_EHIP, std::to_string(v) + " chunk consumer(s) gave up waiting for the other "
+                                            "producer's partial; their output chunks were not written");
+}
+
+cce_status cce_debug_signal_giveup(int polls) {
+  if (polls < 0) return fail(CCE_EINVAL, "cce_debug_signal_giveup: polls must be >= 0");
+  g_giveup_polls = polls;
   return CCE_OK;
 }
 
@@ -872,6 +986,7 @@ cce_status cce_ctx_destroy(cce_ctx* ctx) {
   for (hipEvent_t e : ctx->events) hipEventDestroy(e);
   for (hipEvent_t e : ctx->timing_pool) hipEventDestroy(e);
   hipStreamDestroy(ctx->copy);
+  if (ctx->err) hipFree(ctx->err);
   delete ctx;
   return CCE_OK;
 }
@@ -1042,16 +1157,24 @@ static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype
                           const RsEpiArgs* ea) {
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
-                CCE_FLAG_BIDIRECTIONAL))
+                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED))
     return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
   const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
+  const bool fine = (flags & CCE_FLAG_FINE_GRAINED) != 0;
+  if (fine && bidir && !fused)
+    return fail(CCE_EUNSUPPORTED, "CCE_FLAG_FINE_GRAINED with CCE_FLAG_BIDIRECTIONAL needs "
+                                  "CCE_FLAG_FUSED_PERMUTE (with copies, the last partial of the "
+                                  "counter-clockwise direction still travels after the loop)");
   if (bidir && 2 * n_ranks > CCE_MAX_RANKS)
     return fail(CCE_EUNSUPPORTED, "the bidirectional form takes at most CCE_MAX_RANKS / 2 ranks");
   if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   RsGeom g;
   CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g, fused));
+  // (the chunk consumers address a published partial by 32-bit offsets)
+  if (fine && g.half_bytes > kMaxOperandBytes)
+    return fail(CCE_EUNSUPPORTED, "CCE_FLAG_FINE_GRAINED: an accumulator exceeds 1 GiB");
   CCE_TRY(check_mat("a_shape", a_shape));
   CCE_TRY(check_mat("b_shape", b_shape));
   const int64_t nn = n_ranks;
@@ -1130,13 +1253,18 @@ static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype
 
   DeviceGuard guard(ctx->device);
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
-  const Plan plan = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, g.h1 > 0, serial, fused)
-                          : build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
+  Plan plan = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, g.h1 > 0, serial, fused)
+                    : build_reducescatter_plan(n_ranks, mode, g.h1 > 0, serial, fused);
+  if (fine) make_fine_grained(plan, ea != nullptr);
   CCE_TRY(ensure_events(ctx, std::max(plan.n_events, 1)));
   RsCall c{g, in_t, out_t, a, a_shape, b, b_shape, out, out_shard, static_cast<char*>(workspace),
            copy_kind(flags)};
   c.epi = ea ? &epi : nullptr;
-  return joined(ctx, static_cast<hipStream_t>(stream), rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream)));
+  c.err = ctx->err;
+  const cce_status st =
+      joined(ctx, static_cast<hipStream_t>(stream), rs_execute(ctx, c, plan, static_cast<hipStream_t>(stream)));
+  if (fine) g_giveup_polls = 0;   // the test hook fires once
+  return st;
 }
 
 cce_status cce_looped_einsum_reducescatter(cce_ctx* ctx, int n_ranks, cce_rs_mode mode,
@@ -1440,8 +1568,10 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
   if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
   if (!dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
-                CCE_FLAG_BIDIRECTIONAL))
+                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED))
     return fail(CCE_EINVAL, "unknown flags");
+  if (kind == 0 && (flags & CCE_FLAG_FINE_GRAINED))
+    return fail(CCE_EINVAL, "CCE_FLAG_FINE_GRAINED applies to the ReduceScatter");
   const bool serial = (flags & CCE_FLAG_SERIAL) != 0;
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
   const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
@@ -1456,12 +1586,16 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
     p = bidir ? build_allgather_plan_bidir(n_ranks, mode, serial, fused)
               : build_allgather_plan(n_ranks, mode, case2 && out_t == CCE_BF16 && n_ranks > 1,
                                      serial, fused);
-  } else if (kind == 1) {
+  } else if (kind == 1 || kind == 2) {
     if (mode != 0 && mode != 1) return fail(CCE_EINVAL, "bad ReduceScatter mode");
+    if ((flags & CCE_FLAG_FINE_GRAINED) && bidir && !fused)
+      return fail(CCE_EUNSUPPORTED, "CCE_FLAG_FINE_GRAINED with CCE_FLAG_BIDIRECTIONAL needs "
+                                    "CCE_FLAG_FUSED_PERMUTE");
     p = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, true, serial, fused)
               : build_reducescatter_plan(n_ranks, mode, true, serial, fused);
+    if (flags & CCE_FLAG_FINE_GRAINED) make_fine_grained(p, kind == 2);
   } else {
-    return fail(CCE_EINVAL, "kind must be 0 or 1");
+    return fail(CCE_EINVAL, "kind must be 0, 1 or 2");
   }
   const std::string s = describe_plan(p);
   if (needed) *needed = s.size() + 1;

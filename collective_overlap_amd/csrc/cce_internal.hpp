@@ -24,9 +24,47 @@ cce_status fail(cce_status s, const std::string& msg);
 enum Epi : int {
   EPI_STORE = 0,        // C = part
   EPI_ACCUM = 1,        // C = Cin + part       (Cin fp32, may alias C)
+  EPI_FINAL = 2,        // Cin + part is the last partial of an output chunk: the
+                        // chunk's consumer (FinalArgs) runs in the same launch
 };
 
 constexpr int kMaxGroups = CCE_MAX_RANKS;
+
+// Fine-grained overlap of the ReduceScatter's last launch with its consumer
+// (CoCoNet's fine-grained overlap of a MatMul with the collective that
+// consumes it, chunk by chunk): every output tile ("chunk") of rank s is
+// complete when its last partials -- one per ring direction -- are computed;
+// the consumer (the align-and-sum of the two directions, or the fused reduce
+// epilogue) then runs for that chunk inside the producing launch.  With two
+// producers in the launch, they claim the chunk through a per-chunk counter:
+// the first stores its fp32 partial at its accumulator (C) and publishes a
+// ready word; the second waits for that word (a bounded poll) and consumes its
+// own partial from registers plus the published one.  The consumer computes
+//   out = residual + keep * ((p_own + p_other) + bias) * scale
+// in the standalone epilogue's order, each step rounded to fp32.
+constexpr unsigned kSignalPollCap = 1u << 18;   // polls before a consumer gives up
+
+struct FinalArgs {
+  int8_t oid[kMaxGroups];               // output (rank) of each group's chunks
+  int8_t partner[kMaxGroups];           // group producing the other partial in this launch, or -1
+  const float* other[kMaxGroups];       // per output: the other partial, already in memory, or NULL
+  const void* res[kMaxGroups];          // per output: residual, or NULL
+  void* out[kMaxGroups];                // per output
+  int64_t mrow0[kMaxGroups];            // per output: global row of its first row (keep mask)
+  const void* bias = nullptr;           // [N] of the output type, or NULL
+  int64_t ld_res = 0, ld_out = 0;
+  int mode = 0;                         // 0 no dropout, 1 dropout, 2 drop everything
+  uint32_t threshold = 0;
+  float scale = 1.0f;
+  uint32_t key0 = 0, key1 = 0, off0 = 0, off1 = 0;
+  int64_t mcol0 = 0, mld = 0;
+  bool aligned = true;                  // 4 | mld and 4 | mcol0: one Philox block per 4 columns
+  unsigned* sig = nullptr;              // [2 * (oid * tiles_per_group + tile)]: claim, ready
+  int64_t sig_tiles = 0;                // chunks per output the signal words hold (>= tiles_per_group)
+  unsigned* err = nullptr;              // counts consumers that gave up waiting
+  unsigned cap = kSignalPollCap;
+  int nopub = 0;                        // test hook: first producers do not publish
+};
 
 struct GemmGroupPtrs {
   const void* a[kMaxGroups];
@@ -50,7 +88,13 @@ struct GemmLaunch {
   int fwd = FWD_NONE;          // forward A or B of every group to p.fwd[g]
   int64_t ldfwd = 0;
   GemmGroupPtrs p{};
+  FinalArgs fin{};             // EPI_FINAL only
 };
+
+// Enqueue a kernel that sets n 32-bit words at p to zero (the chunk signal
+// words of a call, cleared by a kernel rather than a memset so that the call
+// can be captured in a graph).
+cce_status launch_zero_words(unsigned* p, int64_t n, void* stream);
 
 // Enqueue one grouped GEMM on `stream` (a hipStream_t).  Returns CCE_OK or
 // CCE_EHIP.  Shapes must already be validated.
@@ -119,6 +163,14 @@ struct Item {            // one rank's share of a GEMM or copy
   BufRef fwd;            // gemm with a fused permute: writes the looped operand here
   bool has_cin = false;
   bool has_fwd = false;
+  // EPI_FINAL gemm (fine-grained overlap): c is the output the chunk's
+  // consumer writes; `meet` is this item's own accumulator, where it stores
+  // its partial when it is the first of a pair; `other` is the other partial
+  // of the same output -- the pair item's meet (pair >= 0, read after its
+  // ready signal) or a buffer finished by an earlier launch.
+  BufRef meet, other;
+  bool has_other = false;
+  int pair = -1;         // index of the pair item in the same op
 };
 
 // OP_SUM: out = a + c-side input per item (the bidirectional ReduceScatter's
@@ -175,6 +227,13 @@ Plan build_reducescatter_plan(int n, int mode, bool two_halves, bool serial, boo
 // Bidirectional forms ([OV] 5.4.2).  AllGather: case 1 modes only.
 Plan build_allgather_plan_bidir(int n, int mode, bool serial, bool fused);
 Plan build_reducescatter_plan_bidir(int n, int mode, bool two_halves, bool serial, bool fused);
+// Fine-grained overlap (FinalArgs): the consumer of every output chunk runs
+// in the launch that produces the chunk's last partials.  Two-way fused
+// plans: the last GEMM op becomes EPI_FINAL and the align-and-sum op goes.
+// One-way plans with `epilogue`: the final GEMM ops become EPI_FINAL.
+// Returns false (plan unchanged) for a plan it does not apply to (two-way
+// with copies, one-way without an epilogue).
+bool make_fine_grained(Plan& p, bool epilogue);
 
 std::string describe_plan(const Plan& p);
 

@@ -29,6 +29,7 @@
 #include <cstdint>
 
 #include "cce_internal.hpp"
+#include "philox.hpp"
 
 #pragma clang fp contract(off)
 
@@ -58,38 +59,11 @@ struct EArgs {
   bool aligned;             // 4 | mld and 4 | mcol0: two Philox blocks per vector
 };
 
-// ---- Philox4x32-10 -------------------------------------------------------
-struct Philox4 {
-  uint32_t w[4];
-};
-
-__device__ __forceinline__ Philox4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                            uint32_t k0, uint32_t k1) {
-  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
-  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
-    const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
-    c1 = static_cast<uint32_t>(p1);
-    c3 = static_cast<uint32_t>(p0);
-    c0 = n0;
-    c2 = n2;
-    k0 += kW0;
-    k1 += kW1;
-  }
-  return Philox4{{c0, c1, c2, c3}};
-}
-
-__device__ __forceinline__ uint32_t pick(const Philox4& x, uint32_t i) {
-  return i == 0 ? x.w[0] : (i == 1 ? x.w[1] : (i == 2 ? x.w[2] : x.w[3]));
-}
+// ---- Philox4x32-10 (philox.hpp) -------------------------------------------
+__device__ __forceinline__ uint32_t pick(const Philox4& x, uint32_t i) { return philox_pick(x, i); }
 
 __device__ __forceinline__ Philox4 block_for(const EArgs& a, uint64_t blk) {
-  return philox10(static_cast<uint32_t>(blk), static_cast<uint32_t>(blk >> 32), a.off0, a.off1,
-                  a.key0, a.key1);
+  return philox_block(blk, a.off0, a.off1, a.key0, a.key1);
 }
 
 // ---- typed loads / stores -------------------------------------------------

@@ -30,10 +30,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
 #include "cce_internal.hpp"
+#include "philox.hpp"
 
 namespace cce {
 namespace {
@@ -73,6 +75,7 @@ struct KArgs {
   int tiles_m, tiles_n, tiles_per_group, total_tiles;
   int fwd, ldfwd;             // fused permute: operand to forward, its destination ld
   GemmGroupPtrs p;
+  FinalArgs fin;              // EPI_FINAL: the chunk consumer
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -176,6 +179,293 @@ __device__ __forceinline__ void store_quad(const KArgs& a, void* cbase, int m, i
     } else {
       for (int e = 0; e < 4; ++e)
         if (n + e < a.N) c[e] = h[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk consumer of EPI_FINAL launches (fine-grained overlap; FinalArgs in
+// cce_internal.hpp).  Four consecutive columns [n, n+4) of row m at a time,
+// n a multiple of 4: loads of the other partial and of the residual (zeros
+// past column N), and the consumer arithmetic.
+// ---------------------------------------------------------------------------
+template <bool WHOLE = false>
+__device__ __forceinline__ f32x4 load_f32x4_nt(const float* p, int n, int N) {
+  if (WHOLE || n + 3 < N) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N) r[e] = p[e];
+  return r;
+}
+
+template <typename T, bool WHOLE = false>
+__device__ __forceinline__ f32x4 load_t4(const void* base, int64_t idx, int n, int N, bool nt) {
+  f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (sizeof(T) == 4) {
+    const float* p = reinterpret_cast<const float*>(base) + idx;
+    if (WHOLE || n + 3 < N) return nt ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p))
+                             : *reinterpret_cast<const f32x4*>(p);
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) r[e] = p[e];
+  } else {
+    const __bf16* p = reinterpret_cast<const __bf16*>(base) + idx;
+    if (WHOLE || n + 3 < N) {
+      const u32x2 w = nt ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                         : *reinterpret_cast<const u32x2*>(p);
+      const bf16x4 h = __builtin_bit_cast(bf16x4, w);
+      for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(h[e]);
+      return r;
+    }
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) r[e] = static_cast<float>(p[e]);
+  }
+  return r;
+}
+
+// Keep decisions of the 4 elements [n, n+4) of output row m (bit e: element
+// n+e kept), from the Philox mask of the standalone epilogue: element index
+// e = (mrow0 + m) * mld + mcol0 + n + e.
+__device__ __forceinline__ unsigned keep_bits4(const FinalArgs& f, int64_t mrow0, int m, int n) {
+  const int64_t e0 = (mrow0 + m) * f.mld + f.mcol0 + n;
+  unsigned bits = 0;
+  if (f.aligned) {
+    const Philox4 k = philox_block(static_cast<uint64_t>(e0) >> 2, f.off0, f.off1, f.key0, f.key1);
+    for (int e = 0; e < 4; ++e) bits |= (k.w[e] >= f.threshold ? 1u : 0u) << e;
+  } else {
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t ee = static_cast<uint64_t>(e0 + e);
+      const Philox4 k = philox_block(ee >> 2, f.off0, f.off1, f.key0, f.key1);
+      bits |= (philox_pick(k, static_cast<uint32_t>(ee & 3)) >= f.threshold ? 1u : 0u) << e;
+    }
+  }
+  return bits;
+}
+
+// out[m, n..n+3] = r + keep * ((v + w) + b) * scale, in the order of the
+// standalone epilogue kernel (the sum of the partials, the bias, the mask
+// and scale, the residual; each step one fp32 operation, no contraction),
+// rounded once to TOut.  v is this producer's partial; w the other one
+// (has_w), b the bias (f.bias), r the residual (has_r); keep holds the keep
+// bits (keep_bits4) when f.mode is 1.
+template <typename TOut, bool WHOLE = false>
+__device__ __forceinline__ void consume4(const FinalArgs& f, int m, int n, int N, f32x4 v,
+                                         bool has_w, f32x4 w, f32x4 b, bool has_r, f32x4 r,
+                                         unsigned keep, void* out) {
+#pragma clang fp contract(off)
+  float x[4] = {v[0], v[1], v[2], v[3]};
+  if (has_w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] + w[e];
+  }
+  if (f.bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] + b[e];
+  }
+  if (f.mode == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ((keep >> e) & 1u) ? x[e] * f.scale : 0.0f;
+  } else if (f.mode == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = 0.0f;
+  }
+  if (has_r) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] + r[e];
+  }
+  const int64_t oi = static_cast<int64_t>(m) * f.ld_out + n;
+  if constexpr (sizeof(TOut) == 4) {
+    float* o = reinterpret_cast<float*>(out) + oi;
+    if (WHOLE || n + 3 < N) {
+      __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(o));
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) o[e] = x[e];
+    }
+  } else {
+    __bf16* o = reinterpret_cast<__bf16*>(out) + oi;
+    bf16x4 h;
+    for (int e = 0; e < 4; ++e) h[e] = static_cast<__bf16>(x[e]);
+    if (WHOLE || n + 3 < N) {
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), reinterpret_cast<u32x2*>(o));
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) o[e] = h[e];
+    }
+  }
+}
+
+// The partial a first producer publishes crosses workgroups, usually on
+// different XCDs, each with its own L2.  It is written and read with the
+// device-coherent cache policy (sc1): such accesses are performed at the
+// device's coherence point, past the XCD's L2, so neither side has to write
+// back or invalidate its whole L2 -- which is what an agent-scope release or
+// acquire fence does on this chip, and what made every co-running tile
+// re-fetch its operands.  The ready word is stored only after every thread's
+// stores have been performed (vmcnt 0, then the workgroup barrier), and the
+// consumer issues its loads only after it has seen the word.
+constexpr int kDevCoherent = 16;   // buffer instruction cache policy: sc1
+
+template <bool WHOLE = false>
+__device__ __forceinline__ void store_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v, int n,
+                                           int N) {
+  if (WHOLE || n + 3 < N) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDevCoherent);
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[e]), r, off + 4 * e, 0,
+                                              kDevCoherent);
+  }
+}
+
+template <bool WHOLE = false>
+__device__ __forceinline__ f32x4 load_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, int n, int N) {
+  if (WHOLE || n + 3 < N)
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevCoherent));
+  f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N)
+      v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0,
+                                                                            kDevCoherent));
+  return v;
+}
+
+// Chunk protocol of an EPI_FINAL workgroup, run once its partial is in
+// registers.  Returns the role -- 0: the chunk's only producer in this launch
+// (consume; *other is the other partial finished by an earlier launch, or
+// NULL), 1: the first of two producers (store the partial at C with
+// store_dev4, then publish_chunk), 2: the second (consume *other, the pair's
+// partial, after its ready word) -- or -1 when the wait gave up (the
+// workgroup then writes nothing).  The claim is an agent-scope atomic on the
+// chunk's counter; the first producer is already running when the second
+// claims, so the second's wait ends once the first has stored its partial.
+// Every thread of the workgroup must call it.
+// (Values read back from LDS are per-lane to the compiler: the role and the
+// pointer are made wave-uniform with readfirstlane, so that branches on them
+// are scalar and buffer resources built from them need no per-lane loop.)
+__device__ __forceinline__ const float* uniform_ptr(const float* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const float*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int claim_chunk(const KArgs& a, int g, int slot, const float** other) {
+  __shared__ int s_role, s_ok;
+  const int part = a.fin.partner[g];
+  if (part < 0) {
+    *other = a.fin.other[a.fin.oid[g]];
+    return 0;
+  }
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(a.fin.sig + 2 * slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_role = old == 0u ? 1 : 2;
+  }
+  __syncthreads();
+  const int role = __builtin_amdgcn_readfirstlane(s_role);
+  if (role == 1) return 1;
+  if (threadIdx.x == 0) {
+    const unsigned* rdy = a.fin.sig + 2 * slot + 1;
+    unsigned polls = 0;
+    int ok = 0;
+    for (;;) {
+      if (__hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        ok = 1;
+        break;
+      }
+      if (++polls >= a.fin.cap) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    if (!ok) __hip_atomic_fetch_add(a.fin.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = ok;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(s_ok)) return -1;
+  *other = reinterpret_cast<const float*>(a.p.c[part]);
+  return 2;
+}
+
+// The first producer's partial is stored (store_dev4): once every thread's
+// stores have been performed, set the chunk's ready word.  Every thread of
+// the workgroup must call it.
+__device__ __forceinline__ void publish_chunk(const KArgs& a, int slot) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 && !a.fin.nopub)
+    __hip_atomic_store(a.fin.sig + 2 * slot + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tile row of staged read instruction `it` of pass p, for thread row 0 (the
+// staged epilogue of the bf16 kernel: ERI rows per instruction, EJP 32-row
+// blocks per wave and pass, WTM rows per wave).
+template <int ERI, int EJP, int WTM>
+__device__ __forceinline__ int staged_row(int p, int it) {
+  const int lr = ERI * it;
+  return (lr / (32 * EJP)) * WTM + 32 * (p * EJP + (lr / 32) % EJP) + lr % 32;
+}
+
+// Chunk consumer of one staged pass of an EPI_FINAL tile: this producer's
+// partial (Cin + the staged accumulators), the other partial (rpw, when
+// has_pw), the residual and the bias go through consume4.  The pass's keep
+// bits come first, from a rolled loop (the Philox rounds stay out of the
+// unrolled loop, so that the whole pass is straight-line code).  WHOLE: the
+// tile lies inside the matrix -- no per-lane edge checks, so loads and
+// stores of consecutive chunks are counted exactly by the wait counters
+// (a per-lane branch between them makes every wait a full drain, stores
+// included).
+template <typename TOut, bool WHOLE, int EIT, int ERI, int EJP, int WTM, int ERB, int ESW, int EPC>
+__device__ __forceinline__ void consume_pass(const KArgs& a, const char* smem, int p, int m0, int n0,
+                                             int e_r, int e_c, const float* cin,
+                                             __amdgpu_buffer_rsrc_t rpw, bool has_pw,
+                                             const void* resp, void* outp, int64_t mr0, f32x4 b4) {
+  const int n = n0 + EPC * e_c;
+  static_assert(EIT <= 32, "keep bits");
+  uint64_t kb0 = 0, kb1 = 0;   // 4 bits per chunk: chunk it at bit 4 (it % 16) of kb[it / 16]
+  if (a.fin.mode == 1) {
+#pragma unroll 1
+    for (int it = 0; it < EIT; ++it) {
+      const int m = m0 + staged_row<ERI, EJP, WTM>(p, it) + e_r;
+      if (!WHOLE && (m >= a.M || n >= a.N)) continue;
+      const uint64_t bits = keep_bits4(a.fin, mr0, m, n);
+      if (it < 16) kb0 |= bits << (4 * it);
+      else kb1 |= bits << (4 * (it - 16));
+    }
+  }
+  constexpr int CB = 4;
+  static_assert(EIT % CB == 0, "consumer batch");
+#pragma unroll
+  for (int i0 = 0; i0 < EIT; i0 += CB) {
+    // one batch at a time: loads of later batches are not hoisted here
+    // (that would hold every batch's loads in registers at once)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 cv[CB], wv[CB], rv[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int m = m0 + staged_row<ERI, EJP, WTM>(p, i0 + j) + e_r;
+      const bool ok = WHOLE || (m < a.M && n < a.N);
+      cv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      wv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      rv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (ok && cin) cv[j] = load_f32x4_nt<WHOLE>(cin + static_cast<int64_t>(m) * a.ldcin + n, n, a.N);
+      if (ok && has_pw) wv[j] = load_dev4<WHOLE>(rpw, static_cast<uint32_t>((m * a.ldc + n) * 4), n, a.N);
+      if (ok && resp)
+        rv[j] = load_t4<TOut, WHOLE>(resp, static_cast<int64_t>(m) * a.fin.ld_res + n, n, a.N, true);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int it = i0 + j;
+      const int lr = ERI * it + e_r;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + lr * ERB + ((e_c ^ (lr & ESW)) << 4));
+      const int m = m0 + staged_row<ERI, EJP, WTM>(p, it) + e_r;
+      if (!WHOLE && (m >= a.M || n >= a.N)) continue;
+      // (a first iteration's partial has no input: used as is, not added to
+      // zero, which would turn -0 into +0)
+      const f32x4 v = cin ? cv[j] + __builtin_bit_cast(f32x4, raw) : __builtin_bit_cast(f32x4, raw);
+      const unsigned keep =
+          static_cast<unsigned>((it < 16 ? kb0 >> (4 * it) : kb1 >> (4 * (it - 16))) & 15u);
+      consume4<TOut, WHOLE>(a.fin, m, n, a.N, v, has_pw, wv[j], b4, resp != nullptr, rv[j], keep,
+                            outp);
     }
   }
 }
@@ -404,7 +694,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // blocks in each of two iterations, one load per MFMA slot of the step
   // after the barrier -- so that its HBM traffic overlaps MFMAs instead of
   // stalling the epilogue.
-  constexpr bool ACS = (EPI == EPI_ACCUM) && !GELU && sizeof(TOut) == 4 && kStagedStore;
+  // EPI_FINAL (the ReduceScatter's last launch with fine-grained overlap)
+  // takes the staged fp32 accumulate path; its chunk consumer writes TOut.
+  constexpr bool FIN = (EPI == EPI_FINAL);
+  static_assert(!FIN || (kStagedStore && !GELU), "EPI_FINAL runs on the staged fp32 path");
+  constexpr bool ACS = (((EPI == EPI_ACCUM) && sizeof(TOut) == 4) || FIN) && !GELU && kStagedStore;
   constexpr bool PREF = (EPI == EPI_ACCUM) && !ACS;
   constexpr int PER_IT = PREF ? NB / 8 : 0;   // blocks per prefetch iteration
   constexpr int NPRE = 2 * PER_IT;
@@ -431,7 +725,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   // the registers' layout).  With GELU or bf16 results it keeps the
   // register path.
   constexpr bool STAGED = ((EPI == EPI_STORE) && kStagedStore) || ACS;
-  constexpr int ESZ = static_cast<int>(sizeof(TOut));
+  using TS = std::conditional_t<FIN, float, TOut>;   // staged (and stored) element type
+  constexpr int ESZ = static_cast<int>(sizeof(TS));
   constexpr int ERB = BN * ESZ;                  // staged row bytes
   constexpr int ECR = ERB / 16;                  // chunks per staged row
   constexpr int EPC = 16 / ESZ;                  // elements per chunk
@@ -525,7 +820,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   };
   using P0 = std::integral_constant<int, 0>;
   const bool peel = NPRE > 0 && KT >= 3 && 4 * PER_IT <= NMF && m0 + BM <= a.M && n0 + BN <= a.N;
-  const bool pf = ACS && KT >= 2 && m0 + BM <= a.M && n0 + BN <= a.N &&
+  // (EPI_FINAL: no early load -- a consumer tile reads its input batch by
+  // batch with the other partial and the residual, see the staged epilogue)
+  const bool pf = ACS && !FIN && KT >= 2 && m0 + BM <= a.M && n0 + BN <= a.N &&
                   (reinterpret_cast<uintptr_t>(cin) & 15) == 0 && a.ldcin % 4 == 0;
   const int KT_main = peel ? KT - 3 : (pf ? KT - 2 : KT);
   for (int kt = 0; kt < KT_main; ++kt) iteration(kt, P0{});
@@ -552,14 +849,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   wait_vmcnt<0>();
 
   if constexpr (STAGED) {
+    // EPI_FINAL: this tile's role in its chunk (claim_chunk)
+    int role = 0, slot = 0;
+    const float* pw = nullptr;
+    if constexpr (FIN) {
+      slot = a.fin.oid[g] * a.tiles_per_group + tm * a.tiles_n + tn;
+      role = claim_chunk(a, g, slot, &pw);
+      if (role < 0) return;
+    }
     // every wave's last fragment reads are done before LDS is overwritten
     __syncthreads();
+    f32x4 b4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rc = make_rsrc(cbase, kMaxRsrcBytes);
+    if constexpr (FIN) {
+      const int n = n0 + EPC * e_c;   // every chunk of this thread has this column
+      if (role != 1 && a.fin.bias) b4 = load_t4<TOut>(a.fin.bias, n, n, a.N, false);
+    }
 #pragma unroll
     for (int p = 0; p < EP; ++p) {
       if (p > 0) __syncthreads();   // the previous pass's reads are done
       if constexpr (ACS) {
-        // this pass's input chunks, in flight while the pass is staged
-        if (p > 0 || !pf) {
+        // this pass's input chunks, in flight while the pass is staged (a
+        // consumer tile of an EPI_FINAL launch loads them batch by batch)
+        if ((p > 0 || !pf) && !(FIN && (role != 1 || cin == nullptr))) {
 #pragma unroll
           for (int it = 0; it < EIT; ++it)
             cinv[it] = load_cin_quad(a, cin, m0 + erow(p, it) + e_r, n0 + EPC * e_c);
@@ -592,6 +904,51 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         }
       }
       __syncthreads();
+      if constexpr (FIN) {
+        if (role != 1) {
+          // Chunk consumer (consume_pass); one uniform branch on `whole`.
+          const int oid = a.fin.oid[g];
+          const void* resp = a.fin.res[oid];
+          void* outp = a.fin.out[oid];
+          const int64_t mr0 = a.fin.mrow0[oid];
+          const __amdgpu_buffer_rsrc_t rpw = make_rsrc(uniform_ptr(pw), kMaxRsrcBytes);
+          if (whole)
+            consume_pass<TOut, true, EIT, ERI, EJP, WTM, ERB, ESW, EPC>(
+                a, smem, p, m0, n0, e_r, e_c, cin, rpw, pw != nullptr, resp, outp, mr0, b4);
+          else
+            consume_pass<TOut, false, EIT, ERI, EJP, WTM, ERB, ESW, EPC>(
+                a, smem, p, m0, n0, e_r, e_c, cin, rpw, pw != nullptr, resp, outp, mr0, b4);
+          continue;
+        }
+      }
+      if constexpr (FIN) {
+        // The first producer's partial, published to the pair's consumer
+        // (device-coherent stores); whole tiles take a path without per-lane
+        // edge checks.
+        if (whole) {
+#pragma unroll
+          for (int it = 0; it < EIT; ++it) {
+            const int lr = ERI * it + e_r;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + lr * ERB + ((e_c ^ (lr & ESW)) << 4));
+            const int m = m0 + erow(p, it) + e_r;
+            const int n = n0 + EPC * e_c;
+            const f32x4 v = cin ? cinv[it] + __builtin_bit_cast(f32x4, raw) : __builtin_bit_cast(f32x4, raw);
+            store_dev4<true>(rc, static_cast<uint32_t>((m * a.ldc + n) * 4), v, n, a.N);
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < EIT; ++it) {
+            const int lr = ERI * it + e_r;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + lr * ERB + ((e_c ^ (lr & ESW)) << 4));
+            const int m = m0 + erow(p, it) + e_r;
+            const int n = n0 + EPC * e_c;
+            if (m >= a.M || n >= a.N) continue;
+            const f32x4 v = cin ? cinv[it] + __builtin_bit_cast(f32x4, raw) : __builtin_bit_cast(f32x4, raw);
+            store_dev4(rc, static_cast<uint32_t>((m * a.ldc + n) * 4), v, n, a.N);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int it = 0; it < EIT; ++it) {
         const int lr = ERI * it + e_r;
@@ -599,7 +956,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         const int m = m0 + erow(p, it) + e_r;
         const int n = n0 + EPC * e_c;
         if (!whole && (m >= a.M || n >= a.N)) continue;
-        TOut* dst = reinterpret_cast<TOut*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
+        TS* dst = reinterpret_cast<TS*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
         if constexpr (ACS) {
           // C = Cin + part, the register epilogue's addition.  Results are
           // read once, by a later launch: nontemporal stores, here and below.
@@ -615,11 +972,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         if (vec && (whole || n + EPC <= a.N)) {
           __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(dst));
         } else {
-          const TOut* src = reinterpret_cast<const TOut*>(&raw);
+          const TS* src = reinterpret_cast<const TS*>(&raw);
           for (int e = 0; e < EPC; ++e)
             if (n + e < a.N) dst[e] = src[e];
         }
       }
+    }
+    if constexpr (FIN) {
+      if (role == 1) publish_chunk(a, slot);
     }
     return;
   }
@@ -699,13 +1059,59 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
     __syncthreads();
   }
   const int m = m0 + wm * 32 + (lane & 31);
+  if constexpr (EPI == EPI_FINAL) {
+    // the chunk protocol of the bf16 kernel on the register path
+    static_assert(!GELU, "EPI_FINAL has no GELU");
+    const int slot = a.fin.oid[g] * a.tiles_per_group + tm * a.tiles_n + tn;
+    const float* pw = nullptr;
+    const int role = claim_chunk(a, g, slot, &pw);
+    if (role < 0) return;
+    const int oid = a.fin.oid[g];
+    const float* cin = a.p.cin[g];
+    f32x4 cv[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int n = n0 + wn * 32 + 8 * q + 4 * (lane >> 5);
-    f32x4 v = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    const f32x4 cinv = EPI == EPI_ACCUM ? load_cin_quad(a, a.p.cin[g], m, n) : f32x4{};
-    store_quad<TOut, EPI, GELU>(a, a.p.c[g], m, n, v, cinv);
+    for (int q = 0; q < 4; ++q)
+      cv[q] = cin ? load_cin_quad(a, cin, m, n0 + wn * 32 + 8 * q + 4 * (lane >> 5)) : f32x4{};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn * 32 + 8 * q + 4 * (lane >> 5);
+      if (m >= a.M || n >= a.N) continue;
+      const f32x4 part = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      const f32x4 v = cin ? cv[q] + part : part;
+      if (role == 1) {
+        store_dev4(make_rsrc(a.p.c[g], kMaxRsrcBytes), static_cast<uint32_t>((m * a.ldc + n) * 4), v,
+                   n, a.N);
+        continue;
+      }
+      const f32x4 w = pw ? load_dev4(make_rsrc(pw, kMaxRsrcBytes),
+                                     static_cast<uint32_t>((m * a.ldc + n) * 4), n, a.N)
+                         : f32x4{};
+      const void* resp = a.fin.res[oid];
+      const f32x4 r = resp ? load_t4<TOut>(resp, static_cast<int64_t>(m) * a.fin.ld_res + n, n, a.N, true)
+                           : f32x4{};
+      const f32x4 b = a.fin.bias ? load_t4<TOut>(a.fin.bias, n, n, a.N, false) : f32x4{};
+      const unsigned keep = a.fin.mode == 1 ? keep_bits4(a.fin, a.fin.mrow0[oid], m, n) : 0u;
+      consume4<TOut>(a.fin, m, n, a.N, v, pw != nullptr, w, b, resp != nullptr, r, keep,
+                     a.fin.out[oid]);
+    }
+    if (role == 1) publish_chunk(a, slot);
+    return;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn * 32 + 8 * q + 4 * (lane >> 5);
+      f32x4 v = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      const f32x4 cinv = EPI == EPI_ACCUM ? load_cin_quad(a, a.p.cin[g], m, n) : f32x4{};
+      store_quad<TOut, EPI, GELU>(a, a.p.c[g], m, n, v, cinv);
+    }
   }
+}
+
+// Zeroes n 32-bit words (the chunk signal words of a call).
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -713,15 +1119,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 template <typename TOut, int EPI, bool GELU>
 hipError_t launch_typed(const GemmLaunch& L, KArgs& k, hipStream_t s) {
+  bool sig_fits = true;
   auto grid_for = [&](int bm, int bn) {
     k.tiles_m = static_cast<int>((L.M + bm - 1) / bm);
     k.tiles_n = static_cast<int>((L.N + bn - 1) / bn);
     k.tiles_per_group = k.tiles_m * k.tiles_n;
     k.total_tiles = k.tiles_per_group * L.groups;
+    // EPI_FINAL: each output's chunks index its signal words
+    if (EPI == EPI_FINAL && k.tiles_per_group > L.fin.sig_tiles) sig_fits = false;
     return k.total_tiles;
   };
   if (L.in_t == CCE_F32) {
     const int t = grid_for(64, 64);
+    if (!sig_fits) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_f32_kernel<TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
     return hipGetLastError();
   }
@@ -732,12 +1142,15 @@ hipError_t launch_typed(const GemmLaunch& L, KArgs& k, hipStream_t s) {
   };
   if (tiles(256, 256) >= kCUs) {
     const int t = grid_for(256, 256);
+    if (!sig_fits) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   } else if (tiles(256, 128) >= kCUs) {
     const int t = grid_for(256, 128);
+    if (!sig_fits) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 128, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   } else {
     const int t = grid_for(128, 128);
+    if (!sig_fits) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, kBK, kNS, TOut, EPI, GELU>), dim3(t), dim3(256), 0, s, k);
   }
   return hipGetLastError();
@@ -745,6 +1158,7 @@ hipError_t launch_typed(const GemmLaunch& L, KArgs& k, hipStream_t s) {
 
 template <typename TOut>
 hipError_t launch_out(const GemmLaunch& L, KArgs& k, hipStream_t s) {
+  if (L.epi == EPI_FINAL) return launch_typed<TOut, EPI_FINAL, false>(L, k, s);
   if (L.epi == EPI_STORE)
     return L.gelu ? launch_typed<TOut, EPI_STORE, true>(L, k, s)
                   : launch_typed<TOut, EPI_STORE, false>(L, k, s);
@@ -768,9 +1182,20 @@ cce_status launch_grouped_gemm(const GemmLaunch& L, void* stream) {
   k.fwd = L.fwd;
   k.ldfwd = static_cast<int>(L.ldfwd);
   k.p = L.p;
+  k.fin = L.fin;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (L.out_t == CCE_F32) ? launch_out<float>(L, k, s) : launch_out<__bf16>(L, k, s);
   if (e != hipSuccess) return fail(CCE_EHIP, std::string("gemm launch: ") + hipGetErrorString(e));
+  return CCE_OK;
+}
+
+cce_status launch_zero_words(unsigned* p, int64_t n, void* stream) {
+  if (n <= 0) return CCE_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p, n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CCE_EHIP, std::string("zero_words launch: ") + hipGetErrorString(e));
   return CCE_OK;
 }
 

@@ -518,6 +518,78 @@ Plan build_reducescatter_plan_bidir(int n, int mode, bool two_halves, bool seria
 }
 
 namespace {
+bool same_buf(const BufRef& x, const BufRef& y) {
+  return x.kind == y.kind && x.parity == y.parity && x.half == y.half && x.rank == y.rank;
+}
+}  // namespace
+
+bool make_fine_grained(Plan& p, bool epilogue) {
+  if (p.kind != 1) return false;
+  if (p.bidir) {
+    // Two-way ring: out[s] = cw[s] + ccw[s] is the consumer.  Only the fused
+    // form has both last partials in the last launch (with copies, the ccw
+    // one still has to travel).
+    if (!p.fused) return false;
+    bool any = false;
+    for (size_t si = 0; si < p.ops.size(); ++si) {
+      if (p.ops[si].kind != OP_SUM) continue;
+      int last = -1;
+      for (int k = static_cast<int>(si) - 1; k >= 0; --k)
+        if (p.ops[k].kind == OP_GEMM) {
+          last = k;
+          break;
+        }
+      if (last < 0) return false;
+      Op& g = p.ops[last];
+      const Op sum = p.ops[si];
+      for (const Item& o : sum.items) {
+        int icw = -1, iccw = -1;
+        for (int q = 0; q < static_cast<int>(g.items.size()); ++q) {
+          if (same_buf(g.items[q].c, o.a)) icw = q;
+          if (same_buf(g.items[q].c, o.cin)) iccw = q;
+        }
+        if (icw < 0) return false;   // the cw chain always ends in the last launch
+        Item& cw = g.items[icw];
+        cw.meet = cw.c;
+        cw.c = o.c;
+        cw.other = o.cin;
+        cw.has_other = true;
+        if (iccw >= 0) {
+          Item& ccw = g.items[iccw];
+          ccw.meet = ccw.c;
+          ccw.c = o.c;
+          ccw.other = o.a;
+          ccw.has_other = true;
+          cw.pair = iccw;
+          ccw.pair = icw;
+        }
+      }
+      g.epi = EPI_FINAL;
+      g.final_store = true;
+      p.ops.erase(p.ops.begin() + static_cast<std::ptrdiff_t>(si));
+      --si;
+      any = true;
+    }
+    return any;
+  }
+  // One-way ring: the last partial of each output is the only one in its
+  // launch; with the fused epilogue as consumer it writes the output itself.
+  if (!epilogue) return false;
+  bool any = false;
+  for (Op& o : p.ops) {
+    if (o.kind != OP_GEMM || !o.final_store) continue;
+    for (Item& it : o.items) {
+      it.meet = it.c;
+      it.pair = -1;
+      it.has_other = false;
+    }
+    o.epi = EPI_FINAL;
+    any = true;
+  }
+  return any;
+}
+
+namespace {
 
 std::string bufname(const BufRef& b) {
   char s[64];
@@ -565,13 +637,28 @@ std::string describe_plan(const Plan& p) {
         const bool slice_out = p.kind == 0 && o.kind == OP_GEMM &&
                                (p.mode == CCE_AG_LHS_ROWS || p.mode == CCE_AG_RHS_COLS ||
                                 p.mode == CCE_AG_LHS_BATCH);
-        std::string rd, wr, sh, xs;
-        for (const Item& it : o.items) {
+        std::string rd, wr, sh, xs, prs;
+        for (size_t q = 0; q < o.items.size(); ++q) {
+          const Item& it = o.items[q];
           std::string ir = bufname(it.a), iw = bufname(it.c);
           if (slice_out && it.c.kind == B_OUT) iw += ".s" + std::to_string(it.shard);
           if (o.kind == OP_GEMM) ir += "+" + bufname(it.b);
           if (it.has_cin) ir += "+" + bufname(it.cin);
           if (it.has_fwd) iw += "+" + bufname(it.fwd);
+          // EPI_FINAL: a paired item stores its partial at its meet buffer
+          // when it claims the chunk first, and reads the pair's meet buffer
+          // only after the pair's ready signal (listed under pairs=, not r=).
+          if (o.kind == OP_GEMM && o.epi == EPI_FINAL) {
+            if (it.pair >= 0) {
+              iw += "+" + bufname(it.meet);
+              if (static_cast<int>(q) < it.pair) {
+                if (!prs.empty()) prs += ",";
+                prs += std::to_string(q) + ":" + std::to_string(it.pair);
+              }
+            } else if (it.has_other) {
+              ir += "+" + bufname(it.other);
+            }
+          }
           if (!rd.empty()) rd += ",";
           rd += ir;
           if (!wr.empty()) wr += ",";
@@ -583,7 +670,9 @@ std::string describe_plan(const Plan& p) {
         }
         for (char& ch : rd) if (ch == '+') ch = ',';
         for (char& ch : wr) if (ch == '+') ch = ',';
-        out += " r=" + rd + " w=" + wr + " x=" + xs + " shard=" + sh + "\n";
+        out += " r=" + rd + " w=" + wr + " x=" + xs + " shard=" + sh;
+        if (!prs.empty()) out += " pairs=" + prs;
+        out += "\n";
         break;
       }
     }

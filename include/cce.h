@@ -104,6 +104,35 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
                                   and both ReduceScatter modes; n_ranks <= 32.
                                   Combines with SERIAL, GELU, COPY_DMA and
                                   FUSED_PERMUTE. */
+#define CCE_FLAG_FINE_GRAINED 0x20u /* [CC] fine-grained overlap: the consumer
+                                  of each output chunk (tile) of a looped
+                                  Einsum-ReduceScatter -- the align-and-sum of
+                                  the two ring directions, or the fused reduce
+                                  epilogue -- runs inside the launch that
+                                  produces the chunk's last partials, as soon
+                                  as that chunk is complete, instead of in a
+                                  launch after the loop.  The two producers of
+                                  a chunk claim it through a per-chunk counter
+                                  in the workspace: the first stores its fp32
+                                  partial and publishes a ready word, the
+                                  second waits for that word (a bounded poll)
+                                  and writes the chunk's output from its own
+                                  partial and the published one.  Results are
+                                  bit-identical to the form without the flag.
+                                  Applies to the two-way ring with
+                                  CCE_FLAG_FUSED_PERMUTE (both ReduceScatter
+                                  entry points) and to the one-way ring of
+                                  cce_looped_einsum_reducescatter_epilogue
+                                  (any permute form); the one-way
+                                  cce_looped_einsum_reducescatter already
+                                  writes its output from its last launch, so
+                                  the flag changes nothing there; the two-way
+                                  ring with copies returns CCE_EUNSUPPORTED.
+                                  A consumer that waits too long (it cannot
+                                  under the protocol: the first producer is
+                                  already running) gives up, leaves its chunk
+                                  unwritten and counts the event for
+                                  cce_ctx_check_signals. */
 
 /* Status text; never NULL. */
 const char* cce_status_string(cce_status s);
@@ -118,6 +147,14 @@ const char* cce_version(void);
  * priority, non-blocking) and a pool of events.  *out receives the context. */
 cce_status cce_ctx_create(int device, cce_ctx** out);
 cce_status cce_ctx_destroy(cce_ctx* ctx);
+
+/* Fine-grained overlap status (CCE_FLAG_FINE_GRAINED): waits for the work
+ * queued on `stream`, then reads and clears the context's device error word,
+ * which counts chunk consumers that gave up waiting for their pair's partial
+ * (those chunks' outputs were not written).  Returns CCE_EHIP, with the count
+ * in cce_last_error(), when it is nonzero, CCE_OK otherwise.  Blocks the
+ * host. */
+cce_status cce_ctx_check_signals(cce_ctx* ctx, cce_stream stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  While profiling is enabled on a context, every GEMM launch,
@@ -458,8 +495,13 @@ int cce_overlap_choose(double comp, double comm0, double shard_bytes0, double co
  * stream is "compute" or "copy"; op is gemm, copy, record or wait; gemm and
  * copy lines list the symbolic buffers they read (r=) and write (w=); record
  * and wait lines name an event (ev=).  kind 0 = AllGather (mode is a
- * cce_ag_mode), kind 1 = ReduceScatter (mode is a cce_rs_mode).  Used to check
- * the stream/event ordering for races on the CPU.
+ * cce_ag_mode), kind 1 = ReduceScatter, kind 2 = ReduceScatter with the fused
+ * epilogue (mode is a cce_rs_mode).  With CCE_FLAG_FINE_GRAINED, the gemm
+ * line of the launch that runs the chunk consumers has epi=2 and lists the
+ * pairs of items that claim chunks together (pairs=i:j; a paired item stores
+ * its partial at its own accumulator, named among its writes, when it claims
+ * the chunk first, and the other reads it only after the ready signal).  Used
+ * to check the stream/event ordering for races on the CPU.
  * ---------------------------------------------------------------------- */
 cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t,
                              uint32_t flags, char* buf, size_t buf_len, size_t* needed);
@@ -477,6 +519,14 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t,
  * path and of the state a failed call leaves behind.
  * ---------------------------------------------------------------------- */
 cce_status cce_debug_fail_op(int index);
+
+/* Test hook of the fine-grained overlap's bounded wait: in the next
+ * CCE_FLAG_FINE_GRAINED call on this thread, the first producer of each
+ * chunk does not publish its ready word and every waiting consumer gives up
+ * after at most `polls` polls, so the give-up path runs while every kernel
+ * still ends normally.  polls >= 1 arms the hook (it fires once), 0 disarms
+ * it, a negative value returns CCE_EINVAL. */
+cce_status cce_debug_signal_giveup(int polls);
 
 #ifdef __cplusplus
 }

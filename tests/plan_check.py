@@ -27,6 +27,7 @@ class POp:
     reads: set = field(default_factory=set)
     writes: set = field(default_factory=set)
     items: list = field(default_factory=list)   # per rank: (reads, writes)
+    pairs: list = field(default_factory=list)   # item pairs that claim chunks together
 
 
 def parse(text: str) -> list[POp]:
@@ -44,6 +45,8 @@ def parse(text: str) -> list[POp]:
             op.writes = set(attrs["w"].split(","))
             op.items = [(set(x.split(">")[0].split("+")), set(x.split(">")[1].split("+")))
                         for x in attrs.get("x", "").split(",") if x]
+            op.pairs = [tuple(int(v) for v in pr.split(":"))
+                        for pr in attrs.get("pairs", "").split(",") if pr]
         ops.append(op)
     return ops
 
@@ -105,12 +108,21 @@ def intra_op_conflicts(op: POp) -> list[str]:
     """The items of one operation run concurrently (one kernel, or one
     batch of copies): no item may write what another item touches, and an
     item may overlap its own reads only by updating a buffer in place
-    (its accumulator input is its output)."""
+    (its accumulator input is its output).  The one exception is a declared
+    pair of a fine-grained launch (pairs=i:j): both name the output chunk
+    among their writes, and the chunk claim lets exactly one of them write
+    it; every other buffer they share is still a conflict."""
     out = []
+    paired = {(i, j) for i, j in op.pairs} | {(j, i) for i, j in op.pairs}
     for i, (ri, wi) in enumerate(op.items):
         for j, (rj, wj) in enumerate(op.items):
-            if i != j and wi & (rj | wj):
-                out.append(f"op {op.idx}: item {i} writes {sorted(wi & (rj | wj))} used by item {j}")
+            if i == j:
+                continue
+            shared = wi & (rj | wj)
+            if (i, j) in paired:
+                shared = {b for b in shared if not (b.startswith("out") and b in wj and b not in rj)}
+            if shared:
+                out.append(f"op {op.idx}: item {i} writes {sorted(shared)} used by item {j}")
         own = wi & ri
         if own and not (op.kind == "gemm" and len(own) == 1 and len(ri) == 3):
             out.append(f"op {op.idx}: item {i} reads and writes {sorted(own)}")

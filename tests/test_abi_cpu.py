@@ -227,7 +227,10 @@ def test_reducescatter_workspace_and_validation(cce):
     nb = ctypes.c_size_t()
     assert cce.cce_looped_einsum_reducescatter_workspace(
         8, 0, 0, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 0
-    assert nb.value == 2 * 2 * 8 * 2 * 1024 * 4096 * 4    # two chains, two directions
+    # two chains, two directions; then the chunk signal words of the
+    # fine-grained overlap: 2 per (64 x 64)-tile of each of the 8 outputs
+    sig = 2 * 8 * (2048 // 64) * (4096 // 64) * 4
+    assert nb.value == 2 * 2 * 8 * 2 * 1024 * 4096 * 4 + (sig + 255) // 256 * 256
     # bf16 travelling accumulator is not offered
     assert cce.cce_looped_einsum_reducescatter_workspace(
         8, 0, 1, cce_mat(2048, 4096, 4096), ctypes.byref(nb)) == 2
