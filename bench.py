@@ -79,6 +79,11 @@ class Gpt3Ffn:
             n, "slice_lhs_rows", (ts, self.Hd)), dtype=torch.uint8, device=dev)
         self.flops = 2 * (2.0 * self.T * self.Hd * fs * n)
         self.p = 0.1
+        # The fused epilogue's algorithmic bytes per step: one fp32 partial
+        # (the reduced result), the bf16 residual and output, the bias.  The
+        # two-way ring's epilogue reads two fp32 accumulators (cw and ccw),
+        # so the bytes it moves exceed these by one fp32 plane.
+        self.epi_alg_bytes = self.T * self.Hd * (4 + 2 + 2) + self.Hd * 2
 
     def config(self):
         return {"workload": self.name, "n_ranks": self.n, "tokens": self.T, "hidden": self.Hd,
@@ -155,6 +160,7 @@ class AttnOutProj:
     name = "attn_outproj_n8"
     sample_default, sample_cap = 16, 8192      # token rows in the oracle sample
     dtype = "bf16"
+    has_permute = False        # local GEMMs, then the fused reduction: no ring
 
     def __init__(self, dev):
         import torch
@@ -170,6 +176,7 @@ class AttnOutProj:
         self.out = torch.empty((self.M, self.N), device=dev, dtype=bf)
         self.flops = 2.0 * self.M * self.N * self.K * n
         self.p = 0.1
+        self.epi_alg_bytes = self.M * self.N * 2 * (n + 2) + self.N * 2   # 8 partials + R + out, bias
 
     def config(self):
         return {"workload": self.name, "n_ranks": self.n, "tokens": self.M, "in_shard": self.K,
@@ -355,6 +362,8 @@ class AgFp32N2:
 
 
 WORKLOADS = {c.name: c for c in (Gpt3Ffn, AttnOutProj, Mlp2, RsN8, AgFp32N2)}
+# the configurations in the order the workload list of the benchmark names them
+WORKLOAD_ORDER = ["ag_fp32_n2", "attn_outproj_n8", "mlp2_n4", "rs_n8", "gpt3_ffn_n8"]
 
 
 def _f64(t):
@@ -426,6 +435,164 @@ def measured_traffic(workload, permute, transfer):
     return t["gemm_bytes_per_launch"]["mean"]
 
 
+def epilogue_summary(recs, step):
+    """Rates of the fused epilogue launches: over the bytes each launch moves,
+    and over the workload's algorithmic bytes (one reduced partial) when
+    those differ (the two-way ring's epilogue reads both chains' fp32
+    accumulators)."""
+    epi = [r for r in recs if r["kind"] == "epilogue"]
+    if not epi:
+        return None
+    tb = sum(r["bytes"] for r in epi)
+    tm = sum(r["ms"] for r in epi)
+    gbs = tb / (tm * 1e-3) / 1e9
+    out = {"GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "launches": len(epi), "avg_launch_ms": round(tm / len(epi), 4),
+           "bytes_per_launch": tb / len(epi), "bytes": "moved by the launch"}
+    alg = getattr(step, "epi_alg_bytes", None)
+    if alg and abs(alg - tb / len(epi)) > 1e-3 * alg:
+        ag = alg / (tm / len(epi) * 1e-3) / 1e9
+        out["algorithmic"] = {"bytes_per_launch": alg, "GB/s": round(ag, 1),
+                              "frac_of_hbm_peak": round(ag / PEAK_HBM_GBS, 4),
+                              "bytes": "one reduced fp32 partial + residual + output + bias"}
+    return out
+
+
+def measure(step, ctx, workload, steps, warmup, main_flags, bid, permute, transfer, serial=True):
+    """One workload: the timed steps (with the library's per-launch timing
+    events), the dominant GEMM launch's roofline, the epilogue's HBM rate, the
+    unlooped (monolithic) comparison, and the permute forms (stream, serial,
+    fused) with the hidden copy fraction."""
+    import torch
+    import collective_overlap_amd as cce
+    log(f"{workload}: warmup")
+    for _ in range(warmup):
+        step.run(ctx, main_flags)
+    log(f"{workload}: timed region (permute {permute})")
+    wall, recs = timed(step, ctx, steps, main_flags, profile=True)
+    ms_per_step = wall / steps * 1e3
+    value = step.flops * steps / wall / 1e12
+    roof, per_shape = gemm_roofline(recs, step.dtype, steps)
+    if roof is not None:
+        roof["traffic"] = measured_traffic(workload, permute, transfer)
+        if roof["traffic"] is not None:
+            roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 counters)"
+    epi_info = epilogue_summary(recs, step)
+    gemm_ms = sum(r["ms"] for r in recs if r["kind"] == "gemm") / steps
+
+    mono = None
+    if hasattr(step, "monolithic") and serial:
+        # The decomposition's cost: the same FLOPs as one grouped GEMM per
+        # layer on pre-gathered operands, against the looped step.
+        log(f"{workload}: the same layers unlooped (monolithic grouped GEMMs)")
+        run_mono = step.monolithic()
+        for _ in range(max(1, warmup // 2)):
+            run_mono(ctx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_mono(ctx)
+        torch.cuda.synchronize()
+        mono_ms = (time.perf_counter() - t0) / steps * 1e3
+        mono = {"ms": round(mono_ms, 4), "TFLOP/s": round(step.flops / (mono_ms * 1e-3) / 1e12, 2),
+                "looped_step_over_monolithic": round(ms_per_step / mono_ms, 4),
+                "looped_gemms_over_monolithic": round(gemm_ms / mono_ms, 4)}
+        del run_mono
+        torch.cuda.empty_cache()
+
+    overlap = None
+    if serial and getattr(step, "has_permute", True):
+        log(f"{workload}: copies on a second stream; the same kernels serialised")
+        res = {}
+        for name, fl in (("stream", bid), ("serial", cce.CCE_FLAG_SERIAL | bid)):
+            for _ in range(max(1, warmup // 2)):
+                step.run(ctx, fl)
+            w, r = timed(step, ctx, steps, fl, profile=True)
+            res[name] = (w / steps * 1e3, r)
+        fused_ms = ms_per_step if main_flags & cce.CCE_FLAG_FUSED_PERMUTE else None
+        if fused_ms is None:
+            fl = cce.CCE_FLAG_FUSED_PERMUTE | bid
+            for _ in range(max(1, warmup // 2)):
+                step.run(ctx, fl)
+            w, _ = timed(step, ctx, steps, fl, profile=False)
+            fused_ms = w / steps * 1e3
+        s_ms, srecs = res["serial"]
+        st_ms = res["stream"][0]
+        copy_ms = sum(r["ms"] for r in srecs if r["kind"] == "copy") / steps
+        copy_bytes = sum(r["bytes"] for r in srecs if r["kind"] == "copy") / steps
+        base = s_ms - copy_ms            # the same GEMMs and epilogues without the copies
+        hidden = (round(min(1.0, max(0.0, 1.0 - (st_ms - base) / copy_ms)), 4)
+                  if copy_ms > 0 else None)
+        overlap = {"serial_ms": round(s_ms, 3), "stream_ms": round(st_ms, 3),
+                   "copy_ms_serial": round(copy_ms, 3),
+                   "copy_GB/s_serial": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
+                   "hidden_copy_frac_stream": hidden,
+                   # The fused form has no copies to hide: the GEMMs send the
+                   # data themselves.  Its step is compared with the serial
+                   # step less its copies; in the ReduceScatter the two run
+                   # different chains (two half-shard chains serial, one
+                   # whole-shard chain fused), so the ratio mixes the chain
+                   # count with the cost of the forwarding stores.
+                   "fused": {"permute": "in the GEMMs (no copies)", "step_ms": round(fused_ms, 3),
+                             "over_serial_without_copies": round(fused_ms / base, 4) if base > 0 else None},
+                   "speedup_vs_serial": round(s_ms / ms_per_step, 4)}
+    return {"ms_per_step": ms_per_step, "value": value, "roofline": roof, "per_shape": per_shape,
+            "epilogue": epi_info, "gemm_ms": gemm_ms, "monolithic": mono, "overlap": overlap}
+
+
+def config_summary(name, dev, ctx, steps, warmup, bid_default):
+    """A workload other than the headline, measured in the benchmark's form
+    (fused permute, two-way ring), for the same JSON line: per-step time and
+    rate, the dominant GEMM launch's roofline, the epilogue's HBM rate, the
+    permute forms, the unlooped comparison and parity against the oracle on a
+    small sample."""
+    import torch
+    import collective_overlap_amd as cce
+    step = WORKLOADS[name](dev)
+    bid = bid_default if name != "attn_outproj_n8" else 0
+    flags = cce.CCE_FLAG_FUSED_PERMUTE | bid
+    m = measure(step, ctx, name, steps, warmup, flags, bid, "fused",
+                "bidir" if bid else "one-way", serial=True)
+    # parity of the timed outputs on a small oracle sample (the outputs hold
+    # the last timed step's results)
+    step.run(ctx, flags)
+    torch.cuda.synchronize()
+    _, _, desc, err = step.oracle_sample()
+    bar = 2e-2 if step.dtype == "bf16" else 1e-5
+    roof = m["roofline"]
+    out = {"config": step.config(), "dtype": step.dtype,
+           "ms_per_step": round(m["ms_per_step"], 4),
+           "TFLOP/s": round(m["value"], 2),
+           "frac_of_mfma_peak": round(m["value"] / PEAK_TFLOPS[step.dtype], 4),
+           "gemm_launch": None if roof is None else {
+               k: roof[k] for k in ("achieved", "frac", "avg_launch_ms", "flops_per_launch",
+                                    "launches")},
+           "epilogue": m["epilogue"], "overlap": m["overlap"], "monolithic": m["monolithic"],
+           "parity": {"rel_fro_err_vs_oracle": err, "bar": bar, "ok": err <= bar, "sample": desc}}
+    del step
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_info():
+    """The host's CPU model (from /proc/cpuinfo) and the cores this process
+    may run on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return model, affinity
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +613,9 @@ def main(argv=None):
                     help="gpt3_ffn_n8: the ReduceScatter stores its fp32 result and a second "
                          "call applies the epilogue (default: one call, the accumulators go "
                          "straight into the epilogue)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (by default each is measured after the "
+                         "headline one and reported under `configs` of the same JSON line)")
     ap.add_argument("--fine-grained", action="store_true",
                     help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
                          "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
@@ -490,84 +660,14 @@ def main(argv=None):
         step.fuse_epilogue = False
     ctx = cce.Context(0)
     torch.cuda.synchronize()
-    log("inputs ready; warmup")
     bid = cce.CCE_FLAG_BIDIRECTIONAL if a.transfer == "bidir" else 0
     main_flags = (cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0) | bid
     if a.fine_grained:
         main_flags |= cce.CCE_FLAG_FINE_GRAINED
-    for _ in range(a.warmup):
-        step.run(ctx, main_flags)
-    log(f"timed region (permute {a.permute})")
-    wall, recs = timed(step, ctx, a.steps, main_flags, profile=True)
-    ms_per_step = wall / a.steps * 1e3
-    value = step.flops * a.steps / wall / 1e12
-    roof, per_shape = gemm_roofline(recs, step.dtype, a.steps)
-    if roof is not None:
-        roof["traffic"] = measured_traffic(a.workload, a.permute, a.transfer)
-        if roof["traffic"] is not None:
-            roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 counters)"
-
-    epi = [r for r in recs if r["kind"] == "epilogue"]
-    epi_info = None
-    if epi:
-        tb = sum(r["bytes"] for r in epi)
-        tm = sum(r["ms"] for r in epi)
-        gbs = tb / (tm * 1e-3) / 1e9
-        epi_info = {"GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                    "launches": len(epi), "avg_launch_ms": round(tm / len(epi), 4),
-                    "bytes_per_launch": tb / len(epi)}
-    gemm_ms = sum(r["ms"] for r in recs if r["kind"] == "gemm") / a.steps
-
-    mono = None
-    if hasattr(step, "monolithic") and not a.no_serial:
-        # The decomposition's cost: the same FLOPs as one grouped GEMM per
-        # layer on pre-gathered operands, against the looped step.
-        log("timed region: the same layers unlooped (monolithic grouped GEMMs)")
-        run_mono = step.monolithic()
-        for _ in range(max(1, a.warmup // 2)):
-            run_mono(ctx)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(a.steps):
-            run_mono(ctx)
-        torch.cuda.synchronize()
-        mono_ms = (time.perf_counter() - t0) / a.steps * 1e3
-        mono = {"ms": round(mono_ms, 4), "TFLOP/s": round(step.flops / (mono_ms * 1e-3) / 1e12, 2),
-                "looped_step_over_monolithic": round(ms_per_step / mono_ms, 4),
-                "looped_gemms_over_monolithic": round(gemm_ms / mono_ms, 4)}
-        del run_mono
-        torch.cuda.empty_cache()
-
-    overlap = None
-    has_permute = a.workload not in ("attn_outproj_n8",)
-    if not a.no_serial and has_permute:
-        log("timed regions: copies on a second stream; the same kernels serialised")
-        res = {}
-        for name, fl in (("stream", bid), ("serial", cce.CCE_FLAG_SERIAL | bid)):
-            for _ in range(max(1, a.warmup // 2)):
-                step.run(ctx, fl)
-            w, r = timed(step, ctx, a.steps, fl, profile=True)
-            res[name] = (w / a.steps * 1e3, r)
-        fused_ms = ms_per_step if a.permute == "fused" else None
-        if fused_ms is None:
-            for _ in range(max(1, a.warmup // 2)):
-                step.run(ctx, cce.CCE_FLAG_FUSED_PERMUTE | bid)
-            w, _ = timed(step, ctx, a.steps, cce.CCE_FLAG_FUSED_PERMUTE | bid, profile=False)
-            fused_ms = w / a.steps * 1e3
-        s_ms, srecs = res["serial"]
-        st_ms = res["stream"][0]
-        copy_ms = sum(r["ms"] for r in srecs if r["kind"] == "copy") / a.steps
-        copy_bytes = sum(r["bytes"] for r in srecs if r["kind"] == "copy") / a.steps
-        base = s_ms - copy_ms            # the same GEMMs and epilogues without the copies
-
-        def hidden(t):
-            return round(min(1.0, max(0.0, 1.0 - (t - base) / copy_ms)), 4) if copy_ms > 0 else None
-        overlap = {"serial_ms": round(s_ms, 3), "stream_ms": round(st_ms, 3),
-                   "fused_ms": round(fused_ms, 3), "copy_ms_serial": round(copy_ms, 3),
-                   "copy_GB/s_serial": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
-                   "hidden_copy_frac_stream": hidden(st_ms),
-                   "hidden_copy_frac_fused": hidden(fused_ms),
-                   "speedup_vs_serial": round(s_ms / ms_per_step, 4)}
+    m = measure(step, ctx, a.workload, a.steps, a.warmup, main_flags, bid, a.permute,
+                a.transfer, serial=not a.no_serial)
+    ms_per_step, value, roof, per_shape = m["ms_per_step"], m["value"], m["roofline"], m["per_shape"]
+    epi_info, gemm_ms, mono, overlap = m["epilogue"], m["gemm_ms"], m["monolithic"], m["overlap"]
 
     cpu = None
     parity = None
@@ -592,9 +692,11 @@ def main(argv=None):
             log(f"cpu baseline: {t_next} rows ({dt:.2f} s at {t})")
             t = t_next
             dt, fl, desc, err = step.oracle_sample(t)
+        model, affinity = cpu_info()
         cpu = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle", "sample": desc, "seconds": round(dt, 3),
-               "host_cpus": os.cpu_count(), "cpu_model": platform.processor() or platform.machine()}
+               "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": threads,
+               "cpu_model": model}
         parity = {"rel_fro_err_vs_oracle": err, "bar": 2e-2 if step.dtype == "bf16" else 1e-5,
                   "ok": err <= (2e-2 if step.dtype == "bf16" else 1e-5)}
 
@@ -628,6 +730,16 @@ def main(argv=None):
         "gemm_shapes": list(per_shape.values()),
         "parity": parity,
     }
+    if not a.no_configs:
+        # Every other workload, in the benchmark's form, under one key.
+        configs = {}
+        for name in WORKLOAD_ORDER:
+            if name == a.workload:
+                continue
+            log(f"config {name}")
+            configs[name] = config_summary(name, dev, ctx, min(a.steps, 10), max(2, a.warmup),
+                                           cce.CCE_FLAG_BIDIRECTIONAL)
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
     ctx.close()
     return 0
