@@ -61,6 +61,7 @@ PROTOTYPES = {
     "cce_ctx_set_profiling": (_I, [_P, _I]),
     "cce_ctx_read_profile": (_I, [_P, _I, ctypes.POINTER(cce_prof_record), ctypes.POINTER(_I)]),
     "cce_ctx_check_signals": (_I, [_P, _P]),
+    "cce_ctx_set_copy_stream": (_I, [_P, _P]),
     "cce_debug_signal_giveup": (_I, [_I]),
     "cce_shard_schedule": (_I, [_I, _I, ctypes.POINTER(ctypes.c_int32)]),
     "cce_looped_allgather_einsum_workspace": (_I, [_I, _I, _I, _I, cce_mat, cce_mat,

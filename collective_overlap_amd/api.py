@@ -106,6 +106,15 @@ class Context:
         return [dict(kind=kinds.get(r.kind, str(r.kind)), iter=r.iter, ms=r.ms, flops=r.flops,
                      bytes=r.bytes) for r in recs[:n.value]]
 
+    def set_copy_stream(self, stream=None):
+        """Run the permute copies of this context's looped calls on `stream`
+        (a torch.cuda.Stream or a hipStream_t handle); None restores the
+        context's own copy stream.  The caller keeps the stream alive."""
+        h = None if stream is None else (stream.cuda_stream if hasattr(stream, "cuda_stream")
+                                         else int(stream))
+        self._copy_stream = stream
+        check(lib().cce_ctx_set_copy_stream(self._h, h), "cce_ctx_set_copy_stream")
+
     def check_signals(self, stream=None):
         """Wait for `stream` (default: the current one), then raise CceError
         (CCE_EHIP) if a fine-grained chunk consumer gave up waiting since the

@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcce.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["gemm.hip", "epilogue.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["gemm.hip", "epilogue.hip", "permute.hip", "plan.cpp", "abi.cpp"]
 ARCH = "gfx950"
 
 

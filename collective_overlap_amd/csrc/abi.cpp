@@ -31,7 +31,8 @@ struct cce_prof_slot {
 
 struct cce_ctx {
   int device = 0;
-  hipStream_t copy = nullptr;
+  hipStream_t copy = nullptr;            // the stream the permute copies run on
+  hipStream_t own_copy = nullptr;        // the context's own copy stream
   unsigned* err = nullptr;               // device word: chunk consumers that gave up (fine-grained overlap)
   std::vector<hipEvent_t> events;        // ordering events (no timing)
   bool profiling = false;
@@ -426,6 +427,14 @@ hipMemcpyKind copy_kind(uint32_t flags) {
   return (flags & CCE_FLAG_COPY_DMA) ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
 }
 
+// Copies of the overlapped form run as the library's permute kernel, which
+// shares compute units with the GEMM beside it; the DMA form keeps the DMA
+// engines, and the serial form (the unoverlapped comparison) the runtime's
+// full-device copy.
+bool use_permute_kernel(hipMemcpyKind kind, bool serial) {
+  return kind == hipMemcpyDeviceToDevice && !serial;
+}
+
 hipStream_t stream_of(const Op& o, hipStream_t compute, hipStream_t copy, bool serial) {
   return (serial || o.stream == S_COMPUTE) ? compute : copy;
 }
@@ -501,17 +510,37 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
       int slot;
       CCE_TRY(prof_begin(ctx, s, 1, o.iter, 0.0,
                          2.0 * static_cast<double>(w) * c.lshape.rows * o.items.size(), &slot));
+      // The shard's exact span (contiguous when both sides share the ld): no
+      // read of the caller's memory past its last row.
+      std::vector<PermuteItem> pitems;
+      bool kernel_ok = use_permute_kernel(c.copy_kind, plan.serial);
       for (const Item& it : o.items) {
         const PtrLd src = ag_resolve(c, it.a), dst = ag_resolve(c, it.c);
         if (c.lshape.rows == 0 || w == 0) continue;
+        PermuteItem pi;
+        pi.src = src.p;
+        pi.dst = dst.p;
         if (src.ld == dst.ld) {
-          // the shard's exact span: no read of the caller's memory past its
-          // last row
-          const int64_t span = ((c.lshape.rows - 1) * src.ld + c.lshape.cols) * ein;
-          HIP_TRY(hipMemcpyAsync(dst.p, src.p, span, c.copy_kind, s));
+          pi.rows = 1;
+          pi.width = ((c.lshape.rows - 1) * src.ld + c.lshape.cols) * ein;
         } else {
-          HIP_TRY(hipMemcpy2DAsync(dst.p, dst.ld * ein, src.p, src.ld * ein, w, c.lshape.rows,
-                                   c.copy_kind, s));
+          pi.rows = c.lshape.rows;
+          pi.width = w;
+          pi.src_pitch = src.ld * ein;
+          pi.dst_pitch = dst.ld * ein;
+        }
+        kernel_ok = kernel_ok && permute_item_ok(pi);
+        pitems.push_back(pi);
+      }
+      if (kernel_ok) {
+        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s));
+      } else {
+        for (const PermuteItem& pi : pitems) {
+          if (pi.rows == 1)
+            HIP_TRY(hipMemcpyAsync(pi.dst, pi.src, pi.width, c.copy_kind, s));
+          else
+            HIP_TRY(hipMemcpy2DAsync(pi.dst, pi.dst_pitch, pi.src, pi.src_pitch, pi.width, pi.rows,
+                                     c.copy_kind, s));
         }
       }
       CCE_TRY(prof_end(ctx, s, slot));
@@ -823,9 +852,23 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       if (bytes == 0) continue;
       int slot;
       CCE_TRY(prof_begin(ctx, s, 1, o.iter, 0.0, 2.0 * bytes * o.items.size(), &slot));
+      std::vector<PermuteItem> pitems;
+      bool kernel_ok = use_permute_kernel(c.copy_kind, plan.serial);
       for (const Item& it : o.items) {
         const PtrLd src = rs_resolve(c, it.a), dst = rs_resolve(c, it.c);
-        HIP_TRY(hipMemcpyAsync(dst.p, src.p, bytes, c.copy_kind, s));
+        PermuteItem pi;
+        pi.src = src.p;
+        pi.dst = dst.p;
+        pi.rows = 1;
+        pi.width = bytes;
+        kernel_ok = kernel_ok && permute_item_ok(pi);
+        pitems.push_back(pi);
+      }
+      if (kernel_ok) {
+        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s));
+      } else {
+        for (const PermuteItem& pi : pitems)
+          HIP_TRY(hipMemcpyAsync(pi.dst, pi.src, pi.width, c.copy_kind, s));
       }
       CCE_TRY(prof_end(ctx, s, slot));
       continue;
@@ -941,21 +984,29 @@ cce_status cce_ctx_create(int device, cce_ctx** out) {
   scratch_setup(device);
   cce_ctx* c = new cce_ctx();
   c->device = device;
-  hipError_t e = hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking);
+  hipError_t e = hipStreamCreateWithFlags(&c->own_copy, hipStreamNonBlocking);
   if (e != hipSuccess) {
     delete c;
     return fail(CCE_EHIP, std::string("hipStreamCreateWithFlags: ") + hipGetErrorString(e));
   }
+  c->copy = c->own_copy;
   // The fine-grained overlap's give-up counter (cce_ctx_check_signals).
   e = hipMalloc(reinterpret_cast<void**>(&c->err), 256);
   if (e == hipSuccess) e = hipMemset(c->err, 0, 256);
   if (e != hipSuccess) {
     if (c->err) hipFree(c->err);
-    hipStreamDestroy(c->copy);
+    hipStreamDestroy(c->own_copy);
     delete c;
     return fail(CCE_EHIP, std::string("context error word: ") + hipGetErrorString(e));
   }
   *out = c;
+  return CCE_OK;
+}
+
+cce_status cce_ctx_set_copy_stream(cce_ctx* ctx, cce_stream copy) {
+  clear_error();
+  if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
+  ctx->copy = copy ? static_cast<hipStream_t>(copy) : ctx->own_copy;
   return CCE_OK;
 }
 
@@ -982,10 +1033,10 @@ cce_status cce_ctx_destroy(cce_ctx* ctx) {
   clear_error();
   if (!ctx) return CCE_OK;
   DeviceGuard guard(ctx->device);
-  hipStreamSynchronize(ctx->copy);
+  hipStreamSynchronize(ctx->own_copy);
   for (hipEvent_t e : ctx->events) hipEventDestroy(e);
   for (hipEvent_t e : ctx->timing_pool) hipEventDestroy(e);
-  hipStreamDestroy(ctx->copy);
+  hipStreamDestroy(ctx->own_copy);
   if (ctx->err) hipFree(ctx->err);
   delete ctx;
   return CCE_OK;

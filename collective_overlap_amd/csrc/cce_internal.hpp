@@ -91,6 +91,20 @@ struct GemmLaunch {
   FinalArgs fin{};             // EPI_FINAL only
 };
 
+// Ring-permute copy (permute.hip): `rows` rows of `width` bytes, row i at
+// src + i * src_pitch -> dst + i * dst_pitch.  One launch copies every item
+// of a permute step on the copy stream.  permute_item_ok: base pointers and
+// pitches 16-byte aligned, width even (else the caller uses the runtime's
+// copy).
+constexpr int kMaxPermuteItems = kMaxGroups;
+struct PermuteItem {
+  const void* src = nullptr;
+  void* dst = nullptr;
+  int64_t rows = 0, width = 0, src_pitch = 0, dst_pitch = 0;
+};
+bool permute_item_ok(const PermuteItem& it);
+cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream);
+
 // Enqueue a kernel that sets n 32-bit words at p to zero (the chunk signal
 // words of a call, cleared by a kernel rather than a memset so that the call
 // can be captured in a graph).

@@ -1,0 +1,120 @@
+// Ring-permute copies for gfx950: one launch moves every shard (or
+// accumulator) of one permute step -- the CollectivePermute of the looped
+// CollectiveEinsum (Wang et al., ASPLOS'23, Sections 5.1 and 5.2), rank r's
+// buffer to rank r-1's (and, two-way, r+1's) -- on the copy stream, beside the
+// partial GEMM of the same iteration.
+//
+// The kernel is built to run on the same compute units as that GEMM rather
+// than to take units from it: a workgroup is four waves (one per SIMD) of few
+// registers and no LDS, so it fits beside a GEMM workgroup whose tile leaves
+// registers free, and it needs a small share of a unit's memory path (a
+// permute step moves a few hundred MB over a GEMM launch of 1-2 ms).  Data is
+// read once and written once: 16-byte nontemporal loads and stores, a few in
+// flight per lane.
+//
+// Item layout: `rows` rows of `width` bytes (a multiple of 2), row i at
+// src + i * src_pitch and dst + i * dst_pitch; base pointers and pitches are
+// 16-byte aligned.  A row's last width % 16 bytes are copied 2 bytes at a
+// time, so nothing past the row's last element is read or written.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "cce_internal.hpp"
+
+namespace cce {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct PermArgs {
+  int n;
+  PermuteItem it[kMaxPermuteItems];
+};
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;   // 16-byte loads in flight per lane
+
+// Chunks [c0, c1) of one row (16-byte units), kUnroll loads in flight per
+// lane before their stores.
+__device__ __forceinline__ void copy_chunks(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                            int64_t c0, int64_t c1) {
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (c + u * kThreads < c1) v[u] = __builtin_nontemporal_load(src + c + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (c + u * kThreads < c1) __builtin_nontemporal_store(v[u], dst + c + u * kThreads);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void permute_copy_kernel(PermArgs a) {
+  const PermuteItem& it = a.it[blockIdx.y];
+  const int64_t cpr = it.width >> 4;                    // whole 16-byte chunks per row
+  const char* src = static_cast<const char*>(it.src);
+  char* dst = static_cast<char*>(it.dst);
+  if (it.rows == 1) {
+    // one contiguous span, split evenly over the item's workgroups
+    const int64_t per = (cpr + gridDim.x - 1) / gridDim.x;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t c1 = c0 + per < cpr ? c0 + per : cpr;
+    copy_chunks(reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), c0, c1);
+  } else {
+    // pitched rows, dealt to the item's workgroups
+    for (int64_t r = blockIdx.x; r < it.rows; r += gridDim.x)
+      copy_chunks(reinterpret_cast<const u32x4*>(src + r * it.src_pitch),
+                  reinterpret_cast<u32x4*>(dst + r * it.dst_pitch), 0, cpr);
+  }
+  // Row tails (width % 16 bytes), two bytes at a time, by the first
+  // workgroup of the item.
+  const int64_t half = (it.width & 15) >> 1;
+  if (half && blockIdx.x == 0) {
+    for (int64_t i = threadIdx.x; i < it.rows * half; i += kThreads) {
+      const int64_t r = i / half, off = cpr * 16 + 2 * (i - r * half);
+      *reinterpret_cast<uint16_t*>(dst + r * it.dst_pitch + off) =
+          *reinterpret_cast<const uint16_t*>(src + r * it.src_pitch + off);
+    }
+  }
+}
+
+}  // namespace
+
+bool permute_item_ok(const PermuteItem& it) {
+  const auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return al(it.src) && al(it.dst) && it.rows >= 0 && it.width >= 0 && (it.width & 1) == 0 &&
+         (it.rows <= 1 || ((it.src_pitch & 15) == 0 && (it.dst_pitch & 15) == 0 &&
+                           it.src_pitch >= it.width && it.dst_pitch >= it.width));
+}
+
+cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream) {
+  if (n <= 0) return CCE_OK;
+  if (n > kMaxPermuteItems) return fail(CCE_EINVAL, "permute copy: too many items");
+  PermArgs k{};
+  k.n = n;
+  int64_t biggest = 0;
+  for (int i = 0; i < n; ++i) {
+    k.it[i] = items[i];
+    biggest = items[i].rows * items[i].width > biggest ? items[i].rows * items[i].width : biggest;
+  }
+  if (biggest == 0) return CCE_OK;
+  // 128 workgroups in all, over the items: the copy shares compute units
+  // with the GEMM beside it and spreads its HBM traffic over the GEMM's
+  // duration.  (One per unit, 256, finished sooner but slowed the GEMM's
+  // accumulate epilogues more; 64 or 32 made the copy outlast the GEMM it
+  // hides behind.  GPT-3 FFN two-way stream form: 18.13 / 18.03 / 18.99 /
+  // 19.55 ms for 256 / 128 / 64 / 32.)
+  constexpr int kUnits = 128;
+  int per_item = (kUnits + n - 1) / n;
+  const int64_t chunks = biggest / 16;
+  if (per_item > chunks / (kThreads * kUnroll) + 1) per_item = static_cast<int>(chunks / (kThreads * kUnroll) + 1);
+  hipLaunchKernelGGL(permute_copy_kernel, dim3(per_item, n), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), k);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CCE_EHIP, std::string("permute copy launch: ") + hipGetErrorString(e));
+  return CCE_OK;
+}
+
+}  // namespace cce

@@ -144,9 +144,20 @@ const char* cce_last_error(void);
 const char* cce_version(void);
 
 /* Create a context on HIP device `device`: it owns a copy stream (default
- * priority, non-blocking) and a pool of events.  *out receives the context. */
+ * priority, non-blocking) and a pool of events.  *out receives the context.
+ * It also allocates one 256-byte device word (cce_ctx_check_signals). */
 cce_status cce_ctx_create(int device, cce_ctx** out);
 cce_status cce_ctx_destroy(cce_ctx* ctx);
+
+/* The stream the context's looped calls run their permute copies on (the
+ * second stream of [OV] Section 5.2's asynchronous CollectivePermute): the
+ * caller's `copy` (a hipStream_t of the context's device, e.g. one created
+ * with a compute-unit mask, or one the caller already synchronises with), or
+ * NULL for the context's own.  Work on it is ordered against each call's
+ * `stream` by events as before.  The caller keeps ownership and must keep it
+ * alive while calls of this context are queued on it; the context never
+ * destroys it.  Host-only. */
+cce_status cce_ctx_set_copy_stream(cce_ctx* ctx, cce_stream copy);
 
 /* Fine-grained overlap status (CCE_FLAG_FINE_GRAINED): waits for the work
  * queued on `stream`, then reads and clears the context's device error word,

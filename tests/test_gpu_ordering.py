@@ -196,3 +196,40 @@ def test_failed_call_joins_and_leaves_the_context_usable(ctx, kind, flags):
     finally:
         cce.cce_debug_fail_op(0)
     assert failures >= 2
+
+
+@pytest.mark.parametrize("kind", ["ag", "rs"])
+@pytest.mark.parametrize("flags", [0x0, 0x10])
+def test_caller_copy_stream(kind, flags):
+    """The permute copies run on a stream the caller hands over
+    (cce_ctx_set_copy_stream), with the caller's stream delayed behind a spin
+    so a missing fork would read unwritten inputs; exact results, and exact
+    again after the context's own copy stream is restored."""
+    import collective_overlap_amd as cce
+    print(f"[gpu] ordering: caller copy stream, {kind} flags={flags:#x}", flush=True)
+    c = cce.Context(0)
+    n = 4
+    x_src, y_src, out, ref = (_ag_case if kind == "ag" else _rs_case)(n)
+    x = [torch.zeros_like(t) for t in x_src]
+    y = [torch.zeros_like(t) for t in y_src]
+    copy_stream = torch.cuda.Stream()
+    c.set_copy_stream(copy_stream)
+    sync()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP)
+        for d, s in zip(x + y, x_src + y_src):
+            d.copy_(s)
+        _call(cce, c, kind, x, y, out, flags, stream=side)
+        got = [o.clone() for o in out]
+    side.synchronize()
+    for r in range(n):
+        assert np.array_equal(np64(got[r]), ref[r]), f"caller copy stream, rank {r}"
+    c.set_copy_stream(None)
+    for o in out:
+        o.fill_(float("nan"))
+    _call(cce, c, kind, x, y, out, flags)
+    sync()
+    for r in range(n):
+        assert np.array_equal(np64(out[r]), ref[r]), f"own copy stream, rank {r}"
+    c.close()
