@@ -17,11 +17,19 @@ are multiplied by 1 / (1 - p), dropped ones become 0.  The keep decision
 comes from oracle.philox.keep_mask.
 
 Float64 throughout; the result is rounded to the output dtype only by the
-caller's comparison.
+caller's comparison.  `fused_reduce_epilogue_fp32` evaluates the same
+definition in float32, one IEEE round-to-nearest-even operation per step in
+a fixed order (the reading of the pages this library takes: the sum in
+partial order, then the bias, the scale if kept, the residual; no fused
+multiply-add), so that a kernel that keeps that order can be compared with it
+bit for bit.
 
 Parity pins (tests/test_oracle_epilogue.py): a per-element pure-Python loop on
 small shapes, p = 0 (exactly sum + bias + residual), p = 1 (exactly the
-residual), linearity in the partials, and the N = 1 case.  The step-by-step
+residual), linearity in the partials, and the N = 1 case.  The float32
+evaluation is pinned to the float64 one within the standard error bound of
+n + 3 rounded operations, and by hand-worked cases in which the order of the
+sum, or a fused multiply-add, would change the result.  The step-by-step
 FusedAllReduce (ReduceScatter, epilogue per slice, AllGather) is pinned to the
 whole-tensor epilogue of the AllReduce sum (the collective identity
 AllReduce = ReduceScatter + AllGather, with the pointwise tail commuting with
@@ -92,3 +100,43 @@ def fused_allreduce(partials, bias, residual, p: float, seed: int, offset: int,
         keeps.append(keep_r)
     full = np.concatenate(blocks, axis=0)                  # AllGather
     return [full.copy() for _ in range(n)], np.concatenate(keeps, axis=0)
+
+
+def fused_reduce_epilogue_fp32(partials, bias, residual, p: float, seed: int,
+                               offset: int, row0: int = 0, col0: int = 0,
+                               mask_ld: int | None = None):
+    """The definition above evaluated in float32, step by step:
+
+        s = ((P0 + P1) + ...) + P(n-1);  s = s + bias
+        d = s * c if kept else 0  (c = 1/(1-p) rounded once to float32;
+                                   p = 0: d = s; p >= 1: d = 0)
+        out = d + residual
+
+    every operation rounded to float32 (NumPy float32 arithmetic is IEEE
+    round-to-nearest-even per operation).  Inputs must be exactly
+    representable in float32 (fp32 or bf16 tensors).  Returns (out float32,
+    keep bool); a bf16 output is this value rounded once more
+    (oracle.numerics.bf16_round)."""
+    f = np.float32
+    parts = [np.asarray(x, dtype=np.float64) for x in partials]
+    for x in parts:
+        if not np.array_equal(x.astype(f).astype(np.float64), x, equal_nan=True):
+            raise ValueError("partials must be exactly representable in float32")
+    rows, cols = parts[0].shape
+    s = parts[0].astype(f)
+    for x in parts[1:]:
+        s = (s + x.astype(f)).astype(f)
+    if bias is not None:
+        s = (s + np.asarray(bias, dtype=np.float64).astype(f)[None, :]).astype(f)
+    keep = keep_mask(rows, cols, p, seed, offset, row0, col0,
+                     mask_ld if mask_ld is not None else col0 + cols)
+    if p <= 0.0:
+        d = s
+    elif p >= 1.0:
+        d = np.zeros_like(s)
+    else:
+        c = f(1.0 / (1.0 - p))
+        d = np.where(keep, (s * c).astype(f), f(0.0)).astype(f)
+    if residual is not None:
+        d = (d + np.asarray(residual, dtype=np.float64).astype(f)).astype(f)
+    return d, keep

@@ -1,11 +1,15 @@
 """GPU parity of the fused reduce epilogue: keep masks bit-exact against the
-oracle's Philox, values against the float64 oracle."""
+oracle's Philox, values against the float64 oracle, and bit for bit against
+the oracle's float32 evaluation in the library's fixed order (the sum in
+partial order, + bias, x scale if kept, + residual, one rounding per step, no
+fused multiply-add)."""
 
 import numpy as np
 import pytest
 import torch
 
 from oracle import epilogue as oep
+from oracle import numerics
 import workloads as W
 from gpu_util import np64, assert_bf16_close, assert_f32_close, sync
 
@@ -20,6 +24,20 @@ def ctx():
     yield c
     sync()
     c.close()
+
+
+def assert_bits_fp32_order(out, parts, bias, res, p, seed, off, r0, c0, mld, what):
+    """out (fp32 or bf16 tensor) equals the float32-order oracle bit for bit
+    (bf16: that value rounded to nearest even once more)."""
+    ref32, _ = oep.fused_reduce_epilogue_fp32(
+        [np64(x) for x in parts], None if bias is None else np64(bias),
+        None if res is None else np64(res), p, seed, off, r0, c0, mld)
+    if out.dtype == torch.bfloat16:
+        ref32 = numerics.bf16_round(ref32)
+    got = out.float().cpu().numpy()
+    bad = got.view(np.uint32) != np.ascontiguousarray(ref32).view(np.uint32)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements differ from the float32-order "
+                           f"oracle, first at {np.argwhere(bad)[0].tolist()}")
 
 
 def _mk(shape, k, dtype, ld=None):
@@ -66,6 +84,8 @@ def test_fused_epilogue(ctx, case):
         assert_f32_close(np64(out), ref, "epilogue", tol=1e-6)
     else:
         assert_bf16_close(np64(out), ref, "epilogue")
+    assert_bits_fp32_order(out, parts, bias, res, p, seed, off, r0, c0, mld if mld else c0 + cols,
+                           "epilogue")
     if ld:
         assert torch.isnan(out_full[:, cols:].float()).all()    # padding untouched
 
@@ -78,6 +98,54 @@ def test_no_bias_no_residual(ctx):
     sync()
     ref, _ = oep.fused_reduce_epilogue([np64(x) for x in parts], None, None, 0.25, 5, 6)
     assert_f32_close(np64(out), ref, "no bias/residual", tol=1e-6)
+
+
+@pytest.mark.parametrize("kernel", ["vector", "general"])
+def test_order_and_no_fused_multiply_add(ctx, kernel):
+    """Hand-worked elements on which another order of the sum, or a fused
+    multiply-add, gives a different result (the cases of the oracle's own
+    float32 pins), through the library.  Asking for the mask output selects
+    the general kernel."""
+    import collective_overlap_amd as cce
+    from test_oracle_epilogue import no_fma_case
+    cols = 64
+    mk = (lambda r: {"mask_out": torch.empty((r, cols), device=DEV, dtype=torch.uint8)}
+          if kernel == "general" else {})
+    big = float(2 ** 25)
+    # p = 0, two partials and a bias: (2^25 + -2^25) + 1 = 1 in this order,
+    # 2^25 + (-2^25 + 1) = 0 in the other (-2^25 + 1 rounds to -2^25)
+    parts = [torch.zeros((2, cols), device=DEV) for _ in range(2)]
+    parts[0][0, 0], parts[1][0, 0] = big, -big
+    bias = torch.zeros((cols,), device=DEV)
+    bias[0] = 1.0
+    out = torch.full((2, cols), float("nan"), device=DEV)
+    cce.cce_fused_reduce_epilogue(ctx, parts, bias, None, out, 0.0, 0, 0, **mk(2))
+    sync()
+    assert out[0, 0].item() == 1.0
+    assert_bits_fp32_order(out, parts, bias, None, 0.0, 0, 0, 0, 0, cols, "bias order")
+    # p = 0, three partials (the general kernel takes any call with more than
+    # two): columns 0 and 1 hold the two orders of 2^25, 1, -2^25
+    parts = [torch.zeros((2, cols), device=DEV) for _ in range(3)]
+    for k, v in enumerate((big, 1.0, -big)):
+        parts[k][0, 0] = v
+    for k, v in enumerate((big, -big, 1.0)):
+        parts[k][0, 1] = v
+    out = torch.full((2, cols), float("nan"), device=DEV)
+    cce.cce_fused_reduce_epilogue(ctx, parts, None, None, out, 0.0, 0, 0, **mk(2))
+    sync()
+    assert out[0, 0].item() == 0.0 and out[0, 1].item() == 1.0
+    assert_bits_fp32_order(out, parts, None, None, 0.0, 0, 0, 0, 0, cols, "sum order")
+    # p = 0.1: a kept element whose residual cancels the rounded product
+    e, s_, r, fma = no_fma_case(cols=cols)
+    part = torch.zeros((1, cols), device=DEV)
+    part[0, e] = float(s_)
+    res = torch.zeros((1, cols), device=DEV)
+    res[0, e] = float(r)
+    out = torch.full((1, cols), float("nan"), device=DEV)
+    cce.cce_fused_reduce_epilogue(ctx, [part], None, res, out, 0.1, 0, 0, **mk(1))
+    sync()
+    assert out[0, e].item() == 0.0, f"got {out[0, e].item()!r}; a fused multiply-add gives {fma!r}"
+    assert_bits_fp32_order(out, [part], None, res, 0.1, 0, 0, 0, 0, cols, "no fma")
 
 
 def test_keep_rate_full_size_mask(ctx):
@@ -141,6 +209,8 @@ def test_batched_equals_single_calls_and_oracle(ctx, case):
             assert_f32_close(np64(outs[b]), ref, f"batched {b}", tol=1e-6)
         else:
             assert_bf16_close(np64(outs[b]), ref, f"batched {b}")
+        assert_bits_fp32_order(outs[b], parts[b], bias, res[b], p, seed, off, row0[b], 0, mld,
+                               f"batched {b}")
 
 
 def test_batched_rejects_too_many_operands(ctx):
@@ -234,6 +304,8 @@ def test_vector_kernel_equals_general_kernel(ctx, case):
         assert_f32_close(np64(fast), ref, "vector epilogue", tol=1e-6)
     else:
         assert_bf16_close(np64(fast), ref, "vector epilogue")
+    assert_bits_fp32_order(fast, parts, bias, res, p, 3, 1, r0, c0, mld if mld else c0 + cols,
+                           "vector epilogue")
 
 
 def test_vector_kernel_replicas(ctx):

@@ -58,7 +58,7 @@ def test_grouped_gemm(ctx, M, N, K, G, dt):
     sync()
     for g in range(G):
         ref = oe.local_matmuls([np64(a[g])], [np64(b[g]).T])[0]
-        assert_f32_close(np64(c32[g]), ref, f"group {g} fp32 out", tol=1e-5 if dt == "bf16" else 2e-5)
+        assert_f32_close(np64(c32[g]), ref, f"group {g} fp32 out", tol=1e-5)
         assert_bf16_close(np64(c16[g]), ref, f"group {g} bf16 out")
 
 

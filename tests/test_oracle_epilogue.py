@@ -85,3 +85,83 @@ def test_fused_allreduce_is_epilogue_of_allreduce(n, rows, cols, p):
     assert np.array_equal(keep, wkeep)
     for o in outs:
         assert np.array_equal(o, whole)
+
+
+# ---------------------------------------------------------------------------
+# The float32 evaluation (fused_reduce_epilogue_fp32)
+# ---------------------------------------------------------------------------
+U32 = 2.0 ** -24            # unit roundoff of float32
+
+
+def _gamma(m):
+    return m * U32 / (1 - m * U32)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5])
+def test_fp32_within_rounding_bound_of_fp64(n, p):
+    """n - 1 additions, the bias, the scale (itself rounded once) and the
+    residual: at most n + 3 roundings, so |fp32 - exact| <= gamma_(n+3) *
+    (c (sum |P| + |b|) + |R|) element by element (the standard bound for a
+    chain of rounded operations).  A dropped or doubled term, a wrong sign or
+    a wrong scale breaks it by orders of magnitude."""
+    rng = np.random.default_rng(100 + n)
+    rows, cols = 7, 45
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)
+    parts = [f32(rng.normal(0, 1, (rows, cols))) for _ in range(n)]
+    bias = f32(rng.normal(0, 0.02, cols))
+    res = f32(rng.normal(0, 1, (rows, cols)))
+    got, keep = epilogue.fused_reduce_epilogue_fp32(parts, bias, res, p, 3, 1, 2, 5, 60)
+    ref, keep64 = epilogue.fused_reduce_epilogue(parts, bias, res, p, 3, 1, 2, 5, 60)
+    assert got.dtype == np.float32 and np.array_equal(keep, keep64)
+    c = 1.0 / (1.0 - p)
+    mag = c * (sum(np.abs(x) for x in parts) + np.abs(bias)[None, :]) + np.abs(res)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err <= _gamma(n + 3) * mag)
+    assert err.max() > 0            # the evaluation does round (not float64 in disguise)
+
+
+def test_fp32_p1_is_the_residual_exactly():
+    rng = np.random.default_rng(9)
+    parts = [rng.normal(0, 1, (4, 9)).astype(np.float32) for _ in range(3)]
+    res = rng.normal(0, 1, (4, 9)).astype(np.float32)
+    got, keep = epilogue.fused_reduce_epilogue_fp32(parts, None, res, 1.0, 0, 0)
+    assert not keep.any() and np.array_equal(got, res)
+
+
+def test_fp32_sum_order():
+    """2^25 + 1 is not a float32 (its neighbours are 4 apart), so the order of
+    the partial sum shows: ((2^25 + 1) - 2^25) = 0, but ((2^25 - 2^25) + 1) = 1."""
+    big = float(2 ** 25)
+    a = [np.array([[big]]), np.array([[1.0]]), np.array([[-big]])]
+    b = [np.array([[big]]), np.array([[-big]]), np.array([[1.0]])]
+    assert epilogue.fused_reduce_epilogue_fp32(a, None, None, 0.0, 0, 0)[0][0, 0] == 0.0
+    assert epilogue.fused_reduce_epilogue_fp32(b, None, None, 0.0, 0, 0)[0][0, 0] == 1.0
+    # the float64 definition sees the exact sum in both orders
+    assert epilogue.fused_reduce_epilogue(a, None, None, 0.0, 0, 0)[0][0, 0] == 1.0
+
+
+def no_fma_case(p=0.1, seed=0, offset=0, cols=64):
+    """A kept element e (the first of a row of `cols`) with s = 1.2345678 (as
+    float32) and residual R = -fl32(s * c): rounding the product before the
+    add gives exactly 0, a fused multiply-add gives the product's rounding
+    error.  Returns (e, s, R, fused-multiply-add result)."""
+    keep = philox.keep_mask(1, cols, p, seed, offset, 0, 0, cols)[0]
+    e = int(np.argmax(keep))
+    assert keep[e]
+    s = np.float32(1.2345678)
+    c = np.float32(1.0 / (1.0 - p))
+    prod = np.float32(s * c)
+    fma = float(s) * float(c) - float(prod)       # exact in float64 (24 x 24 bits)
+    return e, s, -prod, fma
+
+
+def test_fp32_no_fused_multiply_add():
+    e, s, r, fma = no_fma_case()
+    assert fma != 0.0                              # the case tells the two apart
+    part = np.zeros((1, 64), dtype=np.float32)
+    part[0, e] = s
+    res = np.zeros((1, 64), dtype=np.float32)
+    res[0, e] = r
+    got, keep = epilogue.fused_reduce_epilogue_fp32([part], None, res, 0.1, 0, 0)
+    assert keep[0, e] and got[0, e] == 0.0
