@@ -219,3 +219,61 @@ def test_gpt3_ffn_n8_full(ctx, flags, batched, in_rs):
         ref, _ = oep.fused_reduce_epilogue([full_row], np64(b), np64(R[sh][i:i + 1]), 0.1, 0, 0,
                                            row0=sh * 1024 + i, col0=0, mask_ld=12288)
         assert_bf16_close(np64(out[sh][i][cols]), ref[0, cols], f"out shard {sh} row {i}")
+
+
+# Whole-tensor equality of the permute forms at full size.  The sampled
+# oracle checks above see a few rows of every shard; a copy or forwarding
+# mistake confined to other rows would pass them, but not these.  The
+# stream, serial and fused forms of one ring direction accumulate every
+# element in the same order, so their outputs agree bit for bit.
+def _forms(cce, bid):
+    return {"stream": bid, "serial": bid | cce.CCE_FLAG_SERIAL,
+            "fused": bid | cce.CCE_FLAG_FUSED_PERMUTE}
+
+
+@pytest.mark.parametrize("bid", [0, 0x10])     # one-way ring; two-way ring
+def test_rs_n8_full_forms_equal(ctx, bid):
+    import collective_overlap_amd as cce
+    print(f"[gpu] rs_n8 full, whole-tensor form equality bid={bid:#x}", flush=True)
+    n = 8
+    X = [W.normal((16384, 2048), 1.0, r, device=DEV) for r in range(n)]
+    Wt = [W.weight_store(2048, 4096, 0.02, 10 + r, device=DEV) for r in range(n)]
+    outs = {}
+    for name, fl in _forms(cce, bid).items():
+        o = [torch.full((2048, 4096), float("nan"), device=DEV) for _ in range(n)]
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", X, Wt, o, flags=fl)
+        outs[name] = o
+    sync()
+    for name in ("serial", "fused"):
+        for r in range(n):
+            assert torch.equal(outs["stream"][r].view(torch.int32), outs[name][r].view(torch.int32)), \
+                f"{name} differs from stream, shard {r}"
+    assert all(bool(torch.isfinite(o).all()) for o in outs["stream"])
+
+
+@pytest.mark.parametrize("bid", [0, 0x10])
+def test_gpt3_ffn_n8_full_forms_equal(ctx, bid):
+    """Both layers: H (AllGather, bf16 with GELU) and the fp32 accumulator
+    (ReduceScatter) over every element of every rank."""
+    import collective_overlap_amd as cce
+    print(f"[gpu] gpt3_ffn_n8 full, whole-tensor form equality bid={bid:#x}", flush=True)
+    n = 8
+    X = [W.normal((1024, 12288), 1.0, s, device=DEV) for s in range(n)]
+    W1 = [W.weight_store(12288, 6144, 0.02, 10 + r, device=DEV) for r in range(n)]
+    W2 = [W.weight_store(6144, 12288, 0.02, 20 + r, device=DEV) for r in range(n)]
+    Hs, accs = {}, {}
+    for name, fl in _forms(cce, bid).items():
+        H = [torch.full((8192, 6144), float("nan"), device=DEV, dtype=BF) for _ in range(n)]
+        acc = [torch.full((1024, 12288), float("nan"), device=DEV) for _ in range(n)]
+        cce.cce_looped_allgather_einsum(ctx, "lhs_rows", X, W1, H, flags=fl | cce.CCE_FLAG_GELU)
+        cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", H, W2, acc, flags=fl)
+        Hs[name], accs[name] = H, acc
+    sync()
+    for name in ("serial", "fused"):
+        for r in range(n):
+            assert torch.equal(Hs["stream"][r].view(torch.int16), Hs[name][r].view(torch.int16)), \
+                f"H: {name} differs from stream, rank {r}"
+            assert torch.equal(accs["stream"][r].view(torch.int32), accs[name][r].view(torch.int32)), \
+                f"acc: {name} differs from stream, rank {r}"
+    assert all(bool(torch.isfinite(h).all()) for h in Hs["stream"])
+    assert all(bool(torch.isfinite(a).all()) for a in accs["stream"])
