@@ -601,9 +601,11 @@ def main(argv=None):
     ap.add_argument("--workload", default="gpt3_ffn_n8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true", help="skip the unoverlapped comparison")
-    ap.add_argument("--permute", choices=("fused", "stream"), default="fused",
+    ap.add_argument("--permute", choices=("fused", "stream", "serial", "dma"), default="fused",
                     help="fused: each partial GEMM sends the data itself; stream: async "
-                         "copies on a second stream ordered by events")
+                         "copies on a second stream ordered by events; serial: the stream "
+                         "form's kernels, every copy on the caller's stream; dma: the stream "
+                         "form with the copies on the SDMA engines")
     ap.add_argument("--transfer", choices=("bidir", "one-way"), default="bidir",
                     help="bidir (default): two-way ring, two partial einsums per iteration, "
                          "ceil(n/2) iterations; one-way: the ring of the loop's pairs only")
@@ -661,7 +663,8 @@ def main(argv=None):
     ctx = cce.Context(0)
     torch.cuda.synchronize()
     bid = cce.CCE_FLAG_BIDIRECTIONAL if a.transfer == "bidir" else 0
-    main_flags = (cce.CCE_FLAG_FUSED_PERMUTE if a.permute == "fused" else 0) | bid
+    main_flags = {"fused": cce.CCE_FLAG_FUSED_PERMUTE, "stream": 0, "serial": cce.CCE_FLAG_SERIAL,
+                  "dma": cce.CCE_FLAG_COPY_DMA}[a.permute] | bid
     if a.fine_grained:
         main_flags |= cce.CCE_FLAG_FINE_GRAINED
     m = measure(step, ctx, a.workload, a.steps, a.warmup, main_flags, bid, a.permute,

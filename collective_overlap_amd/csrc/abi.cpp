@@ -435,6 +435,25 @@ bool use_permute_kernel(hipMemcpyKind kind, bool serial) {
   return kind == hipMemcpyDeviceToDevice && !serial;
 }
 
+// Plan positions of the first and last GEMM op: a copy before the first or
+// after the last has no GEMM beside it.
+struct GemmSpan {
+  size_t first = SIZE_MAX, last = 0;
+  bool alone(const Plan& plan, const Op& o) const {
+    const size_t j = static_cast<size_t>(&o - plan.ops.data());
+    return first == SIZE_MAX || j < first || j > last;
+  }
+};
+GemmSpan gemm_span(const Plan& plan) {
+  GemmSpan g;
+  for (size_t j = 0; j < plan.ops.size(); ++j)
+    if (plan.ops[j].kind == OP_GEMM) {
+      g.first = std::min(g.first, j);
+      g.last = j;
+    }
+  return g;
+}
+
 hipStream_t stream_of(const Op& o, hipStream_t compute, hipStream_t copy, bool serial) {
   return (serial || o.stream == S_COMPUTE) ? compute : copy;
 }
@@ -498,6 +517,7 @@ cce_status joined(cce_ctx* ctx, hipStream_t compute, cce_status st) {
 cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream_t compute) {
   const size_t ein = esize(c.in_t);
   g_ops_seen = 0;
+  const GemmSpan gs = gemm_span(plan);
   for (const Op& o : plan.ops) {
     if (fail_due()) return fail(CCE_EHIP, "injected failure at plan op " + std::to_string(g_ops_seen));
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
@@ -533,7 +553,8 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
         pitems.push_back(pi);
       }
       if (kernel_ok) {
-        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s));
+        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s,
+                                    gs.alone(plan, o)));
       } else {
         for (const PermuteItem& pi : pitems) {
           if (pi.rows == 1)
@@ -798,6 +819,7 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
   if (fine)
     CCE_TRY(launch_zero_words(reinterpret_cast<unsigned*>(c.ws + c.g.sig_off), c.g.sig_words,
                               compute));
+  const GemmSpan gs = gemm_span(plan);
   for (const Op& o : plan.ops) {
     if (fail_due()) return fail(CCE_EHIP, "injected failure at plan op " + std::to_string(g_ops_seen));
     hipStream_t s = stream_of(o, compute, ctx->copy, plan.serial);
@@ -865,7 +887,8 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
         pitems.push_back(pi);
       }
       if (kernel_ok) {
-        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s));
+        CCE_TRY(launch_permute_copy(pitems.data(), static_cast<int>(pitems.size()), s,
+                                    gs.alone(plan, o)));
       } else {
         for (const PermuteItem& pi : pitems)
           HIP_TRY(hipMemcpyAsync(pi.dst, pi.src, pi.width, c.copy_kind, s));

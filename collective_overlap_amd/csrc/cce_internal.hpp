@@ -103,7 +103,9 @@ struct PermuteItem {
   int64_t rows = 0, width = 0, src_pitch = 0, dst_pitch = 0;
 };
 bool permute_item_ok(const PermuteItem& it);
-cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream);
+// `alone`: nothing runs beside this copy (the two-way AllGather's prologue,
+// the ReduceScatter's last permute), so it takes the whole GPU.
+cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream, bool alone);
 
 // Enqueue a kernel that sets n 32-bit words at p to zero (the chunk signal
 // words of a call, cleared by a kernel rather than a memset so that the call

@@ -4,13 +4,12 @@
 // buffer to rank r-1's (and, two-way, r+1's) -- on the copy stream, beside the
 // partial GEMM of the same iteration.
 //
-// The kernel is built to run on the same compute units as that GEMM rather
-// than to take units from it: a workgroup is four waves (one per SIMD) of few
-// registers and no LDS, so it fits beside a GEMM workgroup whose tile leaves
-// registers free, and it needs a small share of a unit's memory path (a
-// permute step moves a few hundred MB over a GEMM launch of 1-2 ms).  Data is
-// read once and written once: 16-byte nontemporal loads and stores, a few in
-// flight per lane.
+// A GEMM workgroup takes a whole compute unit (one wave per SIMD holding
+// 352-512 of each lane's 512 registers), so the copy takes units from the
+// GEMM for as long as its workgroups live: few workgroups (128), each with
+// many bytes in flight (16 waves, four 16-byte loads per lane), no LDS and few
+// registers.  Data is read once and written once, with nontemporal loads and
+// stores.
 //
 // Item layout: `rows` rows of `width` bytes (a multiple of 2), row i at
 // src + i * src_pitch and dst + i * dst_pitch; base pointers and pitches are
@@ -33,7 +32,7 @@ struct PermArgs {
   PermuteItem it[kMaxPermuteItems];
 };
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kUnroll = 4;   // 16-byte loads in flight per lane
 
 // Chunks [c0, c1) of one row (16-byte units), kUnroll loads in flight per
@@ -89,7 +88,7 @@ bool permute_item_ok(const PermuteItem& it) {
                            it.src_pitch >= it.width && it.dst_pitch >= it.width));
 }
 
-cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream) {
+cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream, bool alone) {
   if (n <= 0) return CCE_OK;
   if (n > kMaxPermuteItems) return fail(CCE_EINVAL, "permute copy: too many items");
   PermArgs k{};
@@ -100,14 +99,20 @@ cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream) {
     biggest = items[i].rows * items[i].width > biggest ? items[i].rows * items[i].width : biggest;
   }
   if (biggest == 0) return CCE_OK;
-  // 128 workgroups in all, over the items: the copy shares compute units
-  // with the GEMM beside it and spreads its HBM traffic over the GEMM's
-  // duration.  (One per unit, 256, finished sooner but slowed the GEMM's
-  // accumulate epilogues more; 64 or 32 made the copy outlast the GEMM it
-  // hides behind.  GPT-3 FFN two-way stream form: 18.13 / 18.03 / 18.99 /
-  // 19.55 ms for 256 / 128 / 64 / 32.)
+  // 128 workgroups in all, over the items: the copy shares the GPU with the
+  // GEMM beside it and spreads its HBM traffic over the GEMM's duration.
+  // (256 finished sooner but slowed the GEMM's accumulate epilogues more; 64
+  // or 32 made the copy outlast the GEMM it hides behind.  GPT-3 FFN two-way
+  // stream form, 256-thread workgroups: 18.13 / 18.03 / 18.99 / 19.55 ms for
+  // 256 / 128 / 64 / 32.)  1024-thread workgroups (four waves per SIMD, more
+  // bytes in flight per compute unit) measured 18.09 against 18.22 ms for 256
+  // threads in the same process; many short-lived workgroups of 512 KB or
+  // 2 MB each were slower (18.26 and 18.44 ms; 3.34 and 3.41 against 3.03 ms
+  // on the 8-way fp32 ReduceScatter).
   constexpr int kUnits = 128;
-  int per_item = (kUnits + n - 1) / n;
+  // A copy with nothing beside it takes the whole GPU.
+  constexpr int kAloneUnits = 1024;
+  int per_item = ((alone ? kAloneUnits : kUnits) + n - 1) / n;
   const int64_t chunks = biggest / 16;
   if (per_item > chunks / (kThreads * kUnroll) + 1) per_item = static_cast<int>(chunks / (kThreads * kUnroll) + 1);
   hipLaunchKernelGGL(permute_copy_kernel, dim3(per_item, n), dim3(kThreads), 0,
