@@ -593,6 +593,64 @@ def cpu_info():
     return model, affinity
 
 
+VENDOR_SHAPES = [
+    # name, groups, M, N, K (C = A B^T per group, bf16 operands, bf16 result)
+    ("square_8192", 1, 8192, 8192, 8192),
+    ("gpt3_ffn_layer1_looped", 16, 1024, 6144, 12288),
+    ("gpt3_ffn_layer1_unlooped", 8, 8192, 6144, 12288),
+    ("gpt3_ffn_layer2_looped", 16, 512, 12288, 6144),
+    ("attn_outproj_local", 8, 8192, 8192, 1024),
+]
+
+
+def vendor_gemm(dev, steps, warmup):
+    """The grouped GEMM against the vendor library on the same operands, in
+    one process: hipBLASLt through torch.bmm (right factor passed as a
+    contiguous [K, N] batch) and cce_grouped_gemm (right factor [N, K]), both
+    bf16 in, fp32 accumulation, bf16 out.  Each shape's GEMM time from HIP
+    events around `steps` back-to-back calls.  Both results are compared
+    element by element (they differ only in accumulation order)."""
+    import torch
+    import collective_overlap_amd as cce
+    import workloads as W
+    ctx = cce.Context(0)
+    rows = []
+    for name, g, m, n, k in VENDOR_SHAPES:
+        log(f"vendor gemm {name}: {g} x {m}x{n}x{k}")
+        a = W.normal((g, m, k), 1.0, 1, device=dev)
+        bt = W.normal((g, n, k), 0.02, 2, device=dev)          # [N, K] per group
+        b_kn = bt.transpose(1, 2).contiguous()                  # [K, N] per group
+        ours = torch.empty((g, m, n), device=dev, dtype=torch.bfloat16)
+        lib_out = torch.empty_like(ours)
+        al, bl, cl = list(a.unbind(0)), list(bt.unbind(0)), list(ours.unbind(0))
+
+        def run_ours():
+            cce.cce_grouped_gemm(ctx, al, bl, cl)
+
+        def run_lib():
+            torch.bmm(a, b_kn, out=lib_out)
+        res = {}
+        for tag, fn in (("hipblaslt", run_lib), ("ours", run_ours)):
+            for _ in range(warmup):
+                fn()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+            res[tag] = {"ms": round(ms, 4), "TFLOP/s": round(2.0 * g * m * n * k / (ms * 1e-3) / 1e12, 1)}
+        d = (ours.float() - lib_out.float()).norm() / lib_out.float().norm()
+        rows.append({"shape": name, "groups": g, "M": m, "N": n, "K": k, **res,
+                     "ours_over_hipblaslt": round(res["ours"]["TFLOP/s"] / res["hipblaslt"]["TFLOP/s"], 4),
+                     "rel_fro_diff": float(d)})
+        del a, bt, b_kn, ours, lib_out, al, bl, cl
+        torch.cuda.empty_cache()
+    ctx.close()
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -621,6 +679,9 @@ def main(argv=None):
     ap.add_argument("--fine-grained", action="store_true",
                     help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
                          "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only compare the grouped GEMM with hipBLASLt (torch.bmm) on the "
+                         "headline shapes; prints one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -649,6 +710,10 @@ def main(argv=None):
         dt = (time.perf_counter() - t0) / a.steps
         print(json.dumps({"calibrate_copy_bytes": nb, "read_bytes": nb, "write_bytes": nb,
                           "steps": a.steps, "GB/s": round(2 * nb / dt / 1e9, 1)}), flush=True)
+        return 0
+    if a.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(dev, a.steps, a.warmup),
+                          "peak_TFLOP/s": PEAK_TFLOPS["bf16"]}), flush=True)
         return 0
     log(f"device {torch.cuda.get_device_name(0)}; workload {a.workload}")
     step = WORKLOADS[a.workload](dev)

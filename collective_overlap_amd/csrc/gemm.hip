@@ -1170,6 +1170,16 @@ hipError_t launch_out(const GemmLaunch& L, KArgs& k, hipStream_t s) {
 
 cce_status launch_grouped_gemm(const GemmLaunch& L, void* stream) {
   if (L.groups <= 0 || L.M <= 0 || L.N <= 0) return CCE_OK;
+  // The accumulator input is read in 16-byte vectors (load_cin_quad and the
+  // staged path): every cin must be 16-byte aligned with ldcin % 4 == 0.
+  // The plans only pass workspace accumulators, which are; anything else is a
+  // planning error, caught here before a launch.
+  if (L.epi == EPI_ACCUM || L.epi == EPI_FINAL) {
+    if (L.ldcin % 4 != 0) return fail(CCE_EINVAL, "gemm launch: accumulator input ld % 4 != 0");
+    for (int g = 0; g < L.groups; ++g)
+      if (reinterpret_cast<uintptr_t>(L.p.cin[g]) & 15)
+        return fail(CCE_EINVAL, "gemm launch: accumulator input not 16-byte aligned");
+  }
   KArgs k{};
   k.groups = L.groups;
   k.M = static_cast<int>(L.M);

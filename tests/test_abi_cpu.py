@@ -455,3 +455,23 @@ def test_overlap_enabling_rule_properties(cce):
 ])
 def test_overlap_candidate_choice(cce, comp, c0, s0, c1, s1, want):
     assert cce.cce_overlap_choose(comp, c0, s0, c1, s1) == want
+
+
+# ---------------------------------------------------------------------------
+# The build's spill guard (collective_overlap_amd/build.py)
+# ---------------------------------------------------------------------------
+def test_spill_guard_reads_the_compiler_remarks():
+    from collective_overlap_amd import build
+    remarks = "\n".join([
+        "x.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    sc = build.scratch_by_kernel(remarks)
+    assert sc == {"kern_a": 0, "kern_b": 12}
+    assert build.check_spills(sc, known={}) == ["kern_b: 12 bytes/lane (allowed 0)"]
+    assert build.check_spills(sc, known={"kern_b": 12}) == []
+    assert build.check_spills(sc, known={"kern_b": 8}) == ["kern_b: 12 bytes/lane (allowed 8)"]
+
