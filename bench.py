@@ -651,6 +651,62 @@ def vendor_gemm(dev, steps, warmup):
     return rows
 
 
+def epilogue_ceiling(dev, steps, warmup):
+    """The fused epilogue's kernels on the benchmark shapes, each in two
+    forms: the full epilogue (bias, dropout p = 0.1, residual) and the same
+    partials with p = 0 and no bias or residual, which leaves the kernel
+    moving data with one add per partial.  The ratio of the two rates is the
+    cost of the epilogue's arithmetic; the second rate is what the kernel's
+    access pattern reaches on this GPU."""
+    import torch
+    import collective_overlap_amd as cce
+    import workloads as W
+    ctx = cce.Context(0)
+    rows = []
+    shapes = [
+        # name, partials, rows, cols, partial dtype, batch (ranks)
+        ("attn_outproj_n8: 8 bf16 partials [8192, 8192]", 8, 8192, 8192, torch.bfloat16, 1),
+        ("gpt3_ffn_n8: 2 fp32 accumulators [1024, 12288] x 8 ranks", 2, 1024, 12288, torch.float32, 8),
+        ("gpt3_ffn_n8 one-way: 1 fp32 accumulator [1024, 12288] x 8 ranks", 1, 1024, 12288,
+         torch.float32, 8),
+    ]
+    for name, n, r, c, pdt, nb in shapes:
+        log(f"epilogue ceiling {name}")
+        parts = [[W.normal((r, c), 1.0, 300 + 10 * b + k, device=dev, dtype=pdt) for k in range(n)]
+                 for b in range(nb)]
+        bias = W.normal((c,), 0.02, 90, device=dev)
+        res = [W.normal((r, c), 1.0, 91 + b, device=dev) for b in range(nb)]
+        out = [torch.empty((r, c), device=dev, dtype=torch.bfloat16) for _ in range(nb)]
+        row0 = [b * r for b in range(nb)]
+        esz = torch.tensor([], dtype=pdt).element_size()
+        full_bytes = nb * r * c * (n * esz + 2 + 2) + c * 2
+        bare_bytes = nb * r * c * (n * esz + 2)
+        res_ = {}
+        for tag, fn in (
+                ("full", lambda: cce.cce_fused_reduce_epilogue_batched(
+                    ctx, parts, bias, res, out, 0.1, 0, 0, mask_row0=row0, mask_col0=0, mask_ld=c)),
+                ("data_only", lambda: cce.cce_fused_reduce_epilogue_batched(
+                    ctx, parts, None, None, out, 0.0, 0, 0, mask_row0=row0, mask_col0=0, mask_ld=c))):
+            for _ in range(warmup):
+                fn()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+            nbytes = full_bytes if tag == "full" else bare_bytes
+            res_[tag] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        rows.append({"shape": name, **res_,
+                     "full_over_data_only_rate": round(res_["full"]["GB/s"] / res_["data_only"]["GB/s"], 4)})
+        del parts, res, out
+        torch.cuda.empty_cache()
+    ctx.close()
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -682,6 +738,9 @@ def main(argv=None):
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only compare the grouped GEMM with hipBLASLt (torch.bmm) on the "
                          "headline shapes; prints one JSON line")
+    ap.add_argument("--epilogue-ceiling", action="store_true",
+                    help="only time the fused epilogue's kernels on the benchmark shapes, full "
+                         "and reduced to moving data; prints one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run `steps` plain device copies of MiB mebibytes (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -710,6 +769,10 @@ def main(argv=None):
         dt = (time.perf_counter() - t0) / a.steps
         print(json.dumps({"calibrate_copy_bytes": nb, "read_bytes": nb, "write_bytes": nb,
                           "steps": a.steps, "GB/s": round(2 * nb / dt / 1e9, 1)}), flush=True)
+        return 0
+    if a.epilogue_ceiling:
+        print(json.dumps({"epilogue_ceiling": epilogue_ceiling(dev, a.steps, a.warmup),
+                          "hbm_peak_GB/s": PEAK_HBM_GBS}), flush=True)
         return 0
     if a.vendor_gemm:
         print(json.dumps({"vendor_gemm": vendor_gemm(dev, a.steps, a.warmup),
