@@ -431,8 +431,12 @@ hipMemcpyKind copy_kind(uint32_t flags) {
 // shares compute units with the GEMM beside it; the DMA form keeps the DMA
 // engines, and the serial form (the unoverlapped comparison) the runtime's
 // full-device copy.
-bool use_permute_kernel(hipMemcpyKind kind, bool serial) {
-  return kind == hipMemcpyDeviceToDevice && !serial;
+// The copy kernel moves device-to-device permutes, except in the serial form
+// (CCE_FLAG_SERIAL), which keeps the runtime's own copies as the baseline the
+// overlapped forms are measured against.  A fused plan's few copies (the
+// two-way AllGather's prologue) take the kernel too.
+bool use_permute_kernel(hipMemcpyKind kind, const Plan& plan) {
+  return kind == hipMemcpyDeviceToDevice && (!plan.serial || plan.fused);
 }
 
 // Plan positions of the first and last GEMM op: a copy before the first or
@@ -533,7 +537,7 @@ cce_status ag_execute(cce_ctx* ctx, const AgCall& c, const Plan& plan, hipStream
       // The shard's exact span (contiguous when both sides share the ld): no
       // read of the caller's memory past its last row.
       std::vector<PermuteItem> pitems;
-      bool kernel_ok = use_permute_kernel(c.copy_kind, plan.serial);
+      bool kernel_ok = use_permute_kernel(c.copy_kind, plan);
       for (const Item& it : o.items) {
         const PtrLd src = ag_resolve(c, it.a), dst = ag_resolve(c, it.c);
         if (c.lshape.rows == 0 || w == 0) continue;
@@ -875,7 +879,7 @@ cce_status rs_execute(cce_ctx* ctx, const RsCall& c, const Plan& plan, hipStream
       int slot;
       CCE_TRY(prof_begin(ctx, s, 1, o.iter, 0.0, 2.0 * bytes * o.items.size(), &slot));
       std::vector<PermuteItem> pitems;
-      bool kernel_ok = use_permute_kernel(c.copy_kind, plan.serial);
+      bool kernel_ok = use_permute_kernel(c.copy_kind, plan);
       for (const Item& it : o.items) {
         const PtrLd src = rs_resolve(c, it.a), dst = rs_resolve(c, it.c);
         PermuteItem pi;
