@@ -93,9 +93,9 @@ struct GemmLaunch {
 
 // Ring-permute copy (permute.hip): `rows` rows of `width` bytes, row i at
 // src + i * src_pitch -> dst + i * dst_pitch.  One launch copies every item
-// of a permute step on the copy stream.  permute_item_ok: base pointers and
-// pitches 16-byte aligned, width even (else the caller uses the runtime's
-// copy).
+// of a permute step on the copy stream.  permute_item_ok: the kernel takes
+// single spans (rows == 1) of a multiple of 16 bytes at 16-byte aligned
+// pointers; the caller gives anything else to the runtime's copy.
 constexpr int kMaxPermuteItems = kMaxGroups;
 struct PermuteItem {
   const void* src = nullptr;

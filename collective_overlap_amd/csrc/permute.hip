@@ -11,10 +11,10 @@
 // registers.  Data is read once and written once, with nontemporal loads and
 // stores.
 //
-// Item layout: `rows` rows of `width` bytes (a multiple of 2), row i at
-// src + i * src_pitch and dst + i * dst_pitch; base pointers and pitches are
-// 16-byte aligned.  A row's last width % 16 bytes are copied 2 bytes at a
-// time, so nothing past the row's last element is read or written.
+// Item layout: one contiguous span of `width` bytes (a multiple of 16) at
+// 16-byte aligned src and dst.  Every permute the plans make is one: a
+// looped shard and its receive buffer share a row stride, and accumulators
+// are whole buffers.  Anything else goes to the runtime's copy.
 
 #include <hip/hip_runtime.h>
 
@@ -52,40 +52,19 @@ __device__ __forceinline__ void copy_chunks(const u32x4* __restrict__ src, u32x4
 
 __global__ __launch_bounds__(kThreads) void permute_copy_kernel(PermArgs a) {
   const PermuteItem& it = a.it[blockIdx.y];
-  const int64_t cpr = it.width >> 4;                    // whole 16-byte chunks per row
-  const char* src = static_cast<const char*>(it.src);
-  char* dst = static_cast<char*>(it.dst);
-  if (it.rows == 1) {
-    // one contiguous span, split evenly over the item's workgroups
-    const int64_t per = (cpr + gridDim.x - 1) / gridDim.x;
-    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * per;
-    const int64_t c1 = c0 + per < cpr ? c0 + per : cpr;
-    copy_chunks(reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), c0, c1);
-  } else {
-    // pitched rows, dealt to the item's workgroups
-    for (int64_t r = blockIdx.x; r < it.rows; r += gridDim.x)
-      copy_chunks(reinterpret_cast<const u32x4*>(src + r * it.src_pitch),
-                  reinterpret_cast<u32x4*>(dst + r * it.dst_pitch), 0, cpr);
-  }
-  // Row tails (width % 16 bytes), two bytes at a time, by the first
-  // workgroup of the item.
-  const int64_t half = (it.width & 15) >> 1;
-  if (half && blockIdx.x == 0) {
-    for (int64_t i = threadIdx.x; i < it.rows * half; i += kThreads) {
-      const int64_t r = i / half, off = cpr * 16 + 2 * (i - r * half);
-      *reinterpret_cast<uint16_t*>(dst + r * it.dst_pitch + off) =
-          *reinterpret_cast<const uint16_t*>(src + r * it.src_pitch + off);
-    }
-  }
+  const int64_t chunks = it.width >> 4;
+  // the span split evenly over the item's workgroups
+  const int64_t per = (chunks + gridDim.x - 1) / gridDim.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t c1 = c0 + per < chunks ? c0 + per : chunks;
+  copy_chunks(static_cast<const u32x4*>(it.src), static_cast<u32x4*>(it.dst), c0, c1);
 }
 
 }  // namespace
 
 bool permute_item_ok(const PermuteItem& it) {
   const auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  return al(it.src) && al(it.dst) && it.rows >= 0 && it.width >= 0 && (it.width & 1) == 0 &&
-         (it.rows <= 1 || ((it.src_pitch & 15) == 0 && (it.dst_pitch & 15) == 0 &&
-                           it.src_pitch >= it.width && it.dst_pitch >= it.width));
+  return al(it.src) && al(it.dst) && it.rows == 1 && it.width >= 0 && (it.width & 15) == 0;
 }
 
 cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream, bool alone) {
@@ -96,7 +75,7 @@ cce_status launch_permute_copy(const PermuteItem* items, int n, void* stream, bo
   int64_t biggest = 0;
   for (int i = 0; i < n; ++i) {
     k.it[i] = items[i];
-    biggest = items[i].rows * items[i].width > biggest ? items[i].rows * items[i].width : biggest;
+    biggest = items[i].width > biggest ? items[i].width : biggest;
   }
   if (biggest == 0) return CCE_OK;
   // 128 workgroups in all, over the items: the copy shares the GPU with the
