@@ -473,3 +473,35 @@ def test_empty_extents_are_noops(ctx):
     parts = [torch.zeros((0, 16), device=DEV)]
     cce.cce_fused_reduce_epilogue(ctx, parts, None, None, torch.zeros((0, 16), device=DEV), 0.1)
     sync()
+
+
+# ---------------------------------------------------------------------------
+# The largest operand the ABI takes (2^30 - 256 bytes)
+# ---------------------------------------------------------------------------
+def test_largest_operand_bit_exact_and_one_row_more_rejected(ctx):
+    """A bf16 left factor of 65535 x 8192 (2^30 - 16384 bytes, the most whole
+    rows of that width under the 2^30 - 256 byte limit): integer probes,
+    bit-exact on the first and last tile rows, the ragged last tile
+    included.  One row more (2^30 bytes) is rejected before anything is
+    enqueued."""
+    import collective_overlap_amd as cce
+    from collective_overlap_amd._lib import CceError
+    M, N, K = 65535, 256, 8192
+    print(f"[gpu] largest operand M={M} N={N} K={K}", flush=True)
+    big = W.int_probe((M + 1, K), 60, device=DEV, dtype=torch.bfloat16)
+    a = big[:M]
+    b = W.int_probe((N, K), 61, device=DEV, dtype=torch.bfloat16)
+    assert a.numel() * 2 == (1 << 30) - 16384
+    c = torch.full((M, N), float("nan"), device=DEV)
+    cce.cce_grouped_gemm(ctx, [a], [b], [c])
+    sync()
+    rows = [0, 1, 255, 256, 65279, 65280, 65533, 65534]
+    ref = np64(a[rows]) @ np64(b).T
+    assert np.array_equal(np64(c[rows]), ref)
+    assert not torch.isnan(c).any()
+    c2 = torch.full((M + 1, N), float("nan"), device=DEV)
+    with pytest.raises(CceError) as e:
+        cce.cce_grouped_gemm(ctx, [big], [b], [c2])
+    assert e.value.status == 2 and "1 GiB" in str(e.value)
+    sync()
+    assert torch.isnan(c2).all()
