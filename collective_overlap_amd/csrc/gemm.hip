@@ -350,8 +350,15 @@ __device__ __forceinline__ const float* uniform_ptr(const float* p) {
   return reinterpret_cast<const float*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-__device__ __forceinline__ int claim_chunk(const KArgs& a, int g, int slot, const float** other) {
-  __shared__ int s_role, s_ok;
+// `sh`: two ints of the workgroup's LDS for the role and the wait's result.
+// (They live in the kernel's one LDS array: a second LDS object makes the
+// compiler wait for every global->LDS load of the k loop before the next LDS
+// access, since it can no longer tell the loads' target apart from other
+// LDS accesses -- which serialised the whole k loop.)
+__device__ __forceinline__ int claim_chunk(const KArgs& a, int g, int slot, const float** other,
+                                           int* sh) {
+  int& s_role = sh[0];
+  int& s_ok = sh[1];
   const int part = a.fin.partner[g];
   if (part < 0) {
     *other = a.fin.other[a.fin.oid[g]];
@@ -517,7 +524,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
   static_assert((NS - 1) * N_DMA < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
+  // (EPI_FINAL: 16 more bytes for the chunk claim's role and wait result)
+  constexpr int kClaimBytes = (EPI == EPI_FINAL) ? 16 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE + kClaimBytes];
 
   int g, tm, tn;
   map_tile(a, g, tm, tn);
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
     const float* pw = nullptr;
     if constexpr (FIN) {
       slot = a.fin.oid[g] * a.tiles_per_group + tm * a.tiles_n + tn;
-      role = claim_chunk(a, g, slot, &pw);
+      role = claim_chunk(a, g, slot, &pw, reinterpret_cast<int*>(smem + NS * STAGE));
       if (role < 0) return;
     }
     // every wave's last fragment reads are done before LDS is overwritten
@@ -1064,7 +1073,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
     static_assert(!GELU, "EPI_FINAL has no GELU");
     const int slot = a.fin.oid[g] * a.tiles_per_group + tm * a.tiles_n + tn;
     const float* pw = nullptr;
-    const int role = claim_chunk(a, g, slot, &pw);
+    __shared__ int claim_sh[2];
+    const int role = claim_chunk(a, g, slot, &pw, claim_sh);
     if (role < 0) return;
     const int oid = a.fin.oid[g];
     const float* cin = a.p.cin[g];
