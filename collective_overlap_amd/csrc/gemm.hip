@@ -915,9 +915,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         // this pass's input chunks, in flight while the pass is staged (a
         // consumer tile of an EPI_FINAL launch loads them batch by batch)
         if ((p > 0 || !pf) && !(FIN && (role != 1 || cin == nullptr))) {
+          if (pf) {
+            // whole, aligned tile: no per-lane edge branches between the loads
 #pragma unroll
-          for (int it = 0; it < EIT; ++it)
-            cinv[it] = load_cin_quad(a, cin, m0 + erow(p, it) + e_r, n0 + EPC * e_c);
+            for (int it = 0; it < EIT; ++it)
+              cinv[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+                  cin + static_cast<int64_t>(m0 + erow(p, it) + e_r) * a.ldcin + n0 + EPC * e_c));
+          } else {
+#pragma unroll
+            for (int it = 0; it < EIT; ++it)
+              cinv[it] = load_cin_quad(a, cin, m0 + erow(p, it) + e_r, n0 + EPC * e_c);
+          }
         }
       }
 #pragma unroll
