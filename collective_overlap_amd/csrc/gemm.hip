@@ -1000,6 +1000,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
         }
         continue;
       }
+      if (whole && vec) {
+        // Whole tile, 16-byte rows: straight-line code.  (A per-lane branch
+        // between the stores -- vector or element by element -- leaves the
+        // compiler unsure how many stores are in flight at the next use of a
+        // loaded input, and it then waits for all of them: one full drain
+        // per chunk.)
+#pragma unroll
+        for (int it = 0; it < EIT; ++it) {
+          const int lr = ERI * it + e_r;
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(smem + lr * ERB + ((e_c ^ (lr & ESW)) << 4));
+          const int m = m0 + erow(p, it) + e_r;
+          const int n = n0 + EPC * e_c;
+          TS* dst = reinterpret_cast<TS*>(cbase) + static_cast<int64_t>(m) * a.ldc + n;
+          if constexpr (ACS) {
+            const f32x4 v = cinv[it] + __builtin_bit_cast(f32x4, raw);
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+          } else {
+            __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(dst));
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int it = 0; it < EIT; ++it) {
         const int lr = ERI * it + e_r;
