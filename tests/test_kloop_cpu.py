@@ -56,3 +56,40 @@ def test_every_bf16_kernel_waits_once_per_k_tile(gemm_asm):
             assert full_waits == 1, f"{name}: {full_waits} full vmcnt waits for {loads} loads"
             checked += 1
     assert checked >= 16
+
+
+def _longest_store_run(text):
+    """The longest stretch of the kernel's code without a branch or label
+    that holds 16-byte global stores: (number of stores, the lines)."""
+    lines = [l.split(";")[0].strip() for l in text.splitlines()
+             if l.strip() and not l.strip().startswith(";")]
+    best, cur = (0, []), []
+    for l in lines + [".LBB_end:"]:
+        if l.startswith("s_cbranch") or l.startswith("s_branch") or l.startswith(".LBB"):
+            n = sum("global_store_dwordx4" in x for x in cur)
+            if n > best[0]:
+                best = (n, cur)
+            cur = []
+        else:
+            cur.append(l)
+    return best
+
+
+@pytest.mark.parametrize("variant", [
+    "ILi256ELi256ELi2ELi2ELi64ELi2EfLi1ELb0E",       # fp32 accumulate (ReduceScatter)
+    "ILi256ELi256ELi2ELi2ELi64ELi2EfLi0ELb0E",       # fp32 store
+    "ILi256ELi256ELi2ELi2ELi64ELi2EDF16bLi0ELb1E",   # bf16 store + GELU (AllGather)
+])
+def test_whole_tile_stores_are_not_drained_one_by_one(gemm_asm, variant):
+    """The staged epilogue of a whole tile stores its 32 chunks of a pass in
+    one straight run, and waits for the memory counter there at most once
+    (for the accumulator input): a per-chunk drain of the stores had cost
+    the ReduceScatter's accumulate launches 3%."""
+    name = "_ZN3cce12_GLOBAL__N_116gemm_bf16_kernel" + variant + "EEvNS0_5KArgsE"
+    i = gemm_asm.index(name + ":")
+    body = gemm_asm[i:gemm_asm.index(".Lfunc_end", i)]
+    n, run = _longest_store_run(body)
+    assert n >= 32, f"{variant}: longest straight run of stores {n}"
+    first = next(k for k, l in enumerate(run) if "global_store_dwordx4" in l)
+    drains = [l for l in run[first:] if re.match(r"s_waitcnt vmcnt\(0\)", l)]
+    assert drains == [], f"{variant}: {len(drains)} full waits between the stores"
