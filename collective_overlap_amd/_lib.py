@@ -21,6 +21,7 @@ CCE_FLAG_COPY_DMA = 0x4
 CCE_FLAG_FUSED_PERMUTE = 0x8
 CCE_FLAG_BIDIRECTIONAL = 0x10
 CCE_FLAG_FINE_GRAINED = 0x20
+CCE_FLAG_ONE_CHAIN = 0x40
 CCE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 AG_MODES = {"lhs_rows": 0, "rhs_cols": 1, "lhs_cols": 2, "rhs_rows": 3, "lhs_batch": 4}

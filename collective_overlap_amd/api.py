@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import (CCE_BF16, CCE_F32, CCE_FLAG_BIDIRECTIONAL, CCE_FLAG_COPY_DMA,
                    CCE_FLAG_FINE_GRAINED, CCE_FLAG_FUSED_PERMUTE, CCE_FLAG_GELU,
-                   CCE_FLAG_SERIAL,
+                   CCE_FLAG_ONE_CHAIN, CCE_FLAG_SERIAL,
                    AG_MODES, RS_MODES,
                    cce_mat, check, lib, ptr_array)
 
@@ -31,7 +31,7 @@ __all__ = [
     "cce_fused_allreduce_epilogue", "cce_describe_plan", "cce_debug_fail_op",
     "cce_debug_signal_giveup", "cce_version",
     "CCE_FLAG_SERIAL", "CCE_FLAG_GELU", "CCE_FLAG_COPY_DMA", "CCE_FLAG_FUSED_PERMUTE",
-    "CCE_FLAG_BIDIRECTIONAL", "CCE_FLAG_FINE_GRAINED",
+    "CCE_FLAG_BIDIRECTIONAL", "CCE_FLAG_FINE_GRAINED", "CCE_FLAG_ONE_CHAIN",
     "AG_MODES", "RS_MODES",
 ]
 

@@ -347,7 +347,7 @@ struct RsGeom {
 };
 
 cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsGeom& g,
-                       bool fused = false) {
+                       bool one_chain = false) {
   if (n < 1 || n > CCE_MAX_RANKS)
     return fail(n < 1 ? CCE_EINVAL : CCE_EUNSUPPORTED, "n_ranks out of range: " + std::to_string(n));
   if (mode != CCE_RS_SLICE_LHS_ROWS && mode != CCE_RS_SLICE_RHS_COLS)
@@ -376,7 +376,7 @@ cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsG
     *slot = rows ? align256(h0 * *ld * 4) : align256(g.other * *ld * 4);
   };
   // Two chains of half shards (copies beside the GEMMs), or one chain of
-  // whole shards (permute fused into the GEMM epilogue).
+  // whole shards (permute fused into the GEMM epilogue, or CCE_FLAG_ONE_CHAIN).
   int64_t s0, s1, ld2, slot2, ld1, slot1;
   split(&s0, &s1);
   layout(s0, &ld2, &slot2);
@@ -393,7 +393,7 @@ cce_status rs_geometry(int n, int mode, cce_dtype acc_t, const cce_mat& out, RsG
   g.sig_tiles = ((g.shard + 63) / 64) * ((g.other + 63) / 64);
   g.sig_words = (n > 1) ? 2LL * n * g.sig_tiles : 0;
   g.total += align256(4 * g.sig_words);
-  if (fused) {
+  if (one_chain) {
     g.h0 = g.shard;
     g.h1 = 0;
     g.H = 1;
@@ -1159,7 +1159,7 @@ cce_status cce_looped_allgather_einsum(cce_ctx* ctx, int n_ranks, cce_ag_mode mo
   clear_error();
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
-                CCE_FLAG_BIDIRECTIONAL))
+                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_ONE_CHAIN))
     return fail(CCE_EINVAL, "unknown flags");
   if (!looped || !local || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   AgGeom g;
@@ -1235,9 +1235,10 @@ static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype
                           const RsEpiArgs* ea) {
   if (!ctx) return fail(CCE_EINVAL, "ctx is NULL");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
-                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED))
+                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED | CCE_FLAG_ONE_CHAIN))
     return fail(CCE_EINVAL, "unsupported flags for ReduceScatter");
   const bool fused = (flags & CCE_FLAG_FUSED_PERMUTE) != 0;
+  const bool one_chain = fused || (flags & CCE_FLAG_ONE_CHAIN) != 0;
   const bool bidir = (flags & CCE_FLAG_BIDIRECTIONAL) != 0;
   const bool fine = (flags & CCE_FLAG_FINE_GRAINED) != 0;
   if (fine && bidir && !fused)
@@ -1249,7 +1250,7 @@ static cce_status rs_impl(cce_ctx* ctx, int n_ranks, cce_rs_mode mode, cce_dtype
   if (!a || !b || !out) return fail(CCE_EINVAL, "pointer array is NULL");
   if (!dtype_ok(in_t) || !dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   RsGeom g;
-  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g, fused));
+  CCE_TRY(rs_geometry(n_ranks, mode, acc_t, out_shard, g, one_chain));
   // (the chunk consumers address a published partial by 32-bit offsets)
   if (fine && g.half_bytes > kMaxOperandBytes)
     return fail(CCE_EUNSUPPORTED, "CCE_FLAG_FINE_GRAINED: an accumulator exceeds 1 GiB");
@@ -1646,7 +1647,7 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
   if (n_ranks < 1 || n_ranks > CCE_MAX_RANKS) return fail(CCE_EINVAL, "n_ranks out of range");
   if (!dtype_ok(out_t)) return fail(CCE_EINVAL, "bad dtype");
   if (flags & ~(CCE_FLAG_SERIAL | CCE_FLAG_GELU | CCE_FLAG_COPY_DMA | CCE_FLAG_FUSED_PERMUTE |
-                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED))
+                CCE_FLAG_BIDIRECTIONAL | CCE_FLAG_FINE_GRAINED | CCE_FLAG_ONE_CHAIN))
     return fail(CCE_EINVAL, "unknown flags");
   if (kind == 0 && (flags & CCE_FLAG_FINE_GRAINED))
     return fail(CCE_EINVAL, "CCE_FLAG_FINE_GRAINED applies to the ReduceScatter");
@@ -1669,8 +1670,9 @@ cce_status cce_describe_plan(int kind, int n_ranks, int mode, cce_dtype out_t, u
     if ((flags & CCE_FLAG_FINE_GRAINED) && bidir && !fused)
       return fail(CCE_EUNSUPPORTED, "CCE_FLAG_FINE_GRAINED with CCE_FLAG_BIDIRECTIONAL needs "
                                     "CCE_FLAG_FUSED_PERMUTE");
-    p = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, true, serial, fused)
-              : build_reducescatter_plan(n_ranks, mode, true, serial, fused);
+    const bool halves = (flags & CCE_FLAG_ONE_CHAIN) == 0;
+    p = bidir ? build_reducescatter_plan_bidir(n_ranks, mode, halves, serial, fused)
+              : build_reducescatter_plan(n_ranks, mode, halves, serial, fused);
     if (flags & CCE_FLAG_FINE_GRAINED) make_fine_grained(p, kind == 2);
   } else {
     return fail(CCE_EINVAL, "kind must be 0, 1 or 2");

@@ -133,6 +133,18 @@ typedef void* cce_stream;          /* a hipStream_t; NULL = the null stream */
                                   already running) gives up, leaves its chunk
                                   unwritten and counts the event for
                                   cce_ctx_check_signals. */
+#define CCE_FLAG_ONE_CHAIN 0x40u /* ReduceScatter with copies (stream, serial
+                                  or DMA form): keep each shard's accumulator
+                                  whole, one chain of n launches, instead of
+                                  the default two chains of half shards whose
+                                  copies overlap the other chain's GEMM.  The
+                                  fused permute always runs one chain.  With a
+                                  copy stream each copy then waits for its own
+                                  GEMM, so the flag is for the serial form: the
+                                  unoverlapped comparison with the same GEMMs
+                                  as the fused form.  Same results, bit for
+                                  bit.  The AllGather entry point accepts it
+                                  and is unchanged (its loop is one chain). */
 
 /* Status text; never NULL. */
 const char* cce_status_string(cce_status s);

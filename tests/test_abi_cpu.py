@@ -150,6 +150,48 @@ def test_reducescatter_half_copies_overlap_other_chain(n):
         assert plan_check.concurrent(text, _is("copy", i, 1), _is("gemm", i + 1, 0))
 
 
+ONE_CHAIN = 0x40
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("flags", [ONE_CHAIN, ONE_CHAIN | 1, ONE_CHAIN | 0x10, ONE_CHAIN | 0x11])
+def test_reducescatter_one_chain_plan_race_free(n, mode, flags):
+    text = _plan(1, n, mode, 0, flags)
+    assert plan_check.check(text) == []
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("flags", [ONE_CHAIN, ONE_CHAIN | 1])
+def test_reducescatter_one_chain_plan_matches_simulated_loop(n, flags):
+    """CCE_FLAG_ONE_CHAIN: one whole-shard chain, n GEMM launches and n - 1
+    permutes, each GEMM on the ring's schedule."""
+    ops = plan_check.parse(_plan(1, n, 0, 0, flags))
+    a = [np.zeros((n, 1)) for _ in range(n)]
+    b = [np.zeros((1, 1)) for _ in range(n)]
+    _, sched, _ = ring.simulate_einsum_reducescatter("slice_lhs_rows", a, b)
+    gemms = [o for o in ops if o.kind == "gemm"]
+    assert len(gemms) == n
+    assert {int(o.attrs["h"]) for o in gemms} == {0}
+    for o in gemms:
+        i = int(o.attrs["it"])
+        assert _shards(o) == {r: sched[i][r] for r in range(n)}
+    assert len([o for o in ops if o.kind == "copy"]) == n - 1
+
+
+def test_one_chain_leaves_the_fused_and_allgather_plans_alone():
+    for kind, mode, fl in ((0, 0, 0), (0, 1, 1), (0, 0, 0x8), (1, 0, 0x8), (1, 1, 0x18)):
+        assert _plan(kind, 4, mode, 1, fl | ONE_CHAIN) == _plan(kind, 4, mode, 1, fl)
+
+
+def test_header_flags_match_the_binding():
+    from collective_overlap_amd import _lib
+    defs = dict(re.findall(r"#define (CCE_FLAG_[A-Z_]+) (0x[0-9a-f]+)u", open(HEADER).read()))
+    assert len(defs) >= 7
+    for name, val in defs.items():
+        assert getattr(_lib, name) == int(val, 16), name
+
+
 def test_serial_plan_has_no_copy_stream():
     for kind, mode in ((0, 0), (1, 0)):
         assert all(o.stream == "compute" for o in plan_check.parse(_plan(kind, 4, mode, 1, 1)))

@@ -45,6 +45,8 @@ def _flags(cce, form):
         f |= cce.CCE_FLAG_BIDIRECTIONAL
     if "serial" in form:
         f |= cce.CCE_FLAG_SERIAL
+    if "one-chain" in form:
+        f |= cce.CCE_FLAG_ONE_CHAIN
     return f
 
 
@@ -52,7 +54,8 @@ def _ints(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-EPI_FORMS = ["two-way fused", "one-way fused", "one-way stream", "one-way serial"]
+EPI_FORMS = ["two-way fused", "one-way fused", "one-way stream", "one-way serial",
+             "one-way serial one-chain"]
 EPI_CASES = [
     # mode, (shard, K, other), n, out, p, bias, residual
     ("slice_lhs_rows", (72, 256, 264), 4, "bf16", 0.1, True, True),     # pairs, ragged tiles

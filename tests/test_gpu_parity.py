@@ -289,6 +289,13 @@ def test_einsum_reducescatter(ctx, mode, dims, n, out_dt):
     cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out)
     out_s = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
     cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out_s, flags=cce.CCE_FLAG_SERIAL)
+    # one whole-shard chain instead of two half-shard chains, with copies
+    # beside the GEMMs and serialised
+    one = cce.CCE_FLAG_ONE_CHAIN
+    out_1 = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out_1, flags=one)
+    out_1s = [torch.full(oshape, float("nan"), device=DEV, dtype=odt) for _ in range(n)]
+    cce.cce_looped_einsum_reducescatter(ctx, mode, a, b, out_1s, flags=one | cce.CCE_FLAG_SERIAL)
     sync()
     ref = oe.einsum_reducescatter(mode, oa, ob)
     for r in range(n):
@@ -297,6 +304,8 @@ def test_einsum_reducescatter(ctx, mode, dims, n, out_dt):
         else:
             assert_f32_close(np64(out[r]), ref[r], f"rank {r}")
         assert torch.equal(out[r], out_s[r]), "overlapped and serial results differ"
+        assert torch.equal(out[r], out_1[r]), "one chain and two chains differ"
+        assert torch.equal(out[r], out_1s[r]), "serial one chain and two chains differ"
 
 
 @pytest.mark.parametrize("mode,dims", RS_CASES[:2])

@@ -38,7 +38,8 @@ def _inputs(mode, n, dims, seed):
     return a, b, oshape
 
 
-FORMS = ["one-way stream", "one-way fused", "two-way stream", "two-way fused", "one-way serial"]
+FORMS = ["one-way stream", "one-way fused", "two-way stream", "two-way fused", "one-way serial",
+         "one-way serial one-chain", "two-way stream one-chain"]
 CASES = [
     # mode, (shard, K, other), n, out, p, bias, residual
     ("slice_lhs_rows", (72, 256, 264), 4, "bf16", 0.1, True, True),
@@ -57,6 +58,8 @@ def _flags(cce, form):
         f |= cce.CCE_FLAG_BIDIRECTIONAL
     if "serial" in form:
         f |= cce.CCE_FLAG_SERIAL
+    if "one-chain" in form:
+        f |= cce.CCE_FLAG_ONE_CHAIN
     return f
 
 

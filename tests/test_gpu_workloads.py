@@ -226,10 +226,12 @@ def test_gpt3_ffn_n8_full(ctx, flags, batched, in_rs):
 # Whole-tensor equality of the permute forms at full size.  The sampled
 # oracle checks above see a few rows of every shard; a copy or forwarding
 # mistake confined to other rows would pass them, but not these.  The
-# stream, serial and fused forms of one ring direction accumulate every
-# element in the same order, so their outputs agree bit for bit.
+# stream, serial and fused forms of one ring direction, with one or two
+# accumulator chains, accumulate every element in the same order, so their
+# outputs agree bit for bit.
 def _forms(cce, bid):
     return {"stream": bid, "serial": bid | cce.CCE_FLAG_SERIAL,
+            "serial one-chain": bid | cce.CCE_FLAG_SERIAL | cce.CCE_FLAG_ONE_CHAIN,
             "fused": bid | cce.CCE_FLAG_FUSED_PERMUTE}
 
 
@@ -246,7 +248,7 @@ def test_rs_n8_full_forms_equal(ctx, bid):
         cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", X, Wt, o, flags=fl)
         outs[name] = o
     sync()
-    for name in ("serial", "fused"):
+    for name in ("serial", "serial one-chain", "fused"):
         for r in range(n):
             assert torch.equal(outs["stream"][r].view(torch.int32), outs[name][r].view(torch.int32)), \
                 f"{name} differs from stream, shard {r}"
@@ -271,7 +273,7 @@ def test_gpt3_ffn_n8_full_forms_equal(ctx, bid):
         cce.cce_looped_einsum_reducescatter(ctx, "slice_lhs_rows", H, W2, acc, flags=fl)
         Hs[name], accs[name] = H, acc
     sync()
-    for name in ("serial", "fused"):
+    for name in ("serial", "serial one-chain", "fused"):
         for r in range(n):
             assert torch.equal(Hs["stream"][r].view(torch.int16), Hs[name][r].view(torch.int16)), \
                 f"H: {name} differs from stream, rank {r}"
