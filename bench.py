@@ -673,7 +673,12 @@ def epilogue_ceiling(dev, steps, warmup):
     partials with p = 0 and no bias or residual, which leaves the kernel
     moving data with one add per partial.  The ratio of the two rates is the
     cost of the epilogue's arithmetic; the second rate is what the kernel's
-    access pattern reaches on this GPU."""
+    access pattern reaches on this GPU.  Beside them, PyTorch's own
+    elementwise kernels move the same bytes (`vendor_streaming`): the sum of
+    the partials into a bf16 output, as one launch over the stacked batch,
+    and a plain copy of every partial, as a streaming ceiling that does not
+    come from this library (each working set exceeds the memory-side
+    cache)."""
     import torch
     import collective_overlap_amd as cce
     import workloads as W
@@ -715,9 +720,43 @@ def epilogue_ceiling(dev, steps, warmup):
             nbytes = full_bytes if tag == "full" else bare_bytes
             res_[tag] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        rows.append({"shape": name, **res_,
-                     "full_over_data_only_rate": round(res_["full"]["GB/s"] / res_["data_only"]["GB/s"], 4)})
         del parts, res, out
+        torch.cuda.empty_cache()
+        # PyTorch's kernels over the same bytes: stacked partials [n, nb, r, c]
+        stack = torch.stack([W.normal((nb, r, c), 1.0, 400 + k, device=dev, dtype=pdt)
+                             for k in range(n)])
+        o16 = torch.empty((nb, r, c), device=dev, dtype=torch.bfloat16)
+        ocp = torch.empty_like(stack)
+        if n == 1:
+            vsum = ("cast copy to bf16 (Tensor.copy_)", lambda: o16.copy_(stack[0]))
+        elif n == 2:
+            vsum = ("add into bf16 (torch.add, out=)", lambda: torch.add(stack[0], stack[1], out=o16))
+        else:
+            vsum = ("sum over the partials into bf16 (torch.sum, dim=0, out=)",
+                    lambda: torch.sum(stack, dim=0, out=o16))
+        vendor = {}
+        for tag, (what, fn), nbytes in (
+                ("sum_like_data_only", vsum, bare_bytes),
+                ("copy", ("plain copy of every partial (Tensor.copy_)", lambda: ocp.copy_(stack)),
+                 2 * n * nb * r * c * esz)):
+            for _ in range(warmup):
+                fn()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+            vendor[tag] = {"op": what, "ms": round(ms, 4), "bytes": nbytes,
+                           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        rows.append({"shape": name, **res_,
+                     "full_over_data_only_rate": round(res_["full"]["GB/s"] / res_["data_only"]["GB/s"], 4),
+                     "vendor_streaming": vendor,
+                     "data_only_over_vendor_sum": round(res_["data_only"]["GB/s"] /
+                                                        vendor["sum_like_data_only"]["GB/s"], 4)})
+        del stack, o16, ocp
         torch.cuda.empty_cache()
     ctx.close()
     return rows
