@@ -762,6 +762,115 @@ def epilogue_ceiling(dev, steps, warmup):
     return rows
 
 
+def hip_runtime():
+    """The HIP runtime PyTorch already loaded (found by its soname)."""
+    import ctypes
+    import torch  # noqa: F401
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def cu_masked_stream(hip, n_cus, cus):
+    """A new stream (default priority) whose kernels run only on the compute
+    units `cus` (indices into the runtime's CU mask)."""
+    import ctypes
+    words = (ctypes.c_uint32 * ((n_cus + 31) // 32))()
+    for c in cus:
+        words[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(words), words)
+    if err != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({err})")
+    return h.value
+
+
+def cu_mask_sweep(dev, steps, warmup):
+    """The stream form (copies on a second stream) with compute-unit masks:
+    the copy stream limited to a few CUs, alone or with the GEMMs' stream
+    limited to the others, against the context's own unmasked copy stream.
+    The hidden fraction uses the serial step (same GEMMs, every copy on the
+    compute stream) and its copy time from the same run."""
+    import torch
+    import collective_overlap_amd as cce
+    from collective_overlap_amd._lib import CceError
+    hip = hip_runtime()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx = cce.Context(0)
+    out = []
+    for wl in ("gpt3_ffn_n8", "rs_n8"):
+        log(f"cu-mask sweep {wl}")
+        step = WORKLOADS[wl](dev)
+        bid = cce.CCE_FLAG_BIDIRECTIONAL
+        for _ in range(warmup):
+            step.run(ctx, cce.CCE_FLAG_SERIAL | bid)
+        w, recs = timed(step, ctx, steps, cce.CCE_FLAG_SERIAL | bid, profile=True)
+        s_ms = w / steps * 1e3
+        copy_ms = sum(r["ms"] for r in recs if r["kind"] == "copy") / steps
+        base = s_ms - copy_ms
+        forms = [("own copy stream (no mask)", None, None)]
+        for n in (8, 32):
+            for layout, cus in (("first", list(range(n))),
+                                ("strided", list(range(0, n_cus, n_cus // n))[:n])):
+                rest = sorted(set(range(n_cus)) - set(cus))
+                forms.append((f"copy on {n} CUs ({layout})", cus, None))
+                forms.append((f"copy on {n} CUs ({layout}), GEMMs on the other {n_cus - n}",
+                              cus, rest))
+        forms.append(("copy stream with a mask of every CU", list(range(n_cus)), None))
+        rows = []
+        stop = False
+        for name, ccus, gcus in forms:
+            try:
+                cs = cu_masked_stream(hip, n_cus, ccus) if ccus else None
+            except RuntimeError as e:
+                rows.append({"form": name, "error": str(e)})
+                continue
+            try:
+                gs = cu_masked_stream(hip, n_cus, gcus) if gcus else None
+            except RuntimeError as e:
+                hip.hipStreamDestroy(cs)
+                rows.append({"form": name, "error": str(e)})
+                continue
+            ctx.set_copy_stream(cs)
+            try:
+                with torch.cuda.stream(torch.cuda.ExternalStream(gs) if gs
+                                       else torch.cuda.current_stream()):
+                    for _ in range(warmup):
+                        step.run(ctx, bid)
+                    w, _ = timed(step, ctx, steps, bid, profile=False)
+            except CceError as e:
+                # A runtime that cannot give the masked stream a queue fails
+                # its first launch, and may fail later launches too: stop.
+                rows.append({"form": name, "error": str(e)})
+                stop = True
+            finally:
+                try:
+                    torch.cuda.synchronize()
+                except Exception as e:     # (the runtime's state after such a failure)
+                    rows.append({"form": name, "synchronize_error": str(e).splitlines()[0]})
+                    stop = True
+                ctx.set_copy_stream(None)
+                for h in (cs, gs):
+                    if h:
+                        hip.hipStreamDestroy(h)
+            if stop:
+                break
+            ms = w / steps * 1e3
+            rows.append({"form": name, "step_ms": round(ms, 3),
+                         "hidden_copy_frac": round(1.0 - (ms - base) / copy_ms, 4)})
+        out.append({"workload": wl, "serial_ms": round(s_ms, 3), "copy_ms_serial": round(copy_ms, 3),
+                    "n_cus": n_cus, "stream_form": rows})
+        del step
+        if stop:
+            break
+        torch.cuda.empty_cache()
+    if not stop:
+        ctx.close()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -790,6 +899,10 @@ def main(argv=None):
     ap.add_argument("--fine-grained", action="store_true",
                     help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
                          "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
+    ap.add_argument("--cu-mask-sweep", action="store_true",
+                    help="only time the stream form of gpt3_ffn_n8 and rs_n8 with the copy "
+                         "stream (and optionally the GEMMs' stream) limited to some compute "
+                         "units; prints one JSON line")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only compare the grouped GEMM with hipBLASLt (torch.bmm) on the "
                          "headline shapes; prints one JSON line")
@@ -828,6 +941,9 @@ def main(argv=None):
     if a.epilogue_ceiling:
         print(json.dumps({"epilogue_ceiling": epilogue_ceiling(dev, a.steps, a.warmup),
                           "hbm_peak_GB/s": PEAK_HBM_GBS}), flush=True)
+        return 0
+    if a.cu_mask_sweep:
+        print(json.dumps({"cu_mask_sweep": cu_mask_sweep(dev, a.steps, a.warmup)}), flush=True)
         return 0
     if a.vendor_gemm:
         print(json.dumps({"vendor_gemm": vendor_gemm(dev, a.steps, a.warmup),
