@@ -871,6 +871,30 @@ def cu_mask_sweep(dev, steps, warmup):
     return out
 
 
+def mfma_ceiling(iters=200000):
+    """Run the MFMA ceiling program (collective_overlap_amd/mfma_ceiling, a
+    child process) and summarise its measurements: median TFLOP/s per
+    variant and its fraction of the bf16 peak."""
+    import subprocess
+    exe = os.path.join(ROOT, "collective_overlap_amd", "mfma_ceiling")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is missing: build with `python -m collective_overlap_amd.build`")
+    r = subprocess.run([exe, str(iters)], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        raise SystemExit(f"mfma_ceiling failed ({r.returncode}): {r.stderr.strip()}")
+    rows = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    out = {}
+    for row in rows:
+        out.setdefault((row["mfma"], row["operands"]), []).append(row["TFLOP/s"])
+    res = []
+    for (mf, op), v in out.items():
+        v = sorted(v)
+        med = v[len(v) // 2]
+        res.append({"mfma": mf, "operands": op, "TFLOP/s": med, "all": v,
+                    "frac_of_peak": round(med / PEAK_TFLOPS["bf16"], 4)})
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -899,6 +923,9 @@ def main(argv=None):
     ap.add_argument("--fine-grained", action="store_true",
                     help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
                          "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the MFMA ceiling program: the bf16 rate the matrix cores "
+                         "sustain on MFMAs and LDS operand reads alone; prints one JSON line")
     ap.add_argument("--cu-mask-sweep", action="store_true",
                     help="only time the stream form of gpt3_ffn_n8 and rs_n8 with the copy "
                          "stream (and optionally the GEMMs' stream) limited to some compute "
@@ -920,6 +947,13 @@ def main(argv=None):
                           "n_gpus": a.gpus}), flush=True)
         return 2
 
+    if a.mfma_ceiling:
+        # (before this process touches the GPU: the program is a child)
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(), "peak_TFLOP/s": PEAK_TFLOPS["bf16"],
+                          "loop": "128 x 128 x 32 wave tile per iteration, operands read "
+                                  "from LDS, no global memory traffic, one workgroup per CU"}),
+              flush=True)
+        return 0
     import torch
     import collective_overlap_amd as cce
     if not torch.cuda.is_available():

@@ -25,6 +25,11 @@ LIB = os.path.join(PKG, "libcce.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["gemm.hip", "epilogue.hip", "permute.hip", "plan.cpp", "abi.cpp"]
+# A standalone measurement program, not part of the library: the rate the
+# matrix cores sustain on MFMAs and LDS operand reads alone (bench.py
+# --mfma-ceiling runs it).
+PROBE_SRC = "mfma_ceiling.hip"
+PROBE = os.path.join(PKG, "mfma_ceiling")
 ARCH = "gfx950"
 
 
@@ -125,8 +130,21 @@ def build(jobs: int = 4, verbose: bool = False, extra=(), out: str = LIB,
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout}\n{r.stderr}")
     os.replace(out + ".tmp", out)
+    if out == LIB:
+        build_probe()
     if verbose:
         print(f"built {out}")
+    return out
+
+
+def build_probe(out: str = PROBE) -> str:
+    """Compile the MFMA ceiling program (an executable, not linked into the
+    library)."""
+    cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, PROBE_SRC), "-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(out + ".tmp", out)
     return out
 
 
