@@ -690,8 +690,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
 
+  // The MFMAs of a step walk the accumulator blocks in a snake order: row i
+  // of blocks left to right, row i+1 right to left, so that consecutive
+  // MFMAs always share one operand.  The matrix cores run power-limited and
+  // fewer operand changes cost less: 0.4% per launch, 0.9% in a loop of
+  // MFMAs alone.  Each block still sees the same k sequence (same bits).
   auto mfma_one = [&](int slot, int q) {
-    const int i = q / FM, j = q % FM;
+    const int i = q / FM;
+    const int j = (i & 1) ? FM - 1 - q % FM : q % FM;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][i], fa[slot][j], acc[i][j], 0, 0, 0);
   };
 
