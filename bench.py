@@ -895,6 +895,53 @@ def mfma_ceiling(iters=200000):
     return res
 
 
+def ab_libs(dev, paths, workloads, rounds, steps, warmup):
+    """A/B timing of library builds: the benchmark's form (fused permute,
+    two-way ring) of each workload's step under every build in `paths`
+    (e.g. two git revisions built with `python -m collective_overlap_amd.build
+    --rev REV --out PATH`), interleaved round by round in one process so that
+    clock and power drift hit every build alike.  Per build: the median,
+    minimum and maximum of the rounds' mean step times."""
+    import torch
+    import collective_overlap_amd as cce
+    from collective_overlap_amd import _lib
+    builds = {}
+    for p in paths:
+        _lib._lib = None
+        _lib.LIB_PATH = os.path.abspath(p)
+        builds[p] = (_lib.lib(), cce.Context(0))
+    flags = cce.CCE_FLAG_FUSED_PERMUTE | cce.CCE_FLAG_BIDIRECTIONAL
+    out = []
+    for wl in workloads:
+        log(f"a/b {wl}")
+        step = WORKLOADS[wl](dev)
+        res = {p: [] for p in paths}
+        for _ in range(rounds):
+            for p in paths:
+                lib, ctx = builds[p]
+                _lib._lib = lib
+                for _ in range(warmup):
+                    step.run(ctx, flags)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    step.run(ctx, flags)
+                torch.cuda.synchronize()
+                res[p].append((time.perf_counter() - t0) / steps * 1e3)
+        rows = []
+        for p in paths:
+            v = sorted(res[p])
+            rows.append({"lib": p, "median_ms": round(v[len(v) // 2], 4), "min_ms": round(v[0], 4),
+                         "max_ms": round(v[-1], 4), "rounds": [round(x, 4) for x in res[p]]})
+        base = rows[0]["median_ms"]
+        for r in rows:
+            r["over_first"] = round(r["median_ms"] / base, 4)
+        out.append({"workload": wl, "builds": rows})
+        del step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -923,6 +970,12 @@ def main(argv=None):
     ap.add_argument("--fine-grained", action="store_true",
                     help="the ReduceScatter's chunk consumer (epilogue or align-and-sum) runs "
                          "inside its last launch (CCE_FLAG_FINE_GRAINED; fused permute)")
+    ap.add_argument("--ab", nargs="+", metavar="LIB",
+                    help="only time the listed library builds against each other (A/B, "
+                         "interleaved rounds in one process); prints one JSON line")
+    ap.add_argument("--ab-workloads", default="gpt3_ffn_n8,rs_n8",
+                    help="comma-separated workloads for --ab")
+    ap.add_argument("--ab-rounds", type=int, default=8, help="interleaved rounds for --ab")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the MFMA ceiling program: the bf16 rate the matrix cores "
                          "sustain on MFMAs and LDS operand reads alone; prints one JSON line")
@@ -975,6 +1028,15 @@ def main(argv=None):
     if a.epilogue_ceiling:
         print(json.dumps({"epilogue_ceiling": epilogue_ceiling(dev, a.steps, a.warmup),
                           "hbm_peak_GB/s": PEAK_HBM_GBS}), flush=True)
+        return 0
+    if a.ab:
+        wls = a.ab_workloads.split(",")
+        for w in wls:
+            if w not in WORKLOADS:
+                raise SystemExit(f"unknown workload {w}")
+        print(json.dumps({"ab": ab_libs(dev, a.ab, wls, a.ab_rounds, a.steps, a.warmup),
+                          "form": "fused permute, two-way ring", "steps_per_round": a.steps}),
+              flush=True)
         return 0
     if a.cu_mask_sweep:
         print(json.dumps({"cu_mask_sweep": cu_mask_sweep(dev, a.steps, a.warmup)}), flush=True)

@@ -148,11 +148,54 @@ def build_probe(out: str = PROBE) -> str:
     return out
 
 
+def sources_at(rev: str) -> str:
+    """Write the library's sources (csrc/ and include/cce.h) as of git
+    revision `rev` under the build directory; returns the csrc copy, for
+    building an older library beside the current one (A/B timing)."""
+    top = os.path.join(BUILD, "rev_" + re.sub(r"[^0-9A-Za-z_.-]", "_", rev))
+    csrc = os.path.join(top, "collective_overlap_amd", "csrc")
+    os.makedirs(csrc, exist_ok=True)
+    os.makedirs(os.path.join(top, "include"), exist_ok=True)
+
+    def show(path):
+        r = subprocess.run(["git", "-C", ROOT, "show", f"{rev}:{path}"], capture_output=True)
+        return r.stdout if r.returncode == 0 else None
+
+    hdr = show("include/cce.h")
+    if hdr is None:
+        raise RuntimeError(f"include/cce.h not found at {rev}")
+    open(os.path.join(top, "include", "cce.h"), "wb").write(hdr)
+    ls = subprocess.run(["git", "-C", ROOT, "ls-tree", "--name-only", f"{rev}:collective_overlap_amd/csrc"],
+                        capture_output=True, text=True)
+    if ls.returncode != 0:
+        raise RuntimeError(ls.stderr.strip())
+    for f in ls.stdout.split():
+        open(os.path.join(csrc, f), "wb").write(show(f"collective_overlap_amd/csrc/{f}"))
+    return csrc
+
+
 def main(argv=None):
+    global CSRC
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(4, os.cpu_count() or 1))
+    ap.add_argument("--rev", help="build the sources of this git revision instead of the "
+                                  "working tree (needs --out)")
+    ap.add_argument("--out", help="library path (default: the package's libcce.so)")
     a = ap.parse_args(argv)
-    build(a.jobs, verbose=True)
+    if a.rev and not a.out:
+        ap.error("--rev needs --out: the package's own library is built from the working tree")
+    out = os.path.abspath(a.out) if a.out else LIB
+    bd = BUILD
+    if a.rev:
+        CSRC = sources_at(a.rev)
+        top = os.path.dirname(os.path.dirname(CSRC))
+        # that revision's header, not the working tree's
+        i = COMMON.index(os.path.join(ROOT, "include"))
+        COMMON[i] = os.path.join(top, "include")
+        SOURCES[:] = [f for f in SOURCES if os.path.exists(os.path.join(CSRC, f))]
+        bd = os.path.join(top, "obj")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    build(a.jobs, verbose=True, out=out, build_dir=bd)
 
 
 if __name__ == "__main__":

@@ -111,11 +111,11 @@ def test_gelu_device_values_within_the_erf_bound(ctx):
     assert got[-1, 0] == 0.0                                   # GELU(0) = 0
 
 
-# bf16 results of launches with more tiles than CUs: each workgroup walks
-# several tiles and stores part of a tile's results while it computes the
-# next.  Ragged rows (edge tiles store at once), k-tile counts below and
-# above the spread of those stores, and a padded output row stride.
-PERSISTENT_CASES = [
+# bf16 results of launches with more tiles than CUs (several rounds of
+# workgroups), ragged rows (edge tiles take the element-wise store path),
+# one to 17 k tiles, the 256 x 128 tile shape, and a padded output row
+# stride whose padding must stay untouched.
+MANY_TILE_CASES = [
     # G, M, N, K, output ld (None: N)
     (2, 4000, 4096, 200, None),       # 512 tiles of 256x256, ragged rows, 4 k tiles
     (1, 8192, 8192, 64, None),        # 1024 tiles, one k tile
@@ -124,7 +124,7 @@ PERSISTENT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("G,M,N,K,ld", PERSISTENT_CASES)
+@pytest.mark.parametrize("G,M,N,K,ld", MANY_TILE_CASES)
 def test_grouped_gemm_many_tiles_bf16_integer_probe(ctx, G, M, N, K, ld):
     import collective_overlap_amd as cce
     print(f"[gpu] grouped_gemm many tiles G={G} M={M} N={N} K={K} ld={ld}", flush=True)
