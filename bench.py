@@ -16,7 +16,8 @@ ReduceScatter's accumulate epilogue stores into the next rank's
 accumulator); --permute stream times the form with async copies on a second
 stream instead.  Both, and the same kernels serialised on one stream, are
 reported.  The ring is two-way by default (two partial einsums per
-iteration, one per direction); --transfer one-way times the one-way ring.
+iteration, one per direction) for every workload but the ReduceScatter
+alone (rs_n8), whose one-way ring is faster; --transfer picks either.
 
 Prints one JSON line: whole-step bf16 TFLOP/s (value), the dominant kernel's
 roofline, the epilogue's HBM rate, the looped-vs-serial comparison with the
@@ -276,6 +277,10 @@ class Mlp2:
 class RsN8:
     name = "rs_n8"
     has_rs = True
+    # The one-way ring is this workload's faster form (2.20 against 2.27 ms
+    # per step, interleaved in one process): the two-way ring's closing
+    # align-and-sum launch costs more than its fewer, larger launches save.
+    transfer = "one-way"
     sample_default, sample_cap = 16, 2048      # rows of every shard in the oracle sample
     dtype = "bf16"
 
@@ -556,16 +561,26 @@ def measure(step, ctx, workload, steps, warmup, main_flags, bid, permute, transf
             "epilogue": epi_info, "gemm_ms": gemm_ms, "monolithic": mono, "overlap": overlap}
 
 
-def config_summary(name, dev, ctx, steps, warmup, bid_default):
+def preferred_bid(name):
+    """The ring form a workload is benchmarked in: two-way unless its class
+    says otherwise (the attention out-projection has no ring)."""
+    import collective_overlap_amd as cce
+    cls = WORKLOADS[name]
+    if not getattr(cls, "has_permute", True) or getattr(cls, "transfer", "bidir") != "bidir":
+        return 0
+    return cce.CCE_FLAG_BIDIRECTIONAL
+
+
+def config_summary(name, dev, ctx, steps, warmup):
     """A workload other than the headline, measured in the benchmark's form
-    (fused permute, two-way ring), for the same JSON line: per-step time and
-    rate, the dominant GEMM launch's roofline, the epilogue's HBM rate, the
-    permute forms, the unlooped comparison and parity against the oracle on a
-    small sample."""
+    (fused permute, the workload's ring form), for the same JSON line:
+    per-step time and rate, the dominant GEMM launch's roofline, the
+    epilogue's HBM rate, the permute forms, the unlooped comparison and
+    parity against the oracle on a small sample."""
     import torch
     import collective_overlap_amd as cce
     step = WORKLOADS[name](dev)
-    bid = bid_default if name != "attn_outproj_n8" else 0
+    bid = preferred_bid(name)
     flags = cce.CCE_FLAG_FUSED_PERMUTE | bid
     m = measure(step, ctx, name, steps, warmup, flags, bid, "fused",
                 "bidir" if bid else "one-way", serial=True)
@@ -576,7 +591,10 @@ def config_summary(name, dev, ctx, steps, warmup, bid_default):
     _, _, desc, err = step.oracle_sample()
     bar = 2e-2 if step.dtype == "bf16" else 1e-5
     roof = m["roofline"]
-    out = {"config": step.config(), "dtype": step.dtype,
+    cfg = dict(step.config(), permute="fused")
+    if getattr(step, "has_permute", True):
+        cfg["transfer"] = "bidirectional" if bid else "one-way"
+    out = {"config": cfg, "dtype": step.dtype,
            "ms_per_step": round(m["ms_per_step"], 4),
            "TFLOP/s": round(m["value"], 2),
            "frac_of_mfma_peak": round(m["value"] / PEAK_TFLOPS[step.dtype], 4),
@@ -955,9 +973,10 @@ def main(argv=None):
                          "copies on a second stream ordered by events; serial: the stream "
                          "form's kernels, every copy on the caller's stream; dma: the stream "
                          "form with the copies on the SDMA engines")
-    ap.add_argument("--transfer", choices=("bidir", "one-way"), default="bidir",
-                    help="bidir (default): two-way ring, two partial einsums per iteration, "
-                         "ceil(n/2) iterations; one-way: the ring of the loop's pairs only")
+    ap.add_argument("--transfer", choices=("bidir", "one-way"), default=None,
+                    help="bidir: two-way ring, two partial einsums per iteration, ceil(n/2) "
+                         "iterations; one-way: the ring of the loop's pairs only (default: the "
+                         "workload's faster form, two-way except rs_n8)")
     ap.add_argument("--allreduce", action="store_true",
                     help="attn_outproj_n8: FusedAllReduce epilogue, the result on every rank")
     ap.add_argument("--separate-epilogue", action="store_true",
@@ -1057,6 +1076,8 @@ def main(argv=None):
         step.fuse_epilogue = False
     ctx = cce.Context(0)
     torch.cuda.synchronize()
+    if a.transfer is None:
+        a.transfer = "bidir" if preferred_bid(a.workload) else "one-way"
     bid = cce.CCE_FLAG_BIDIRECTIONAL if a.transfer == "bidir" else 0
     main_flags = {"fused": cce.CCE_FLAG_FUSED_PERMUTE, "stream": 0, "serial": cce.CCE_FLAG_SERIAL,
                   "dma": cce.CCE_FLAG_COPY_DMA}[a.permute] | bid
@@ -1135,8 +1156,7 @@ def main(argv=None):
             if name == a.workload:
                 continue
             log(f"config {name}")
-            configs[name] = config_summary(name, dev, ctx, min(a.steps, 10), max(2, a.warmup),
-                                           cce.CCE_FLAG_BIDIRECTIONAL)
+            configs[name] = config_summary(name, dev, ctx, min(a.steps, 10), max(2, a.warmup))
         out["configs"] = configs
     print(json.dumps(out), flush=True)
     ctx.close()
