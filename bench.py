@@ -561,6 +561,30 @@ def measure(step, ctx, workload, steps, warmup, main_flags, bid, permute, transf
             "epilogue": epi_info, "gemm_ms": gemm_ms, "monolithic": mono, "overlap": overlap}
 
 
+def copy_ceiling(dev, reps=10):
+    """The plain read+write rate of this GPU's memory: a 1 GiB device copy
+    (PyTorch's copy, the runtime's blit kernel), the practical ceiling the
+    epilogue's HBM rate is set against beside the 8 TB/s peak."""
+    import torch
+    nb = 1 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nb / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"op": "plain device copy of 1 GiB (Tensor.copy_)", "bytes_moved": 2 * nb,
+            "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def preferred_bid(name):
     """The ring form a workload is benchmarked in: two-way unless its class
     says otherwise (the attention out-projection has no ring)."""
@@ -1119,6 +1143,9 @@ def main(argv=None):
         parity = {"rel_fro_err_vs_oracle": err, "bar": 2e-2 if step.dtype == "bf16" else 1e-5,
                   "ok": err <= (2e-2 if step.dtype == "bf16" else 1e-5)}
 
+    ceiling = copy_ceiling(dev)
+    if epi_info is not None:
+        epi_info["frac_of_copy_ceiling"] = round(epi_info["GB/s"] / ceiling["GB/s"], 4)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1143,6 +1170,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "epilogue": epi_info,
+        "hbm_copy_ceiling": ceiling,
         "overlap": overlap,
         "monolithic": mono,
         "gemm_ms_per_step": round(gemm_ms, 3),
