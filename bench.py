@@ -333,6 +333,8 @@ class RsN8:
 class AgFp32N2:
     name = "ag_fp32_n2"
     dtype = "f32"
+    # launch-bound (microseconds per kernel): also timed as a captured graph
+    graph = True
 
     def __init__(self, dev):
         import torch
@@ -345,6 +347,9 @@ class AgFp32N2:
         self.b = W.uniform((256,), 30, device=dev)
         self.R = W.uniform((64, 256), 31, device=dev)
         self.out = torch.empty((64, 256), device=dev)
+        import collective_overlap_amd as cce
+        self.ws = torch.empty(cce.cce_looped_allgather_einsum_workspace(
+            2, "rhs_cols", "f32", "f32", (512, 256), (64, 1024)), dtype=torch.uint8, device=dev)
         self.flops = 2.0 * 64 * 256 * 1024 * 2
 
     def config(self):
@@ -353,7 +358,7 @@ class AgFp32N2:
 
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
-        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.Wt, self.X, self.Y,
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.Wt, self.X, self.Y, self.ws,
                                         flags=flags & ~cce.CCE_FLAG_FINE_GRAINED)
         cce.cce_fused_reduce_epilogue(ctx, self.P, self.b, self.R, self.out, 0.1, 0, 0)
 
@@ -585,6 +590,30 @@ def copy_ceiling(dev, reps=10):
             "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def graph_replay_ms(step, ctx, flags, steps, warmup):
+    """The step captured once into a graph (torch.cuda.CUDAGraph over the
+    library's calls: every entry point is capturable when the caller passes
+    its workspace) and replayed: per-step time without the host's work per
+    launch."""
+    import torch
+    step.run(ctx, flags)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run(ctx, flags)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del g
+    torch.cuda.synchronize()
+    return ms
+
+
 def preferred_bid(name):
     """The ring form a workload is benchmarked in: two-way unless its class
     says otherwise (the attention out-projection has no ring)."""
@@ -608,11 +637,19 @@ def config_summary(name, dev, ctx, steps, warmup):
     flags = cce.CCE_FLAG_FUSED_PERMUTE | bid
     m = measure(step, ctx, name, steps, warmup, flags, bid, "fused",
                 "bidir" if bid else "one-way", serial=True)
-    # parity of the timed outputs on a small oracle sample (the outputs hold
-    # the last timed step's results)
-    step.run(ctx, flags)
-    torch.cuda.synchronize()
+    graph = None
+    if getattr(step, "graph", False):
+        g_ms = graph_replay_ms(step, ctx, flags, max(steps, 100), warmup)
+        graph = {"ms_per_step": round(g_ms, 4), "TFLOP/s": round(step.flops / (g_ms * 1e-3) / 1e12, 3),
+                 "how": "the step captured once (torch.cuda.CUDAGraph) and replayed"}
+    else:
+        step.run(ctx, flags)
+        torch.cuda.synchronize()
+    # parity of the outputs on a small oracle sample (they hold the last
+    # step's results: the last graph replay's where the step was replayed)
     _, _, desc, err = step.oracle_sample()
+    if graph:
+        desc += " (outputs of the last graph replay)"
     bar = 2e-2 if step.dtype == "bf16" else 1e-5
     roof = m["roofline"]
     cfg = dict(step.config(), permute="fused")
@@ -626,6 +663,7 @@ def config_summary(name, dev, ctx, steps, warmup):
                k: roof[k] for k in ("achieved", "frac", "avg_launch_ms", "flops_per_launch",
                                     "launches")},
            "epilogue": m["epilogue"], "overlap": m["overlap"], "monolithic": m["monolithic"],
+           **({"graph_replay": graph} if graph else {}),
            "parity": {"rel_fro_err_vs_oracle": err, "bar": bar, "ok": err <= bar, "sample": desc}}
     del step
     torch.cuda.empty_cache()
