@@ -1097,9 +1097,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 template <typename TOut, int EPI, bool GELU>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
-  constexpr int BM = 64, BN = 64, BK = 16, LDK = BK + 1;
-  __shared__ float sa[BM * LDK];
-  __shared__ float sb[BN * LDK];
+  // 64 x 64 tiles, 32-deep k chunks in two LDS buffers: chunk c+1's global
+  // loads are in flight (in registers) while chunk c's MFMAs run, and are
+  // written to the other buffer afterwards, so each chunk costs one barrier
+  // and no exposed load latency beyond the first.  (With 16-deep chunks and
+  // a load-barrier-compute loop, a launch of 4 x 64 x 512 x 256 took 17 us,
+  // almost all of it waiting for loads.)  The MFMAs see k in the same order
+  // as any other chunking, so the results do not depend on it.
+  constexpr int BM = 64, BN = 64, BK = 32, LDK = BK + 1;
+  __shared__ float sa[2][BM * LDK];
+  __shared__ float sb[2][BN * LDK];
   int g, tm, tn;
   map_tile(a, g, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -1107,35 +1114,62 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(KArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const float* A = reinterpret_cast<const float*>(a.p.a[g]);
   const float* B = reinterpret_cast<const float*>(a.p.b[g]);
-  const int lr = tid >> 2, lc = (tid & 3) * 4;
-  f32x16 acc = f32x16{};
-  for (int k0 = 0; k0 < a.K; k0 += BK) {
-    {
-      const int m = m0 + lr, k = k0 + lc;
-      f32x4 v = f32x4{};
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(m) * a.lda + k);
-      for (int e = 0; e < 4; ++e) sa[lr * LDK + lc + e] = v[e];
-      const int n = n0 + lr;
-      f32x4 w = f32x4{};
-      if (n < a.N && k < a.K) w = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(n) * a.ldb + k);
-      for (int e = 0; e < 4; ++e) sb[lr * LDK + lc + e] = w[e];
-      // fused permute: forward the looped operand's k tile (once per row block)
-      const int kt = k0 / BK;
-      float* fd = reinterpret_cast<float*>(a.p.fwd[g]);
-      if (a.fwd == FWD_A && fd != nullptr && kt % a.tiles_n == tn && m < a.M && k < a.K)
-        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(m) * a.ldfwd + k) = v;
-      if (a.fwd == FWD_B && fd != nullptr && kt % a.tiles_m == tm && n < a.N && k < a.K)
-        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(n) * a.ldfwd + k) = w;
+  float* fd = reinterpret_cast<float*>(a.p.fwd[g]);
+  // loads: thread t takes rows t / 8 and t / 8 + 32 of each operand's chunk,
+  // 4 consecutive k at (t % 8) * 4 (K is a multiple of 8)
+  const int lr = tid >> 3, lc = (tid & 7) * 4;
+  f32x4 va[2], vb[2];
+  auto gload = [&](int k0) {
+    const int k = k0 + lc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + lr + 32 * h, n = n0 + lr + 32 * h;
+      va[h] = (m < a.M && k < a.K) ? *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(m) * a.lda + k)
+                                   : f32x4{};
+      vb[h] = (n < a.N && k < a.K) ? *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(n) * a.ldb + k)
+                                   : f32x4{};
     }
+  };
+  auto lstore = [&](int buf, int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[buf][(lr + 32 * h) * LDK + lc + e] = va[h][e];
+        sb[buf][(lr + 32 * h) * LDK + lc + e] = vb[h][e];
+      }
+    // fused permute: forward the looped operand's k chunk (once per row block)
+    const int kt = k0 / BK, k = k0 + lc;
+    if (fd == nullptr || k >= a.K) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + lr + 32 * h, n = n0 + lr + 32 * h;
+      if (a.fwd == FWD_A && kt % a.tiles_n == tn && m < a.M)
+        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(m) * a.ldfwd + k) = va[h];
+      if (a.fwd == FWD_B && kt % a.tiles_m == tm && n < a.N)
+        *reinterpret_cast<f32x4*>(fd + static_cast<int64_t>(n) * a.ldfwd + k) = vb[h];
+    }
+  };
+  f32x16 acc = f32x16{};
+  const int nk = (a.K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    lstore(0, 0);
+  }
+  for (int c = 0; c < nk; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < nk) gload((c + 1) * BK);
+    // chunk c's stores are visible; every wave is done with chunk c-1's
+    // buffer, which the stores below overwrite
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < BK / 2; ++kk) {
       const int k = 2 * kk + (lane >> 5);
-      const float x = sb[(wn * 32 + (lane & 31)) * LDK + k];
-      const float y = sa[(wm * 32 + (lane & 31)) * LDK + k];
+      const float x = sb[cur][(wn * 32 + (lane & 31)) * LDK + k];
+      const float y = sa[cur][(wm * 32 + (lane & 31)) * LDK + k];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, acc, 0, 0, 0);
     }
-    __syncthreads();
+    if (c + 1 < nk) lstore(cur ^ 1, (c + 1) * BK);
   }
   const int m = m0 + wm * 32 + (lane & 31);
   if constexpr (EPI == EPI_FINAL) {
