@@ -230,6 +230,14 @@ class Mlp2:
         self.W2 = [W.weight_store(self.Hh, self.F // n, 0.02, 20 + s, device=dev) for s in range(n)]
         self.H = [torch.empty((self.B, self.Hh), device=dev, dtype=bf) for _ in range(n)]
         self.Y = [torch.empty((self.B, self.F), device=dev, dtype=bf) for _ in range(n)]
+        import collective_overlap_amd as cce
+        w1, w2 = self.W1[0], self.W2[0]
+        self.ws1 = torch.empty(cce.cce_looped_allgather_einsum_workspace(
+            n, "rhs_cols", "bf16", "bf16", tuple(w1.shape), (self.B, self.Hh)), dtype=torch.uint8,
+            device=dev)
+        self.ws2 = torch.empty(cce.cce_looped_allgather_einsum_workspace(
+            n, "rhs_cols", "bf16", "bf16", tuple(w2.shape), (self.B, self.F)), dtype=torch.uint8,
+            device=dev)
         self.flops = 2 * (2.0 * self.B * self.F * self.Hh * n)
 
     def config(self):
@@ -239,9 +247,10 @@ class Mlp2:
     def run(self, ctx, flags=0):
         import collective_overlap_amd as cce
         flags &= ~cce.CCE_FLAG_FINE_GRAINED      # (a ReduceScatter flag)
-        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W1, self.X, self.H,
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W1, self.X, self.H, self.ws1,
                                         flags=flags | cce.CCE_FLAG_GELU)
-        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W2, self.H, self.Y, flags=flags)
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", self.W2, self.H, self.Y, self.ws2,
+                                        flags=flags)
 
     def monolithic(self):
         """Both layers unlooped: each rank multiplies by the gathered weights
