@@ -991,7 +991,7 @@ def mfma_ceiling(iters=200000):
 
 def ab_libs(dev, paths, workloads, rounds, steps, warmup):
     """A/B timing of library builds: the benchmark's form (fused permute,
-    two-way ring) of each workload's step under every build in `paths`
+    the workload's ring form) of each workload's step under every build in `paths`
     (e.g. two git revisions built with `python -m collective_overlap_amd.build
     --rev REV --out PATH`), interleaved round by round in one process so that
     clock and power drift hit every build alike.  Per build: the median,
@@ -1004,10 +1004,10 @@ def ab_libs(dev, paths, workloads, rounds, steps, warmup):
         _lib._lib = None
         _lib.LIB_PATH = os.path.abspath(p)
         builds[p] = (_lib.lib(), cce.Context(0))
-    flags = cce.CCE_FLAG_FUSED_PERMUTE | cce.CCE_FLAG_BIDIRECTIONAL
     out = []
     for wl in workloads:
         log(f"a/b {wl}")
+        flags = cce.CCE_FLAG_FUSED_PERMUTE | preferred_bid(wl)
         step = WORKLOADS[wl](dev)
         res = {p: [] for p in paths}
         for _ in range(rounds):
@@ -1130,7 +1130,7 @@ def main(argv=None):
             if w not in WORKLOADS:
                 raise SystemExit(f"unknown workload {w}")
         print(json.dumps({"ab": ab_libs(dev, a.ab, wls, a.ab_rounds, a.steps, a.warmup),
-                          "form": "fused permute, two-way ring", "steps_per_round": a.steps}),
+                          "form": "fused permute, each workload's ring form", "steps_per_round": a.steps}),
               flush=True)
         return 0
     if a.cu_mask_sweep:
