@@ -517,3 +517,24 @@ def test_spill_guard_reads_the_compiler_remarks():
     assert build.check_spills(sc, known={"kern_b": 12}) == []
     assert build.check_spills(sc, known={"kern_b": 8}) == ["kern_b: 12 bytes/lane (allowed 8)"]
 
+
+
+def test_sources_of_a_revision_are_that_revisions():
+    """build.py --rev writes a revision's library sources beside the working
+    tree for an A/B build: for HEAD they are the committed files, byte for
+    byte, and the header is that revision's."""
+    import subprocess
+    from collective_overlap_amd import build
+    if subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True).returncode != 0:
+        pytest.skip("not a git checkout")
+    csrc = build.sources_at("HEAD")
+    ls = subprocess.run(["git", "-C", ROOT, "ls-tree", "--name-only", "HEAD:collective_overlap_amd/csrc"],
+                        capture_output=True, text=True).stdout.split()
+    assert "gemm.hip" in ls and sorted(os.listdir(csrc)) == sorted(ls)
+    for f in ls:
+        want = subprocess.run(["git", "-C", ROOT, "show", f"HEAD:collective_overlap_amd/csrc/{f}"],
+                              capture_output=True).stdout
+        assert open(os.path.join(csrc, f), "rb").read() == want, f
+    hdr = os.path.join(os.path.dirname(os.path.dirname(csrc)), "include", "cce.h")
+    want = subprocess.run(["git", "-C", ROOT, "show", "HEAD:include/cce.h"], capture_output=True).stdout
+    assert open(hdr, "rb").read() == want
