@@ -856,6 +856,58 @@ def epilogue_ceiling(dev, steps, warmup):
     return rows
 
 
+def k_sweep(dev, steps, warmup):
+    """The grouped GEMM of the GPT-3 FFN's AllGather launch shape (16 groups
+    of 1024 x 6144, bf16 out) at several contraction lengths, with and
+    without GELU: a straight-line fit of launch time against K gives the
+    cost that does not scale with K (the tile's pipeline fill, epilogue and
+    stores, the launch itself), and the difference between the two forms the
+    cost of GELU.  Every launch does its whole work."""
+    import torch
+    import collective_overlap_amd as cce
+    import workloads as W
+    ctx = cce.Context(0)
+    G, M, N = 16, 1024, 6144
+    ks = [768, 1536, 3072, 6144, 12288]
+    data = {}
+    for k in ks:
+        a = [W.normal((M, k), 1.0, g, device=dev) for g in range(G)]
+        b = [W.normal((N, k), 0.02, 10 + g, device=dev) for g in range(G)]
+        c = [torch.empty((M, N), device=dev, dtype=torch.bfloat16) for _ in range(G)]
+        data[k] = (a, b, c)
+    res = {(k, gl): [] for k in ks for gl in (False, True)}
+    for _ in range(3):                      # rounds, interleaved
+        for k in ks:
+            for gl in (False, True):
+                a, b, c = data[k]
+                for _ in range(warmup):
+                    cce.cce_grouped_gemm(ctx, a, b, c, gelu=gl)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    cce.cce_grouped_gemm(ctx, a, b, c, gelu=gl)
+                e1.record()
+                torch.cuda.synchronize()
+                res[(k, gl)].append(e0.elapsed_time(e1) / steps)
+    rows, fit = [], {}
+    for gl in (False, True):
+        pts = []
+        for k in ks:
+            v = sorted(res[(k, gl)])[1]
+            pts.append((k, v))
+            rows.append({"K": k, "gelu": gl, "ms": round(v, 4),
+                         "TFLOP/s": round(2.0 * G * M * N * k / (v * 1e-3) / 1e12, 1)})
+        # least squares over the two longest K (the linear regime)
+        (k1, t1), (k2, t2) = pts[-2], pts[-1]
+        slope = (t2 - t1) / (k2 - k1)
+        fit["gelu" if gl else "no_gelu"] = {"ms_per_1024_k": round(slope * 1024, 5),
+                                            "fixed_ms": round(t2 - slope * k2, 4)}
+    gelu_ms = [round(sorted(res[(k, True)])[1] - sorted(res[(k, False)])[1], 4) for k in ks]
+    ctx.close()
+    return {"shape": f"{G} x {M} x {N} x K, bf16 out", "launches": rows, "fit": fit,
+            "gelu_cost_ms_by_K": dict(zip(ks, gelu_ms))}
+
+
 def hip_runtime():
     """The HIP runtime PyTorch already loaded (found by its soname)."""
     import ctypes
@@ -1074,6 +1126,9 @@ def main(argv=None):
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the MFMA ceiling program: the bf16 rate the matrix cores "
                          "sustain on MFMAs and LDS operand reads alone; prints one JSON line")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="only time the GPT-3 AllGather launch shape at several K, with and "
+                         "without GELU (fixed cost per launch, cost of GELU); one JSON line")
     ap.add_argument("--cu-mask-sweep", action="store_true",
                     help="only time the stream form of gpt3_ffn_n8 and rs_n8 with the copy "
                          "stream (and optionally the GEMMs' stream) limited to some compute "
@@ -1135,6 +1190,9 @@ def main(argv=None):
         return 0
     if a.cu_mask_sweep:
         print(json.dumps({"cu_mask_sweep": cu_mask_sweep(dev, a.steps, a.warmup)}), flush=True)
+        return 0
+    if a.k_sweep:
+        print(json.dumps({"k_sweep": k_sweep(dev, a.steps, a.warmup)}), flush=True)
         return 0
     if a.vendor_gemm:
         print(json.dumps({"vendor_gemm": vendor_gemm(dev, a.steps, a.warmup),
