@@ -638,12 +638,15 @@ def preferred_bid(name):
     return cce.CCE_FLAG_BIDIRECTIONAL
 
 
-def config_summary(name, dev, ctx, steps, warmup):
+def config_summary(name, dev, ctx, steps, warmup, cpu_leg=True):
     """A workload other than the headline, measured in the benchmark's form
     (fused permute, the workload's ring form), for the same JSON line:
     per-step time and rate, the dominant GEMM launch's roofline, the
-    epilogue's HBM rate, the permute forms, the unlooped comparison and
-    parity against the oracle on a small sample."""
+    epilogue's HBM rate, the permute forms and the unlooped comparison.
+    With `cpu_leg` (the CPU-baseline leg, off with --no-cpu-baseline) the
+    oracle also runs on a small sample of the workload on the host: its
+    rate is the entry's cpu_baseline, and the timed outputs are checked
+    against it (parity)."""
     import torch
     import collective_overlap_amd as cce
     step = WORKLOADS[name](dev)
@@ -659,12 +662,18 @@ def config_summary(name, dev, ctx, steps, warmup):
     else:
         step.run(ctx, flags)
         torch.cuda.synchronize()
-    # parity of the outputs on a small oracle sample (they hold the last
-    # step's results: the last graph replay's where the step was replayed)
-    _, _, desc, err = step.oracle_sample()
-    if graph:
-        desc += " (outputs of the last graph replay)"
+    # CPU-baseline leg: the oracle on a small sample, which also checks the
+    # outputs (they hold the last step's results: the last graph replay's
+    # where the step was replayed)
+    cpu, parity = None, None
     bar = 2e-2 if step.dtype == "bf16" else 1e-5
+    if cpu_leg:
+        dt, fl, desc, err = step.oracle_sample()
+        if graph:
+            desc += " (outputs of the last graph replay)"
+        cpu = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "kind": "oracle",
+               "sample": desc, "seconds": round(dt, 3)}
+        parity = {"rel_fro_err_vs_oracle": err, "bar": bar, "ok": err <= bar, "sample": desc}
     roof = m["roofline"]
     cfg = dict(step.config(), permute="fused")
     if getattr(step, "has_permute", True):
@@ -678,7 +687,7 @@ def config_summary(name, dev, ctx, steps, warmup):
                                     "launches")},
            "epilogue": m["epilogue"], "overlap": m["overlap"], "monolithic": m["monolithic"],
            **({"graph_replay": graph} if graph else {}),
-           "parity": {"rel_fro_err_vs_oracle": err, "bar": bar, "ok": err <= bar, "sample": desc}}
+           "cpu_baseline": cpu, "parity": parity}
     del step
     torch.cuda.empty_cache()
     return out
@@ -1294,7 +1303,8 @@ def main(argv=None):
             if name == a.workload:
                 continue
             log(f"config {name}")
-            configs[name] = config_summary(name, dev, ctx, min(a.steps, 10), max(2, a.warmup))
+            configs[name] = config_summary(name, dev, ctx, min(a.steps, 10), max(2, a.warmup),
+                                           cpu_leg=not a.no_cpu_baseline)
         out["configs"] = configs
     print(json.dumps(out), flush=True)
     ctx.close()
