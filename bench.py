@@ -147,9 +147,12 @@ class Gpt3Ffn:
         h = oe.allgather_einsum("lhs_rows", xs, w1)
         h = [numerics.bf16_round(numerics.gelu(x).astype(np.float32)).astype(np.float64) for x in h]
         a = oe.einsum_reducescatter("slice_lhs_rows", h, w2)
+        t1 = time.perf_counter()
         outs = [oep.fused_reduce_epilogue([a[r]], b, rr[r], self.p, 0, 0, row0=r * self.ts,
                                           col0=0, mask_ld=self.Hd)[0] for r in range(self.n)]
         dt = time.perf_counter() - t0
+        # the epilogue's share (its vectorised Philox included), timed apart
+        self.epi_oracle = (time.perf_counter() - t1, self.n * t * self.Hd)
         got = np.concatenate([f64(o[:t]) for o in self.out])
         ref = np.concatenate(outs)
         err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
@@ -1261,6 +1264,13 @@ def main(argv=None):
                "cpu_model": model}
         parity = {"rel_fro_err_vs_oracle": err, "bar": 2e-2 if step.dtype == "bf16" else 1e-5,
                   "ok": err <= (2e-2 if step.dtype == "bf16" else 1e-5)}
+        if getattr(step, "epi_oracle", None):
+            es, elems = step.epi_oracle
+            # bytes the device epilogue moves per element (fp32 partial, bf16
+            # residual and output), for a rate comparable with its GB/s
+            cpu["epilogue_oracle"] = {"seconds": round(es, 4), "elements": elems,
+                                      "Melements/s": round(elems / es / 1e6, 2),
+                                      "GB/s_at_device_bytes": round(8.0 * elems / es / 1e9, 3)}
 
     ceiling = copy_ceiling(dev)
     if epi_info is not None:
