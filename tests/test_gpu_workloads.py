@@ -281,3 +281,31 @@ def test_gpt3_ffn_n8_full_forms_equal(ctx, bid):
                 f"acc: {name} differs from stream, rank {r}"
     assert all(bool(torch.isfinite(h).all()) for h in Hs["stream"])
     assert all(bool(torch.isfinite(a).all()) for a in accs["stream"])
+
+
+@pytest.mark.parametrize("bid", [0, 0x10])
+def test_mlp2_n4_full_forms_equal(ctx, bid):
+    """Both MLP layers (looped weight shards, rhs_cols; GELU between) over
+    every element of every rank, in every permute form."""
+    import collective_overlap_amd as cce
+    print(f"[gpu] mlp2_n4 full, whole-tensor form equality bid={bid:#x}", flush=True)
+    n, B, F, Hh = 4, 2048, 4096, 16384
+    X = [W.normal((B, F), 1.0, r, device=DEV) for r in range(n)]
+    W1 = [W.weight_store(F, Hh // n, 0.02, 10 + s, device=DEV) for s in range(n)]
+    W2 = [W.weight_store(Hh, F // n, 0.02, 20 + s, device=DEV) for s in range(n)]
+    Hs, Ys = {}, {}
+    for name, fl in _forms(cce, bid).items():
+        H = [torch.full((B, Hh), float("nan"), device=DEV, dtype=BF) for _ in range(n)]
+        Y = [torch.full((B, F), float("nan"), device=DEV, dtype=BF) for _ in range(n)]
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W1, X, H, flags=fl | cce.CCE_FLAG_GELU)
+        cce.cce_looped_allgather_einsum(ctx, "rhs_cols", W2, H, Y, flags=fl)
+        Hs[name], Ys[name] = H, Y
+    sync()
+    for name in ("serial", "fused"):
+        for r in range(n):
+            assert torch.equal(Hs["stream"][r].view(torch.int16), Hs[name][r].view(torch.int16)), \
+                f"H: {name} differs from stream, rank {r}"
+            assert torch.equal(Ys["stream"][r].view(torch.int16), Ys[name][r].view(torch.int16)), \
+                f"Y: {name} differs from stream, rank {r}"
+    assert all(bool(torch.isfinite(h).all()) for h in Hs["stream"])
+    assert all(bool(torch.isfinite(y).all()) for y in Ys["stream"])
