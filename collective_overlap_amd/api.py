@@ -199,20 +199,23 @@ def _torch_stream(stream, device):
     return torch.cuda.ExternalStream(int(stream), device=device)
 
 
-def _workspace(nbytes, device, workspace, stream=None):
-    """The caller's workspace, or a temporary one.  A temporary one is freed
-    when the call returns, while the work that uses it may still be queued on
-    `stream` (the copy stream joins back into it).  When that is not the
-    current stream, the caching allocator is told, so that it does not hand
-    the memory out again before `stream` has finished with it."""
+def _workspace(need, device, workspace, stream=None):
+    """The caller's workspace (the library checks its size), or a temporary
+    one of need() bytes.  A temporary one is freed when the call returns,
+    while the work that uses it may still be queued on `stream` (the copy
+    stream joins back into it).  When that is not the current stream, the
+    caching allocator is told, so that it does not hand the memory out again
+    before `stream` has finished with it."""
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    nbytes = need()
     if nbytes == 0:
         return None, 0
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        s = _torch_stream(stream, device)
-        if s != torch.cuda.current_stream(device):
-            workspace.record_stream(s)
-    return workspace, workspace.numel() * workspace.element_size()
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    s = _torch_stream(stream, device)
+    if s != torch.cuda.current_stream(device):
+        workspace.record_stream(s)
+    return workspace, nbytes
 
 
 def cce_looped_allgather_einsum(ctx: Context, mode, looped, local, out, workspace=None,
@@ -222,9 +225,10 @@ def cce_looped_allgather_einsum(ctx: Context, mode, looped, local, out, workspac
     mode = AG_MODES[mode] if isinstance(mode, str) else mode
     lm, cm, om = _same(looped, "looped"), _same(local, "local"), _same(out, "out")
     in_t, out_t = _dtype(looped[0].dtype), _dtype(out[0].dtype)
-    need = cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t,
-                                                 (lm.rows, lm.cols, lm.ld),
-                                                 (om.rows, om.cols, om.ld))
+    def need():
+        return cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t,
+                                                     (lm.rows, lm.cols, lm.ld),
+                                                     (om.rows, om.cols, om.ld))
     ws, wsb = _workspace(need, out[0].device, workspace, stream)
     check(lib().cce_looped_allgather_einsum(
         ctx.handle, n, mode, in_t, out_t,
@@ -253,8 +257,8 @@ def cce_looped_einsum_reducescatter(ctx: Context, mode, a, b, out, workspace=Non
     mode = RS_MODES[mode] if isinstance(mode, str) else mode
     am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
     in_t, out_t = _dtype(a[0].dtype), _dtype(out[0].dtype)
-    need = cce_looped_einsum_reducescatter_workspace(n, mode, (om.rows, om.cols, om.ld))
-    ws, wsb = _workspace(need, out[0].device, workspace, stream)
+    ws, wsb = _workspace(lambda: cce_looped_einsum_reducescatter_workspace(
+        n, mode, (om.rows, om.cols, om.ld)), out[0].device, workspace, stream)
     check(lib().cce_looped_einsum_reducescatter(
         ctx.handle, n, mode, in_t, CCE_F32, out_t,
         ptr_array([t.data_ptr() for t in a]), am,
@@ -281,8 +285,8 @@ def cce_looped_einsum_reducescatter_epilogue(ctx: Context, mode, a, b, bias, res
     if mask_ld is None:
         mask_ld = mask_col0 + om.cols
     rows0 = list(mask_row0) if mask_row0 is not None else [0] * n
-    need = cce_looped_einsum_reducescatter_workspace(n, mode, (om.rows, om.cols, om.ld))
-    ws, wsb = _workspace(need, out[0].device, workspace, stream)
+    ws, wsb = _workspace(lambda: cce_looped_einsum_reducescatter_workspace(
+        n, mode, (om.rows, om.cols, om.ld)), out[0].device, workspace, stream)
     check(lib().cce_looped_einsum_reducescatter_epilogue(
         ctx.handle, n, mode, _dtype(a[0].dtype), _dtype(out[0].dtype),
         ptr_array([t.data_ptr() for t in a]), am,
