@@ -1053,6 +1053,28 @@ def mfma_ceiling(iters=200000):
     return res
 
 
+def hbm_ceiling(reps=5):
+    """Run the HBM streaming ceiling program (collective_overlap_amd/
+    hbm_ceiling, a child process): for each read:write mix, the fastest of its
+    variants (unroll depth, cache hint, grid) and the whole sweep."""
+    import subprocess
+    exe = os.path.join(ROOT, "collective_overlap_amd", "hbm_ceiling")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is missing: build with `python -m collective_overlap_amd.build`")
+    r = subprocess.run([exe, str(reps)], capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise SystemExit(f"hbm_ceiling failed ({r.returncode}): {r.stderr.strip()}")
+    rows = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    best = {}
+    for row in rows:
+        if row["mix"] not in best or row["GB/s"] > best[row["mix"]]["GB/s"]:
+            best[row["mix"]] = row
+    summary = [{"mix": m, "GB/s": b["GB/s"], "frac_of_hbm_peak": round(b["GB/s"] / PEAK_HBM_GBS, 4),
+                "unroll": b["unroll"], "nontemporal": b["nontemporal"],
+                "workgroups": b["workgroups"], "loop": b["loop"]} for m, b in best.items()]
+    return {"best": summary, "sweep": rows}
+
+
 def ab_libs(dev, paths, workloads, rounds, steps, warmup):
     """A/B timing of library builds: the benchmark's form (fused permute,
     the workload's ring form) of each workload's step under every build in `paths`
@@ -1148,6 +1170,9 @@ def main(argv=None):
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only compare the grouped GEMM with hipBLASLt (torch.bmm) on the "
                          "headline shapes; prints one JSON line")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only run the HBM streaming ceiling program (read, write, copy and the "
+                         "epilogue's read:write mixes); prints one JSON line")
     ap.add_argument("--epilogue-ceiling", action="store_true",
                     help="only time the fused epilogue's kernels on the benchmark shapes, full "
                          "and reduced to moving data; prints one JSON line")
@@ -1167,6 +1192,12 @@ def main(argv=None):
         print(json.dumps({"mfma_ceiling": mfma_ceiling(), "peak_TFLOP/s": PEAK_TFLOPS["bf16"],
                           "loop": "128 x 128 x 32 wave tile per iteration, operands read "
                                   "from LDS, no global memory traffic, one workgroup per CU"}),
+              flush=True)
+        return 0
+    if a.hbm_ceiling:
+        # (a child process, like the MFMA ceiling)
+        print(json.dumps({"hbm_ceiling": hbm_ceiling(), "peak_GB/s": PEAK_HBM_GBS,
+                          "streams": "1 GiB each, 16-byte vectors, XOR of the inputs written"}),
               flush=True)
         return 0
     import torch

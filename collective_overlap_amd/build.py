@@ -25,11 +25,11 @@ LIB = os.path.join(PKG, "libcce.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["gemm.hip", "epilogue.hip", "permute.hip", "plan.cpp", "abi.cpp"]
-# A standalone measurement program, not part of the library: the rate the
+# Standalone measurement programs, not part of the library: the rate the
 # matrix cores sustain on MFMAs and LDS operand reads alone (bench.py
-# --mfma-ceiling runs it).
-PROBE_SRC = "mfma_ceiling.hip"
-PROBE = os.path.join(PKG, "mfma_ceiling")
+# --mfma-ceiling runs it), and what HBM sustains for plain streaming kernels
+# (bench.py --hbm-ceiling).
+PROBES = ("mfma_ceiling", "hbm_ceiling")
 ARCH = "gfx950"
 
 
@@ -131,16 +131,18 @@ def build(jobs: int = 4, verbose: bool = False, extra=(), out: str = LIB,
         raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout}\n{r.stderr}")
     os.replace(out + ".tmp", out)
     if out == LIB:
-        build_probe()
+        for name in PROBES:
+            build_probe(name)
     if verbose:
         print(f"built {out}")
     return out
 
 
-def build_probe(out: str = PROBE) -> str:
-    """Compile the MFMA ceiling program (an executable, not linked into the
-    library)."""
-    cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, PROBE_SRC), "-o", out + ".tmp"]
+def build_probe(name: str = "mfma_ceiling") -> str:
+    """Compile a measurement program (an executable beside the library, not
+    linked into it) from csrc/<name>.hip."""
+    out = os.path.join(PKG, name)
+    cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, name + ".hip"), "-o", out + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -61,3 +61,32 @@ def test_roofline_takes_the_dominant_launch_shape():
     assert roof["achieved"] == pytest.approx(1000.0, rel=1e-3)      # TFLOP/s
     assert roof["frac"] == pytest.approx(1000.0 / bench.PEAK_TFLOPS["bf16"], rel=1e-3)
     assert roof["bound"] == "mfma" and len(per_shape) == 2
+
+
+def test_hbm_ceiling_keeps_the_fastest_variant_of_each_mix(monkeypatch):
+    """The streaming-ceiling summary: per read:write mix, the variant with
+    the highest rate, as a fraction of the 8 TB/s peak; the program's own
+    lines are kept as the sweep."""
+    import subprocess
+    lines = [
+        {"mix": "read", "reads": 1, "writes": 0, "unroll": 1, "nontemporal": False,
+         "workgroups": 512, "loop": True, "ms_per_launch": 0.2, "GB/s": 5000.0},
+        {"mix": "read", "reads": 1, "writes": 0, "unroll": 4, "nontemporal": True,
+         "workgroups": 512, "loop": True, "ms_per_launch": 0.15, "GB/s": 7000.0},
+        {"mix": "5:1", "reads": 5, "writes": 1, "unroll": 1, "nontemporal": True,
+         "workgroups": 262144, "loop": False, "ms_per_launch": 1.0, "GB/s": 6000.0},
+    ]
+
+    class Done:
+        returncode = 0
+        stdout = "".join(json.dumps(l) + "\n" for l in lines)
+        stderr = ""
+
+    monkeypatch.setattr(os.path, "exists", lambda p: True)
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Done())
+    got = bench.hbm_ceiling()
+    best = {b["mix"]: b for b in got["best"]}
+    assert best["read"]["GB/s"] == 7000.0 and best["read"]["unroll"] == 4
+    assert best["read"]["frac_of_hbm_peak"] == 0.875
+    assert best["5:1"]["frac_of_hbm_peak"] == 0.75
+    assert got["sweep"] == lines
