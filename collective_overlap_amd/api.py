@@ -72,6 +72,25 @@ def _same(ts, what):
     return m0
 
 
+def _dtype_is(ts, dtype, what):
+    """Every tensor of `ts` (None entries skipped) has `dtype`: the C ABI takes
+    one element type for these operands and reads them as that type."""
+    for t in ts:
+        if t is not None and t.dtype != dtype:
+            raise ValueError(f"{what} must be {dtype} here, got {t.dtype}")
+
+
+def _on_device(ctx, ts):
+    """Every tensor of `ts` (None entries skipped) lives on the context's GPU:
+    the library dereferences each pointer on that device."""
+    dev = getattr(ctx, "device", None)
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or (dev is not None and t.device.index != dev):
+            raise ValueError(f"every tensor must be on cuda:{dev}, got one on {t.device}")
+
+
 def _stream(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -224,6 +243,8 @@ def cce_looped_allgather_einsum(ctx: Context, mode, looped, local, out, workspac
     n = len(looped)
     mode = AG_MODES[mode] if isinstance(mode, str) else mode
     lm, cm, om = _same(looped, "looped"), _same(local, "local"), _same(out, "out")
+    _dtype_is(local, looped[0].dtype, "the local operand")
+    _on_device(ctx, [*looped, *local, *out, workspace])
     in_t, out_t = _dtype(looped[0].dtype), _dtype(out[0].dtype)
     def need():
         return cce_looped_allgather_einsum_workspace(n, mode, in_t, out_t,
@@ -256,6 +277,8 @@ def cce_looped_einsum_reducescatter(ctx: Context, mode, a, b, out, workspace=Non
     n = len(a)
     mode = RS_MODES[mode] if isinstance(mode, str) else mode
     am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
+    _dtype_is(b, a[0].dtype, "b")
+    _on_device(ctx, [*a, *b, *out, workspace])
     in_t, out_t = _dtype(a[0].dtype), _dtype(out[0].dtype)
     ws, wsb = _workspace(lambda: cce_looped_einsum_reducescatter_workspace(
         n, mode, (om.rows, om.cols, om.ld)), out[0].device, workspace, stream)
@@ -282,9 +305,14 @@ def cce_looped_einsum_reducescatter_epilogue(ctx: Context, mode, a, b, bias, res
     mode = RS_MODES[mode] if isinstance(mode, str) else mode
     am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
     rm = _same(residuals, "residual") if residuals is not None else None
+    # the ABI reads the bias and the residuals as the output's element type
+    _dtype_is(b, a[0].dtype, "b")
+    _dtype_is([bias, *(residuals or [])], out[0].dtype, "the bias and the residuals")
+    _on_device(ctx, [*a, *b, bias, *(residuals or []), *out])
     if mask_ld is None:
         mask_ld = mask_col0 + om.cols
     rows0 = list(mask_row0) if mask_row0 is not None else [0] * n
+    _on_device(ctx, [workspace])
     ws, wsb = _workspace(lambda: cce_looped_einsum_reducescatter_workspace(
         n, mode, (om.rows, om.cols, om.ld)), out[0].device, workspace, stream)
     check(lib().cce_looped_einsum_reducescatter_epilogue(
@@ -314,6 +342,10 @@ def cce_looped_einsum_reducescatter_epilogue_noalloc(ctx: Context, mode, a, b, b
     mode = RS_MODES[mode] if isinstance(mode, str) else mode
     am, bm, om = _same(a, "a"), _same(b, "b"), _same(out, "out")
     rm = _same(residuals, "residual") if residuals is not None else None
+    # the ABI reads the bias and the residuals as the output's element type
+    _dtype_is(b, a[0].dtype, "b")
+    _dtype_is([bias, *(residuals or [])], out[0].dtype, "the bias and the residuals")
+    _on_device(ctx, [*a, *b, bias, *(residuals or []), *out])
     if mask_ld is None:
         mask_ld = mask_col0 + om.cols
     rows0 = list(mask_row0) if mask_row0 is not None else [0] * n
@@ -333,6 +365,8 @@ def cce_looped_einsum_reducescatter_epilogue_noalloc(ctx: Context, mode, a, b, b
 def cce_grouped_gemm(ctx: Context, a, b, c, gelu: bool = False, stream=None):
     """c[g] = a[g] @ b[g]^T for every g, one launch."""
     am, bm, cm = _same(a, "a"), _same(b, "b"), _same(c, "c")
+    _dtype_is(b, a[0].dtype, "b")
+    _on_device(ctx, [*a, *b, *c])
     check(lib().cce_grouped_gemm(
         ctx.handle, len(a), _dtype(a[0].dtype), _dtype(c[0].dtype),
         ptr_array([t.data_ptr() for t in a]), am,
@@ -350,6 +384,7 @@ def cce_fused_reduce_epilogue(ctx: Context, partials, bias, residual, out, p_dro
     pm = _same(partials, "partial")
     om = _mat(out)
     rm = _mat(residual) if residual is not None else None
+    _on_device(ctx, [*partials, bias, residual, out, mask_out])
     if mask_ld is None:
         mask_ld = mask_col0 + pm.cols
     bias_t = _dtype(bias.dtype) if bias is not None else _dtype(out.dtype)
@@ -380,6 +415,7 @@ def cce_fused_reduce_epilogue_batched(ctx: Context, partials, bias, residuals, o
     flat = [t for ps in partials for t in ps]
     pm = _same(flat, "partial")
     om = _same(outs, "out")
+    _on_device(ctx, [*flat, bias, *(residuals or []), *outs, *(mask_outs or [])])
     rm = _same(residuals, "residual") if residuals is not None else None
     if mask_ld is None:
         mask_ld = mask_col0 + pm.cols
@@ -408,6 +444,7 @@ def cce_fused_allreduce_epilogue(ctx: Context, partials, bias, residual, outs, p
     om = _same(outs, "out")
     if len(outs) != len(partials):
         raise ValueError("one output per rank")
+    _on_device(ctx, [*partials, bias, residual, *outs, mask_out])
     rm = _mat(residual) if residual is not None else None
     if mask_ld is None:
         mask_ld = mask_col0 + pm.cols
